@@ -1,0 +1,66 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check the pins catch them.
+
+Each mutant is oracle.c with one edit: a dropped term, a wrong sign, a wrong index, a
+transposed operand or a wrong head map.  The pins of tests/test_oracle_pins.py run against
+the mutant library; at least one must fail, or the pins would not be pinning that part.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "decay_dropped": ("A[a] = alpha * Pc[a];", "A[a] = Pc[a];"),
+    "delta_sign": ("const float u = beta * (v[c] - r);", "const float u = beta * (v[c] + r);"),
+    "beta_dropped": ("const float u = beta * (v[c] - r);", "const float u = (v[c] - r);"),
+    "write_from_parent": ("Sc[a] = A[a] + k[a] * u;", "Sc[a] = Pc[a] + k[a] * u;"),
+    "readout_parent_state": ("acc = acc + Sc[a] * (scale * q[a]);",
+                             "acc = acc + Pc[a] * (scale * q[a]);"),
+    "readout_unscaled": ("acc = acc + Sc[a] * (scale * q[a]);", "acc = acc + Sc[a] * q[a];"),
+    "state_transposed": ("for (int a = 0; a < dk; ++a) A[a] = alpha * Pc[a];",
+                         "for (int a = 0; a < dk; ++a) A[a] = alpha * P[(size_t)a * dv + c];"),
+    "qk_head_map": ("      const int g = h / ratio;\n      for (int a = 0; a < dk; ++a) {",
+                    "      const int g = h % hk;\n      for (int a = 0; a < dk; ++a) {"),
+    "root_not_from_base": ("const float *P = (parent[i] < 0) ? S_base + (size_t)h * hs",
+                           "const float *P = (parent[i] < 0) ? S_base"),
+    "ancestor_order_reversed": (
+        "kv = ld(kt, dtype, ((int64_t)path[depth - 1 - (t - L)] * hkv + m_head) * D + d);",
+        "kv = ld(kt, dtype, ((int64_t)path[t - L] * hkv + m_head) * D + d);"),
+    "kv_head_map": ("const int m_head = j / (hq / hkv);", "const int m_head = j % hkv;"),
+    "attn_unscaled": ("z[t] = scale * dot;", "z[t] = dot;"),
+    "self_not_visible": ("const int64_t nkeys = L + depth;", "const int64_t nkeys = L + depth - 1;"),
+    "mask_without_self": ("mask[i] = ((p < 0) ? 0 : mask[p]) | (1ULL << i);",
+                          "mask[i] = ((p < 0) ? 0 : mask[p]);"),
+    "softmax_unnormalised": ("for (int d = 0; d < D; ++d) o[d] = o[d] / l;",
+                             "for (int d = 0; d < D; ++d) o[d] = o[d];"),
+}
+
+
+def _build_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    path = tmp_path / f"{name}.c"
+    path.write_text(src.replace(old, new))
+    lib = tmp_path / f"lib{name}.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                           "-o", str(lib), str(path), "-lm"])
+    return oracle.configure(ctypes.CDLL(str(lib)))
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path, monkeypatch):
+    lib = _build_mutant(tmp_path, name, *MUTANTS[name])
+    monkeypatch.setattr(oracle, "_lib", lib)
+    failed = []
+    for pin, fn in pins.PINS.items():
+        try:
+            fn()
+        except (AssertionError, ValueError):
+            failed.append(pin)
+    assert failed, f"no pin catches the mutant {name}"

@@ -1,0 +1,268 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+  * hand-worked examples (tests/golden/*.json) with exact expected values;
+  * closed forms of the Gated DeltaNet step and of masked softmax attention;
+  * a float64 brute force in a different formulation (tests/brute.py);
+  * library softmax attention (torch scaled_dot_product_attention, float64, CPU);
+  * the pages' invariant that a verified row equals the sequential decode row
+    ("Adding a model", step 4 of "The adapter path in ten steps"), bit for bit.
+
+PINS maps a name to a check that raises AssertionError on failure;
+tests/test_oracle_mutants.py reruns them against deliberately broken copies
+of the oracle to show each plausible mistake is caught.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+SEED = 1234
+
+
+def _f32(x):
+    return np.asarray(x, np.float32)
+
+
+def _gdn_case(seed, n=9, hk=2, hv=4, dk=8, dv=6, dtype="f32", tree="random"):
+    w = synth.Workload("pin", [0], hk, hv, dk, dv, 2, 1, 8, dtype, [0], n, "random4")
+    parent = synth.random_tree(seed, f"pin/gdn/{seed}", n, 5) if tree == "random" \
+        else synth.chain_tree(n)
+    q, k, v, a, b = synth.gdn_inputs(w, seed, 0, 0, n)
+    S = synth.gdn_state(w, seed, 0, 0)
+    return parent, S, q, k, v, a, b
+
+
+def _attn_case(seed, n=8, hq=6, hkv=2, D=16, L=23, dtype="f32", sharp=False, tree="random"):
+    w = synth.Workload("pin", [1], 1, 1, 8, 8, hq, hkv, D, dtype, [L], n, "random4")
+    parent = synth.random_tree(seed, f"pin/attn/{seed}", n, 5) if tree == "random" \
+        else synth.chain_tree(n)
+    q, kt, vt = synth.attn_inputs(w, seed, 0, 0, n, sharp=sharp)
+    cap = L + n + 3
+    Kc = np.zeros((hkv, cap, D), q.dtype)
+    Vc = np.zeros((hkv, cap, D), q.dtype)
+    for h in range(hkv):
+        K, V = synth.kv_rows(w, seed, 0, 0, h, 0, L, sharp=sharp)
+        Kc[h, :L], Vc[h, :L] = K, V
+    return parent, L, Kc, Vc, q, kt, vt
+
+
+# ---------------------------------------------------------------------------------------------
+# Pins
+# ---------------------------------------------------------------------------------------------
+
+def pin_gdn_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "gdn_hand_example.json")))
+    S = np.transpose(_f32(g["S_base_rows_a_cols_c"]))[None]          # [hv][dv][dk]
+    n = len(g["parent"])
+    q = _f32(g["q"]).reshape(n, 1, 2)
+    k = _f32(g["k"]).reshape(n, 1, 2)
+    v = _f32(g["v"]).reshape(n, 1, 2)
+    a = _f32(g["alpha"]).reshape(n, 1)
+    b = _f32(g["beta"]).reshape(n, 1)
+    o, states = oracle.gdn_tree(g["parent"], S, q, k, v, a, b, scale=g["scale"],
+                                want_states=True)
+    assert np.array_equal(o[:, 0], _f32(g["o"]))
+    assert np.array_equal(states[:, 0], np.transpose(_f32(g["S_nodes_rows_a_cols_c"]), (0, 2, 1)))
+    Sc = oracle.gdn_commit(g["commit_path"], S, k, v, a, b)
+    assert np.array_equal(Sc[0], np.transpose(_f32(g["S_after_commit_rows_a_cols_c"])))
+
+
+def pin_attn_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "attn_hand_example.json")))
+    n, D = len(g["parent"]), g["D"]
+    Kc = _f32(g["K_resident"]).reshape(1, g["L"], D)
+    Vc = _f32(g["V_resident"]).reshape(1, g["L"], D)
+    o = oracle.attn_tree(g["parent"], g["L"], Kc, Vc, _f32(g["q"]).reshape(n, 1, D),
+                         _f32(g["k_tree"]).reshape(n, 1, D), _f32(g["v_tree"]).reshape(n, 1, D),
+                         scale=g["scale"])
+    np.testing.assert_allclose(o[:, 0], _f32(g["o"]), rtol=0, atol=g["tolerance"] * 10)
+
+
+def pin_tree_meta_brute():
+    for seed in range(6):
+        parent = synth.random_tree(seed, "pin/meta", 40, 9)
+        depth, mask, anc, pos = oracle.tree_meta(parent, L=100)
+        for i in range(len(parent)):
+            chain = []
+            x = i
+            while x >= 0:
+                chain.append(x)
+                x = parent[x]
+            assert depth[i] == len(chain) - 1
+            assert pos[i] == 100 + len(chain) - 1
+            assert int(mask[i]) == sum(1 << j for j in chain)
+            assert list(anc[i, :len(chain)]) == chain[::-1]
+            assert (anc[i, len(chain):] == -1).all()
+    for bad in ([0], [-1, 1], [-1, 0, 3], [-1, -1], []):
+        with pytest.raises(ValueError):
+            oracle.tree_meta(bad)
+
+
+def pin_gdn_brute():
+    for seed, dtype in ((1, "f32"), (2, "bf16"), (3, "f32")):
+        parent, S, q, k, v, a, b = _gdn_case(seed, dtype=dtype)
+        s = float(np.float32(1 / np.sqrt(8)))
+        o, states = oracle.gdn_tree(parent, S, q, k, v, a, b, want_states=True)
+        ob, sb = brute.gdn_tree(parent, S, q, k, v, a, b, s)
+        assert brute.rel_err(o, ob) < 1e-5, brute.rel_err(o, ob)
+        assert brute.rel_err(states, sb) < 1e-5
+
+
+def pin_gdn_closed_forms():
+    parent, S, q, k, v, a, b = _gdn_case(7, n=7)
+    s = float(np.float32(1 / np.sqrt(8)))
+    ones, zeros = np.ones_like(a), np.zeros_like(b)
+    # alpha = 1, beta = 0: the state never moves and o = s S_base^T q.
+    o, st = oracle.gdn_tree(parent, S, q, k, v, ones, zeros, want_states=True)
+    for i in range(len(parent)):
+        for h in range(S.shape[0]):
+            assert np.array_equal(st[i, h], S[h])
+            exp = S[h].astype(np.float64) @ (s * q[i, h // 2].astype(np.float64))
+            np.testing.assert_allclose(o[i, h], exp, rtol=1e-5, atol=1e-6)
+    # beta = 0: S_i = (product of alpha along the root path) S_base.
+    o, st = oracle.gdn_tree(parent, S, q, k, v, a, zeros, want_states=True)
+    for i in range(len(parent)):
+        prod = np.ones(S.shape[0])
+        for j in synth.root_path(parent, i):
+            prod = prod * a[j].astype(np.float64)
+        np.testing.assert_allclose(st[i], prod[:, None, None] * S, rtol=1e-5, atol=1e-7)
+    # S_base = 0 at the root: o_0 = s b_0 (k_0 . q_0) v_0.
+    o = oracle.gdn_tree(parent, np.zeros_like(S), q, k, v, a, b)
+    for h in range(S.shape[0]):
+        g = h // 2
+        exp = s * b[0, h] * float(k[0, g].astype(np.float64) @ q[0, g]) * v[0, h]
+        np.testing.assert_allclose(o[0, h], exp, rtol=1e-5, atol=1e-7)
+    # beta = 1 with unit k: the delta rule writes v at key k, k^T S_i = v_i.
+    o, st = oracle.gdn_tree(parent, S, q, k, v, a, ones, want_states=True)
+    for i in range(len(parent)):
+        for h in range(S.shape[0]):
+            kk = k[i, h // 2].astype(np.float64)
+            np.testing.assert_allclose(st[i, h].astype(np.float64) @ kk, v[i, h],
+                                       rtol=0, atol=1e-5)
+
+
+def pin_gdn_chain_is_sequential():
+    # A chain verify equals step-by-step decode with a commit after each step, bit for bit.
+    parent, S, q, k, v, a, b = _gdn_case(11, n=6, tree="chain")
+    o_tree, st_tree = oracle.gdn_tree(parent, S, q, k, v, a, b, want_states=True)
+    cur = S.copy()
+    for i in range(6):
+        sl = slice(i, i + 1)
+        o1 = oracle.gdn_tree([-1], cur, q[sl], k[sl], v[sl], a[sl], b[sl])
+        assert np.array_equal(o1[0], o_tree[i])
+        cur = oracle.gdn_commit([0], cur, k[sl], v[sl], a[sl], b[sl])
+        assert np.array_equal(cur, st_tree[i])
+    # and a commit of the whole path equals the tree state at the path's end
+    assert np.array_equal(oracle.gdn_commit(list(range(6)), S, k, v, a, b), st_tree[5])
+
+
+def pin_attn_brute():
+    for seed, dtype, sharp in ((1, "f32", False), (2, "bf16", False), (3, "f32", True),
+                               (4, "bf16", True)):
+        parent, L, Kc, Vc, q, kt, vt = _attn_case(seed, dtype=dtype, sharp=sharp)
+        s = float(np.float32(1 / np.sqrt(16)))
+        o = oracle.attn_tree(parent, L, Kc, Vc, q, kt, vt)
+        ob = brute.attn_tree(parent, L, Kc, Vc, q, kt, vt, s)
+        assert brute.rel_err(o, ob) < 1e-5, brute.rel_err(o, ob)
+
+
+def pin_attn_library():
+    torch = pytest.importorskip("torch")
+    parent, L, Kc, Vc, q, kt, vt = _attn_case(5, sharp=True)
+    n, hq, D = q.shape
+    hkv = Kc.shape[0]
+    o = oracle.attn_tree(parent, L, Kc, Vc, q, kt, vt)
+    vis = np.zeros((n, L + n), bool)
+    vis[:, :L] = True
+    _, mask, _, _ = oracle.tree_meta(parent)
+    for i in range(n):
+        for j in range(n):
+            vis[i, L + j] = bool((int(mask[i]) >> j) & 1)
+    for j in range(hq):
+        m = j // (hq // hkv)
+        K = np.concatenate([Kc[m, :L], kt[:, m]], 0).astype(np.float64)
+        V = np.concatenate([Vc[m, :L], vt[:, m]], 0).astype(np.float64)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[:, j].astype(np.float64))[None], torch.from_numpy(K)[None],
+            torch.from_numpy(V)[None], attn_mask=torch.from_numpy(vis)[None],
+            scale=1 / np.sqrt(D))[0].numpy()
+        assert brute.rel_err(o[:, j], ref) < 1e-5
+
+
+def pin_attn_closed_forms():
+    # Empty context, the root alone: one key of weight 1, o = v_root exactly.
+    parent, L, Kc, Vc, q, kt, vt = _attn_case(8, L=0)
+    o = oracle.attn_tree(parent, 0, Kc, Vc, q, kt, vt)
+    for j in range(q.shape[1]):
+        assert np.array_equal(o[0, j], vt[0, j // 3])
+    # All keys equal: uniform weights, o = mean of the visible values.
+    parent, L, Kc, Vc, q, kt, vt = _attn_case(9, sharp=True)
+    Kc[:] = Kc[:, :1]
+    kt[:] = Kc[:, 0][None]
+    o = oracle.attn_tree(parent, L, Kc, Vc, q, kt, vt)
+    for i in range(len(parent)):
+        for j in range(q.shape[1]):
+            m = j // 3
+            rows = [Vc[m, t] for t in range(L)] + [vt[x, m] for x in synth.root_path(parent, i)]
+            np.testing.assert_allclose(o[i, j], np.mean(np.asarray(rows, np.float64), 0),
+                                       rtol=1e-5, atol=1e-6)
+
+
+def pin_attn_verify_equals_decode():
+    # Row of node i at context L == row of the decode step at L + depth(i) once the
+    # ancestors' rows are committed, bit for bit.
+    parent, L, Kc, Vc, q, kt, vt = _attn_case(10, dtype="bf16", sharp=True)
+    o = oracle.attn_tree(parent, L, Kc, Vc, q, kt, vt)
+    for i in range(len(parent)):
+        path = synth.root_path(parent, i)
+        Kd, Vd = Kc.copy(), Vc.copy()
+        Kd[:, L:L + len(path) - 1] = oracle.commit_kv_rows(kt, path[:-1])
+        Vd[:, L:L + len(path) - 1] = oracle.commit_kv_rows(vt, path[:-1])
+        sl = slice(i, i + 1)
+        od = oracle.attn_tree([-1], L + len(path) - 1, Kd, Vd, q[sl], kt[sl], vt[sl])
+        assert np.array_equal(od[0], o[i])
+
+
+def pin_identical_siblings():
+    # Two identical subtrees under the root give identical rows, bit for bit.
+    parent = [-1, 0, 1, 0, 3]
+    gp, S, q, k, v, a, b = _gdn_case(12, n=5)
+    for arr in (q, k, v, a, b):
+        arr[3:5] = arr[1:3]
+    o = oracle.gdn_tree(parent, S, q, k, v, a, b)
+    assert np.array_equal(o[1:3], o[3:5])
+    _, L, Kc, Vc, q, kt, vt = _attn_case(12, n=5)
+    for arr in (q, kt, vt):
+        arr[3:5] = arr[1:3]
+    o = oracle.attn_tree(parent, L, Kc, Vc, q, kt, vt)
+    assert np.array_equal(o[1:3], o[3:5])
+
+
+def pin_commit_and_rollback_rules():
+    parent = [-1, 0, 1, 2, 1, 4]
+    assert oracle.leading_chain(parent) == 4
+    assert oracle.rollback_plan(parent, 50, 50) == []
+    assert oracle.rollback_plan(parent, 50, 53) == [0, 1, 2]
+    assert oracle.rollback_plan(parent, 50, 54) == [0, 1, 2, 3]
+    assert oracle.rollback_plan(parent, 50, 55) is None
+    assert oracle.rollback_plan(parent, 50, 49) is None
+    assert oracle.valid_path(parent, [0, 1, 4, 5])
+    assert not oracle.valid_path(parent, [0, 4])
+    assert not oracle.valid_path(parent, [1, 2])
+    kt = np.arange(6 * 2 * 3).reshape(6, 2, 3)
+    rows = oracle.commit_kv_rows(kt, [0, 1, 4])
+    assert rows.shape == (2, 3, 3) and np.array_equal(rows[1, 2], kt[4, 1])
+
+
+PINS = {name[4:]: fn for name, fn in list(globals().items()) if name.startswith("pin_")}
+
+
+@pytest.mark.parametrize("name", sorted(PINS))
+def test_pin(name):
+    PINS[name]()
