@@ -1,0 +1,609 @@
+// engine.cpp - host side of libhdt: validation, launch planning and the
+// pending-round bookkeeping behind the C ABI declared in include/hdt.h.
+//
+// The verbs follow "Adding a model" (step 4 of "The adapter path in ten
+// steps": forward_tree, forward_block, commit_tree, rollback_to, kv.length,
+// reset) and the round of "One request, end to end" (section 2.6: one pass
+// over the merged tree, then the accepted path's KV rows and recurrent state
+// are committed).  Each call is step-granular and keeps activations on the
+// device ("How ignis serves a request", "The shape of the process").
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "hdt.h"
+#include "launch.h"
+
+using namespace hdt;
+
+namespace {
+
+constexpr int kSplitCUs = 256;      // splits are sized so one layer spreads over this many items
+constexpr int64_t kSplitMin = 256;  // smallest split, in keys
+constexpr int64_t kSplitMax = 16384;
+
+struct SlotState {
+  hdt_slot_desc d{};
+  int32_t split = 0;
+  int32_t nsplit_cap = 0;
+  float *u_pend = nullptr;
+  void *k_pend = nullptr;
+  void *a_pend = nullptr;
+  float *part_acc = nullptr;
+  float *part_ml = nullptr;
+  bool pending = false;
+  int32_t n = 0;
+  int32_t chain = 0;
+  int8_t parent[kMaxNodes]{};
+  int8_t depth[kMaxNodes]{};
+};
+
+struct EventPair {
+  hipEvent_t a, b;
+  int kind;
+};
+
+}  // namespace
+
+struct hdt_engine {
+  hdt_model_desc desc{};
+  std::vector<uint8_t> kind;
+  std::vector<int32_t> kind_index;  // index of layer l among layers of its kind
+  int32_t n_gdn = 0, n_attn = 0;
+  int32_t esz = 2;
+  std::vector<SlotState> slots;
+  std::string err;
+  bool allocated = false;
+  int max_lds = 0;  // dynamic LDS a workgroup may use on the device
+  bool profiling = false;
+  std::vector<EventPair> ev_live;
+  std::vector<EventPair> ev_pool;
+  double prof_ms[4] = {0, 0, 0, 0};
+  int64_t prof_count[4] = {0, 0, 0, 0};
+};
+
+namespace {
+
+hdt_status fail(hdt_engine *e, hdt_status code, const char *fmt, ...) {
+  if (e) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    e->err = buf;
+  }
+  return code;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t pow2_floor(int64_t x) {
+  int64_t p = 1;
+  while (p * 2 <= x) p *= 2;
+  return p;
+}
+
+// Split size of a slot: a power of two between kSplitMin and kSplitMax chosen so
+// that a full cache gives about kSplitCUs (kv head, split) items.  It depends on
+// the capacity alone, never on the current length.
+int32_t split_for(int64_t capacity, int32_t hkv) {
+  int64_t s = pow2_floor(std::max<int64_t>(1, capacity * hkv / kSplitCUs));
+  s = std::max(kSplitMin, std::min(kSplitMax, s));
+  return static_cast<int32_t>(s);
+}
+
+// Validates a parent array and fills depth; returns false for a non-tree.
+bool plan_tree(int32_t n, const int32_t *parent, int8_t *par, int8_t *dep, int32_t *chain) {
+  if (n < 1 || n > kMaxNodes || !parent || parent[0] != -1) return false;
+  for (int i = 1; i < n; ++i)
+    if (parent[i] < 0 || parent[i] >= i) return false;
+  for (int i = 0; i < n; ++i) {
+    par[i] = static_cast<int8_t>(parent[i]);
+    dep[i] = static_cast<int8_t>(i == 0 ? 0 : dep[parent[i]] + 1);
+  }
+  int c = 1;
+  while (c < n && parent[c] == c - 1) ++c;
+  *chain = c;
+  return true;
+}
+
+hdt_status check_hip(hdt_engine *e, hipError_t r, const char *what) {
+  if (r != hipSuccess) return fail(e, HDT_E_HIP, "%s: %s", what, hipGetErrorString(r));
+  return HDT_OK;
+}
+
+hdt_status ensure_alloc(hdt_engine *e) {
+  if (e->allocated) return HDT_OK;
+  const hdt_model_desc &m = e->desc;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&e->max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    return fail(e, HDT_E_HIP, "cannot query the current HIP device");
+  const int G = m.attn_hkv > 0 ? m.attn_hq / m.attn_hkv : 0;
+  for (auto &s : e->slots) {
+    const size_t nm = static_cast<size_t>(m.max_nodes);
+    if (e->n_gdn > 0) {
+      const size_t ng = static_cast<size_t>(e->n_gdn);
+      if (hipMalloc(&s.u_pend, ng * nm * m.gdn_hv * m.gdn_dv * sizeof(float)) != hipSuccess ||
+          hipMalloc(&s.k_pend, ng * nm * m.gdn_hk * m.gdn_dk * e->esz) != hipSuccess ||
+          hipMalloc(&s.a_pend, ng * nm * m.gdn_hv * e->esz) != hipSuccess)
+        return fail(e, HDT_E_HIP, "hipMalloc of the pending GDN buffers failed");
+    }
+    if (e->n_attn > 0) {
+      const size_t rows = nm * G;
+      const size_t base = static_cast<size_t>(m.attn_hkv) * s.nsplit_cap * rows;
+      if (hipMalloc(&s.part_acc, base * m.attn_d * sizeof(float)) != hipSuccess ||
+          hipMalloc(&s.part_ml, base * 2 * sizeof(float)) != hipSuccess)
+        return fail(e, HDT_E_HIP, "hipMalloc of the attention partials failed");
+    }
+  }
+  e->allocated = true;
+  return HDT_OK;
+}
+
+void free_scratch(hdt_engine *e) {
+  for (auto &s : e->slots) {
+    (void)hipFree(s.u_pend);
+    (void)hipFree(s.k_pend);
+    (void)hipFree(s.a_pend);
+    (void)hipFree(s.part_acc);
+    (void)hipFree(s.part_ml);
+    s.u_pend = nullptr;
+    s.k_pend = s.a_pend = nullptr;
+    s.part_acc = s.part_ml = nullptr;
+  }
+  e->allocated = false;
+}
+
+// Records an event pair around one launch when profiling is on.
+struct ProfScope {
+  hdt_engine *e;
+  hipStream_t s;
+  int kind;
+  EventPair ev{};
+  bool on = false;
+  ProfScope(hdt_engine *e_, hipStream_t s_, int k) : e(e_), s(s_), kind(k) {
+    if (!e->profiling) return;
+    if (!e->ev_pool.empty()) {
+      ev = e->ev_pool.back();
+      e->ev_pool.pop_back();
+    } else if (hipEventCreate(&ev.a) != hipSuccess || hipEventCreate(&ev.b) != hipSuccess) {
+      return;
+    }
+    ev.kind = k;
+    on = hipEventRecord(ev.a, s) == hipSuccess;
+  }
+  ~ProfScope() {
+    if (!on) return;
+    (void)hipEventRecord(ev.b, s);
+    e->ev_live.push_back(ev);
+  }
+};
+
+hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, const int8_t (*par)[kMaxNodes],
+                          const int8_t (*dep)[kMaxNodes], hipStream_t stream) {
+  const hdt_model_desc &m = e->desc;
+  const int bf = m.io_dtype == HDT_BF16;
+  const int G = m.attn_hkv > 0 ? m.attn_hq / m.attn_hkv : 1;
+  int32_t n_max = 0;
+  for (int t = 0; t < n_trees; ++t) n_max = std::max(n_max, trees[t].n_nodes);
+
+  for (int l = 0; l < m.n_layers; ++l) {
+    const int ki = e->kind_index[l];
+    if (e->kind[l] == 0) {
+      GdnLaunch a;
+      std::memset(&a, 0, sizeof a);
+      a.n_trees = n_trees;
+      a.hk = m.gdn_hk;
+      a.hv = m.gdn_hv;
+      a.dv = m.gdn_dv;
+      a.n_max = n_max;
+      a.scale = m.gdn_scale;
+      int32_t wg = 0;
+      for (int t = 0; t < n_trees; ++t) {
+        const hdt_tree &tr = trees[t];
+        SlotState &s = e->slots[tr.slot];
+        const hdt_layer_io &io = tr.io[l];
+        GdnTree &g = a.t[t];
+        g.q = io.q;
+        g.k = io.k;
+        g.v = io.v;
+        g.alpha = io.alpha;
+        g.beta = io.beta;
+        g.o = io.o;
+        const size_t hs = static_cast<size_t>(m.gdn_hv) * m.gdn_dv * m.gdn_dk;
+        g.state = s.d.gdn_state + static_cast<size_t>(ki) * hs;
+        const size_t nm = static_cast<size_t>(m.max_nodes);
+        g.u_pend = s.u_pend + static_cast<size_t>(ki) * nm * m.gdn_hv * m.gdn_dv;
+        g.k_pend = static_cast<char *>(s.k_pend) +
+                   static_cast<size_t>(ki) * nm * m.gdn_hk * m.gdn_dk * e->esz;
+        g.a_pend = static_cast<char *>(s.a_pend) + static_cast<size_t>(ki) * nm * m.gdn_hv * e->esz;
+        g.n = tr.n_nodes;
+        g.wg_begin = wg;
+        std::memcpy(g.parent, par[t], kMaxNodes);
+        wg += m.gdn_hv * (m.gdn_dv / kGdnCols);
+      }
+      ProfScope p(e, stream, 0);
+      hdt_status st = check_hip(e, launch_gdn_tree(a, m.gdn_dk, bf, stream), "GDN tree launch");
+      if (st != HDT_OK) return st;
+    } else {
+      AttnLaunch a;
+      std::memset(&a, 0, sizeof a);
+      a.n_trees = n_trees;
+      a.hq = m.attn_hq;
+      a.hkv = m.attn_hkv;
+      a.n_max = n_max;
+      a.c2 = m.attn_scale * 1.4426950408889634f;
+      FoldLaunch f;
+      std::memset(&f, 0, sizeof f);
+      f.n_trees = n_trees;
+      f.hq = m.attn_hq;
+      f.hkv = m.attn_hkv;
+      int32_t items = 0, rows = 0;
+      for (int t = 0; t < n_trees; ++t) {
+        const hdt_tree &tr = trees[t];
+        SlotState &s = e->slots[tr.slot];
+        const hdt_layer_io &io = tr.io[l];
+        AttnTree &x = a.t[t];
+        const size_t view = static_cast<size_t>(m.attn_hkv) * s.d.capacity * m.attn_d * e->esz;
+        x.q = io.q;
+        x.kt = io.k;
+        x.vt = io.v;
+        x.kc = static_cast<char *>(s.d.k_cache) + static_cast<size_t>(ki) * view;
+        x.vc = static_cast<char *>(s.d.v_cache) + static_cast<size_t>(ki) * view;
+        x.part_acc = s.part_acc;
+        x.part_ml = s.part_ml;
+        x.L = s.d.length;
+        x.cap = s.d.capacity;
+        x.n = tr.n_nodes;
+        x.split = s.split;
+        x.n_shared = static_cast<int32_t>(s.d.length / s.split);
+        x.nsplit_cap = s.nsplit_cap;
+        x.rows_cap = m.max_nodes * G;
+        x.item_begin = items;
+        x.n_tail_items = m.attn_hkv * ((tr.n_nodes + kAttnWaves - 1) / kAttnWaves);
+        const int blocks16 = (tr.n_nodes * G + 15) / 16;
+        x.row_groups = (blocks16 + kAttnWaves - 1) / kAttnWaves;
+        std::memcpy(x.parent, par[t], kMaxNodes);
+        std::memcpy(x.depth, dep[t], kMaxNodes);
+        items += x.n_tail_items + m.attn_hkv * x.n_shared * x.row_groups;
+
+        FoldTree &y = f.t[t];
+        y.part_acc = s.part_acc;
+        y.part_ml = s.part_ml;
+        y.o = io.o;
+        y.L = s.d.length;
+        y.n = tr.n_nodes;
+        y.split = s.split;
+        y.nsplit_cap = s.nsplit_cap;
+        y.rows_cap = x.rows_cap;
+        y.row_begin = rows;
+        std::memcpy(y.depth, dep[t], kMaxNodes);
+        rows += tr.n_nodes * m.attn_hq;
+      }
+      {
+        ProfScope p(e, stream, 1);
+        hdt_status st = check_hip(e, launch_attn_split(a, m.attn_d, bf, items, stream),
+                                  "attention split launch");
+        if (st != HDT_OK) return st;
+      }
+      {
+        ProfScope p(e, stream, 2);
+        hdt_status st = check_hip(e, launch_attn_fold(f, m.attn_d, bf, rows, stream),
+                                  "attention fold launch");
+        if (st != HDT_OK) return st;
+      }
+    }
+  }
+  return HDT_OK;
+}
+
+hdt_status do_commit(hdt_engine *e, int32_t slot, const int32_t *path, int32_t m_len,
+                     hipStream_t stream) {
+  const hdt_model_desc &m = e->desc;
+  SlotState &s = e->slots[slot];
+  CommitLaunch c;
+  std::memset(&c, 0, sizeof c);
+  c.state = s.d.gdn_state;
+  c.u_pend = s.u_pend;
+  c.k_pend = s.k_pend;
+  c.a_pend = s.a_pend;
+  c.kc = s.d.k_cache;
+  c.vc = s.d.v_cache;
+  c.L = s.d.length;
+  c.cap = s.d.capacity;
+  c.n_gdn = e->n_gdn;
+  c.n_attn = e->n_attn;
+  c.max_nodes = m.max_nodes;
+  c.hk = m.gdn_hk;
+  c.hv = m.gdn_hv;
+  c.dv = m.gdn_dv;
+  c.hkv = m.attn_hkv;
+  c.D = m.attn_d;
+  c.gdn_blocks = e->n_gdn > 0 ? e->n_gdn * m.gdn_hv * (m.gdn_dv / kGdnCols) : 0;
+  c.m = m_len;
+  for (int d = 0; d < m_len; ++d) c.path[d] = static_cast<int8_t>(path[d]);
+  const int blocks = c.gdn_blocks + (e->n_attn > 0 ? e->n_attn * m.attn_hkv : 0);
+  if (blocks > 0) {
+    ProfScope p(e, stream, 3);
+    const int dk = e->n_gdn > 0 ? m.gdn_dk : 64;
+    hdt_status st = check_hip(e, launch_commit(c, dk, m.io_dtype == HDT_BF16, blocks, stream),
+                              "commit launch");
+    if (st != HDT_OK) return st;
+  }
+  s.d.length += m_len;
+  s.pending = false;
+  return HDT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hdt_status hdt_create(const hdt_model_desc *desc, int32_t n_slots, const hdt_slot_desc *slots,
+                      hdt_engine **out) {
+  if (!out) return HDT_E_INVALID;
+  *out = nullptr;
+  if (!desc || !slots || n_slots < 1) return HDT_E_INVALID;
+  const hdt_model_desc &m = *desc;
+  if (m.n_layers < 1 || !m.layer_kind) return HDT_E_INVALID;
+  int n_gdn = 0, n_attn = 0;
+  for (int l = 0; l < m.n_layers; ++l) {
+    if (m.layer_kind[l] > 1) return HDT_E_INVALID;
+    (m.layer_kind[l] == 0 ? n_gdn : n_attn)++;
+  }
+  if (m.io_dtype != HDT_F32 && m.io_dtype != HDT_BF16) return HDT_E_INVALID;
+  if (m.max_nodes < 1 || m.max_nodes > HDT_MAX_NODES) return HDT_E_INVALID;
+  if (n_gdn > 0) {
+    if (m.gdn_hk < 1 || m.gdn_hv < m.gdn_hk || m.gdn_hv % m.gdn_hk != 0) return HDT_E_INVALID;
+    if (m.gdn_dk != m.gdn_dv || (m.gdn_dk != 64 && m.gdn_dk != 128)) return HDT_E_UNSUPPORTED;
+  }
+  if (n_attn > 0) {
+    if (m.attn_hkv < 1 || m.attn_hq < m.attn_hkv || m.attn_hq % m.attn_hkv != 0)
+      return HDT_E_INVALID;
+    if (m.attn_hq / m.attn_hkv > 16) return HDT_E_UNSUPPORTED;
+    if (m.attn_d != 64 && m.attn_d != 256) return HDT_E_UNSUPPORTED;
+    if (m.io_dtype == HDT_F32 && m.attn_d != 64) return HDT_E_UNSUPPORTED;
+  }
+  for (int i = 0; i < n_slots; ++i) {
+    const hdt_slot_desc &s = slots[i];
+    if (s.capacity < 1 || s.length < 0 || s.length > s.capacity) return HDT_E_INVALID;
+    if (s.capacity > (int64_t(1) << 31)) return HDT_E_UNSUPPORTED;
+    if (n_gdn > 0 && (!s.gdn_state || !aligned16(s.gdn_state))) return HDT_E_INVALID;
+    if (n_attn > 0 && (!s.k_cache || !s.v_cache || !aligned16(s.k_cache) || !aligned16(s.v_cache)))
+      return HDT_E_INVALID;
+  }
+  hdt_engine *e = new (std::nothrow) hdt_engine();
+  if (!e) return HDT_E_INVALID;
+  e->desc = m;
+  e->kind.assign(m.layer_kind, m.layer_kind + m.n_layers);
+  e->desc.layer_kind = e->kind.data();
+  if (e->desc.gdn_scale <= 0.0f && n_gdn > 0) e->desc.gdn_scale = 1.0f / std::sqrt(float(m.gdn_dk));
+  if (e->desc.attn_scale <= 0.0f && n_attn > 0) e->desc.attn_scale = 1.0f / std::sqrt(float(m.attn_d));
+  e->n_gdn = n_gdn;
+  e->n_attn = n_attn;
+  e->esz = m.io_dtype == HDT_BF16 ? 2 : 4;
+  int gi = 0, ai = 0;
+  for (int l = 0; l < m.n_layers; ++l) e->kind_index.push_back(m.layer_kind[l] == 0 ? gi++ : ai++);
+  e->slots.resize(n_slots);
+  for (int i = 0; i < n_slots; ++i) {
+    SlotState &s = e->slots[i];
+    s.d = slots[i];
+    s.split = split_for(s.d.capacity, std::max(1, m.attn_hkv));
+    s.nsplit_cap = static_cast<int32_t>((s.d.capacity + s.split - 1) / s.split);
+  }
+  *out = e;
+  return HDT_OK;
+}
+
+void hdt_destroy(hdt_engine *e) {
+  if (!e) return;
+  if (e->allocated || !e->ev_live.empty() || !e->ev_pool.empty()) (void)hipDeviceSynchronize();
+  free_scratch(e);
+  for (auto &p : e->ev_live) {
+    (void)hipEventDestroy(p.a);
+    (void)hipEventDestroy(p.b);
+  }
+  for (auto &p : e->ev_pool) {
+    (void)hipEventDestroy(p.a);
+    (void)hipEventDestroy(p.b);
+  }
+  delete e;
+}
+
+hdt_status hdt_forward_tree(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, void *stream) {
+  if (!e) return HDT_E_INVALID;
+  if (n_trees < 1 || n_trees > HDT_MAX_TREES || !trees)
+    return fail(e, HDT_E_INVALID, "n_trees must be 1..%d", HDT_MAX_TREES);
+  const hdt_model_desc &m = e->desc;
+  int8_t par[HDT_MAX_TREES][kMaxNodes];
+  int8_t dep[HDT_MAX_TREES][kMaxNodes];
+  int32_t chain[HDT_MAX_TREES];
+  for (int t = 0; t < n_trees; ++t) {
+    const hdt_tree &tr = trees[t];
+    if (tr.slot < 0 || tr.slot >= static_cast<int32_t>(e->slots.size()))
+      return fail(e, HDT_E_INVALID, "tree %d: slot %d out of range", t, tr.slot);
+    for (int u = 0; u < t; ++u)
+      if (trees[u].slot == tr.slot) return fail(e, HDT_E_INVALID, "slot %d appears twice", tr.slot);
+    const SlotState &s = e->slots[tr.slot];
+    if (s.pending) return fail(e, HDT_E_ORDER, "slot %d has a pending round", tr.slot);
+    if (tr.n_nodes < 1 || tr.n_nodes > m.max_nodes)
+      return fail(e, HDT_E_INVALID, "tree %d: %d nodes (max_nodes %d)", t, tr.n_nodes, m.max_nodes);
+    std::memset(par[t], 0, kMaxNodes);
+    std::memset(dep[t], 0, kMaxNodes);
+    if (!plan_tree(tr.n_nodes, tr.parent, par[t], dep[t], &chain[t]))
+      return fail(e, HDT_E_TREE, "tree %d: parent array is not a tree", t);
+    if (s.d.length + tr.n_nodes > s.d.capacity)
+      return fail(e, HDT_E_CAPACITY, "slot %d: length %lld + %d nodes exceeds capacity %lld",
+                  tr.slot, (long long)s.d.length, tr.n_nodes, (long long)s.d.capacity);
+    if (!tr.io) return fail(e, HDT_E_INVALID, "tree %d: io is NULL", t);
+    for (int l = 0; l < m.n_layers; ++l) {
+      const hdt_layer_io &io = tr.io[l];
+      if (!io.q || !io.k || !io.v || !io.o)
+        return fail(e, HDT_E_INVALID, "tree %d layer %d: NULL q/k/v/o", t, l);
+      if (e->kind[l] == 0 && (!io.alpha || !io.beta))
+        return fail(e, HDT_E_INVALID, "tree %d layer %d: NULL alpha/beta", t, l);
+      if (e->kind[l] == 1 && (!aligned16(io.q) || !aligned16(io.k) || !aligned16(io.v) ||
+                              !aligned16(io.o)))
+        return fail(e, HDT_E_INVALID, "tree %d layer %d: attention buffers must be 16-byte aligned",
+                    t, l);
+    }
+  }
+  hdt_status st = ensure_alloc(e);
+  if (st != HDT_OK) return st;
+  {
+    int32_t n_max = 0;
+    for (int t = 0; t < n_trees; ++t) n_max = std::max(n_max, trees[t].n_nodes);
+    const size_t need_g = e->n_gdn > 0 ? gdn_lds_bytes(m.gdn_dk, n_max) : 0;
+    const size_t need_a = e->n_attn > 0 ? attn_lds_bytes(m.attn_d, m.io_dtype == HDT_BF16, n_max) : 0;
+    if (need_g > static_cast<size_t>(e->max_lds) || need_a > static_cast<size_t>(e->max_lds))
+      return fail(e, HDT_E_UNSUPPORTED, "kernels need %zu / %zu bytes of LDS; the device allows %d",
+                  need_g, need_a, e->max_lds);
+  }
+  st = launch_forward(e, n_trees, trees, par, dep, static_cast<hipStream_t>(stream));
+  if (st != HDT_OK) return st;
+  for (int t = 0; t < n_trees; ++t) {
+    SlotState &s = e->slots[trees[t].slot];
+    s.pending = true;
+    s.n = trees[t].n_nodes;
+    s.chain = chain[t];
+    std::memcpy(s.parent, par[t], kMaxNodes);
+    std::memcpy(s.depth, dep[t], kMaxNodes);
+  }
+  e->err.clear();
+  return HDT_OK;
+}
+
+hdt_status hdt_forward_block(hdt_engine *e, int32_t slot, int32_t n, const hdt_layer_io *io,
+                             void *stream) {
+  if (!e) return HDT_E_INVALID;
+  if (n < 1 || n > HDT_MAX_NODES) return fail(e, HDT_E_INVALID, "block of %d tokens", n);
+  int32_t parent[HDT_MAX_NODES];
+  for (int i = 0; i < n; ++i) parent[i] = i - 1;
+  hdt_tree t{slot, n, parent, io};
+  return hdt_forward_tree(e, 1, &t, stream);
+}
+
+hdt_status hdt_commit_tree(hdt_engine *e, int32_t slot, const int32_t *path, int32_t m,
+                           void *stream) {
+  if (!e) return HDT_E_INVALID;
+  if (slot < 0 || slot >= static_cast<int32_t>(e->slots.size()))
+    return fail(e, HDT_E_INVALID, "slot %d out of range", slot);
+  SlotState &s = e->slots[slot];
+  if (!s.pending) return fail(e, HDT_E_ORDER, "slot %d has no pending round", slot);
+  if (!path || m < 1 || m > s.n) return fail(e, HDT_E_PATH, "path length %d (tree of %d)", m, s.n);
+  if (path[0] != 0) return fail(e, HDT_E_PATH, "path must start at the root");
+  for (int d = 1; d < m; ++d)
+    if (path[d] < 0 || path[d] >= s.n || s.parent[path[d]] != path[d - 1])
+      return fail(e, HDT_E_PATH, "path[%d] = %d is not a child of %d", d, path[d], path[d - 1]);
+  if (commit_lds_bytes(e->desc.attn_d, e->desc.io_dtype == HDT_BF16, m) > static_cast<size_t>(e->max_lds))
+    return fail(e, HDT_E_UNSUPPORTED, "commit of %d rows needs more LDS than the device allows", m);
+  hdt_status st = do_commit(e, slot, path, m, static_cast<hipStream_t>(stream));
+  if (st == HDT_OK) e->err.clear();
+  return st;
+}
+
+hdt_status hdt_rollback_to(hdt_engine *e, int32_t slot, int64_t n, void *stream) {
+  if (!e) return HDT_E_INVALID;
+  if (slot < 0 || slot >= static_cast<int32_t>(e->slots.size()))
+    return fail(e, HDT_E_INVALID, "slot %d out of range", slot);
+  SlotState &s = e->slots[slot];
+  const int64_t L = s.d.length;
+  if (n < L) return fail(e, HDT_E_UNSUPPORTED, "rollback below the committed length needs state anchors");
+  if (n == L) {
+    s.pending = false;
+    e->err.clear();
+    return HDT_OK;
+  }
+  if (!s.pending) return fail(e, HDT_E_ORDER, "rollback_to(%lld) past length %lld with no pending round",
+                              (long long)n, (long long)L);
+  if (n > L + s.chain)
+    return fail(e, HDT_E_INVALID, "rollback_to(%lld): only the leading chain of %d can be kept",
+                (long long)n, s.chain);
+  int32_t path[HDT_MAX_NODES];
+  const int32_t m = static_cast<int32_t>(n - L);
+  for (int d = 0; d < m; ++d) path[d] = d;
+  hdt_status st = do_commit(e, slot, path, m, static_cast<hipStream_t>(stream));
+  if (st == HDT_OK) e->err.clear();
+  return st;
+}
+
+hdt_status hdt_kv_length(const hdt_engine *e, int32_t slot, int64_t *out) {
+  if (!e || !out || slot < 0 || slot >= static_cast<int32_t>(e->slots.size())) return HDT_E_INVALID;
+  *out = e->slots[slot].d.length;
+  return HDT_OK;
+}
+
+hdt_status hdt_reset(hdt_engine *e, int32_t slot, int64_t length) {
+  if (!e) return HDT_E_INVALID;
+  if (slot < 0 || slot >= static_cast<int32_t>(e->slots.size()))
+    return fail(e, HDT_E_INVALID, "slot %d out of range", slot);
+  SlotState &s = e->slots[slot];
+  if (length < 0 || length > s.d.capacity)
+    return fail(e, HDT_E_INVALID, "length %lld outside [0, %lld]", (long long)length,
+                (long long)s.d.capacity);
+  s.d.length = length;
+  s.pending = false;
+  e->err.clear();
+  return HDT_OK;
+}
+
+hdt_status hdt_tree_meta(int32_t n, const int32_t *parent, int64_t L, int32_t *depth,
+                         uint64_t *mask, int32_t *anc, int64_t *pos) {
+  int8_t par[kMaxNodes], dep[kMaxNodes];
+  int32_t chain;
+  if (!plan_tree(n, parent, par, dep, &chain)) return HDT_E_TREE;
+  uint64_t mk[kMaxNodes];
+  for (int i = 0; i < n; ++i) {
+    mk[i] = (i == 0 ? 0 : mk[par[i]]) | (uint64_t(1) << i);
+    if (depth) depth[i] = dep[i];
+    if (mask) mask[i] = mk[i];
+    if (pos) pos[i] = L + dep[i];
+    if (anc) {
+      for (int d = 0; d < kMaxNodes; ++d) anc[i * kMaxNodes + d] = -1;
+      for (int x = i; x >= 0; x = par[x]) anc[i * kMaxNodes + dep[x]] = x;
+    }
+  }
+  return HDT_OK;
+}
+
+hdt_status hdt_split_size(const hdt_engine *e, int32_t slot, int64_t *out) {
+  if (!e || !out || slot < 0 || slot >= static_cast<int32_t>(e->slots.size())) return HDT_E_INVALID;
+  *out = e->slots[slot].split;
+  return HDT_OK;
+}
+
+hdt_status hdt_profile(hdt_engine *e, int32_t enable) {
+  if (!e) return HDT_E_INVALID;
+  e->profiling = enable != 0;
+  return HDT_OK;
+}
+
+hdt_status hdt_profile_read(hdt_engine *e, int32_t kind, double *ms, int64_t *launches) {
+  if (!e || kind < 0 || kind > 3 || !ms || !launches) return HDT_E_INVALID;
+  for (auto &p : e->ev_live) {
+    if (hipEventSynchronize(p.b) != hipSuccess) return fail(e, HDT_E_HIP, "event wait failed");
+    float t = 0.0f;
+    if (hipEventElapsedTime(&t, p.a, p.b) != hipSuccess) return fail(e, HDT_E_HIP, "event time failed");
+    e->prof_ms[p.kind] += t;
+    e->prof_count[p.kind] += 1;
+    e->ev_pool.push_back(p);
+  }
+  e->ev_live.clear();
+  *ms = e->prof_ms[kind];
+  *launches = e->prof_count[kind];
+  e->prof_ms[kind] = 0.0;
+  e->prof_count[kind] = 0;
+  return HDT_OK;
+}
+
+const char *hdt_last_error(const hdt_engine *e) { return e ? e->err.c_str() : "no engine"; }
+
+}  // extern "C"

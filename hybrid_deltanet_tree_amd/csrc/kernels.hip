@@ -1,0 +1,902 @@
+// kernels.hip - tree-verify kernels for CDNA4 (gfx950).
+//
+//  gdn_tree_kernel    one Gated DeltaNet layer over a tree: every value head
+//                     advances its recurrent state along every root-to-node path
+//                     ("Adding a model", "What is still specific to Qwen3.8":
+//                     state heads of 128 by 128; the step is the published gated
+//                     delta rule).
+//  attn_split_kernel  one attention layer: ancestor-masked GQA over the committed
+//                     rows plus the tree's own rows ("One request, end to end",
+//                     2.6), as per-split partial softmax results.
+//  attn_fold_kernel   folds a row's split partials in ascending split order.
+//  commit_kernel      commit_tree: replays the accepted path's rank-1 steps into
+//                     every GDN layer's committed state and gathers the path's
+//                     pending K/V rows into place ("One request, end to end", 2.6).
+//
+// Bit-exactness (a verified row equals the decode step's row, "Adding a model",
+// step 4 of "The adapter path in ten steps"): every value a row gets is a
+// function of that row's inputs alone.
+//  - GDN: one step function (decay, k^T S with a fixed lane reduction, rank-1
+//    write, S q with the same reduction) serves tree nodes, decode steps, the
+//    replays that restore a branch point, and commit.  The write is
+//    fmaf(k, u, alpha * P) everywhere, so a replay or commit reproduces the
+//    pass's state bit for bit.
+//  - Attention: tiles of kTile keys and splits of `split` keys are anchored at
+//    absolute positions; each tile is reduced by the same MFMA sequence whatever
+//    other rows share the instruction; masked key slots hold exact zeros; splits
+//    fold in ascending order.
+#include "launch.h"
+
+#include <type_traits>
+
+#pragma clang fp contract(off)
+
+namespace hdt {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+template <bool BF>
+using io_t = typename std::conditional<BF, uint16_t, float>::type;
+
+template <bool BF>
+__device__ __forceinline__ float ld_io(const void *p, int64_t i) {
+  if constexpr (BF) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(p)[i]) << 16);
+  } else {
+    return static_cast<const float *>(p)[i];
+  }
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+template <bool BF>
+__device__ __forceinline__ void st_io(void *p, int64_t i, float v) {
+  if constexpr (BF) {
+    static_cast<uint16_t *>(p)[i] = bf16_bits(v);
+  } else {
+    static_cast<float *>(p)[i] = v;
+  }
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the same bits
+// (each stage adds the same two partials in either order).
+__device__ __forceinline__ float rowsum16(float x) {
+  x = x + dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = x + dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = x + dpp<0x141>(x);  // row_half_mirror
+  x = x + dpp<0x140>(x);  // row_mirror
+  return x;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ============================================================================ GDN
+
+// LDS layout of the GDN walk (floats, then bytes): k[n][dk], s*q[n][dk],
+// v[n][16], alpha[n], beta[n], u[n][16], o[n][16], depth[n] (int), anc[n][64] (int8).
+__host__ __device__ constexpr size_t gdn_lds_floats(int dk, int n) {
+  return static_cast<size_t>(n) * (2 * dk + 3 * kGdnCols + 3);
+}
+
+template <bool BF, int DK>
+__global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P) {
+  constexpr int R = DK / 16;  // key rows per lane; 16 lanes hold one value column
+  extern __shared__ __align__(16) float g_lds[];
+  const int bid = blockIdx.x;
+  int t = 0;
+  while (t + 1 < P.n_trees && bid >= P.t[t + 1].wg_begin) ++t;
+  const GdnTree &T = P.t[t];
+  const int n = T.n;
+  const int nm = P.n_max;
+  float *kf = g_lds;
+  float *qs = kf + nm * DK;
+  float *vl = qs + nm * DK;
+  float *al = vl + nm * kGdnCols;
+  float *be = al + nm;
+  float *ul = be + nm;
+  float *ol = ul + nm * kGdnCols;
+  int *dep = reinterpret_cast<int *>(ol + nm * kGdnCols);
+  int8_t *anc = reinterpret_cast<int8_t *>(dep + nm);
+
+  const int cgroups = P.dv / kGdnCols;
+  const int local = bid - T.wg_begin;
+  const int h = local / cgroups, cg = local % cgroups;
+  const int ratio = P.hv / P.hk, qh = h / ratio;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lc = wave * 4 + (lane >> 4);  // value column within the workgroup
+  const int g = lane & 15;                // key rows [g*R, g*R+R)
+  const int col = cg * kGdnCols + lc;
+
+  // Stage the tree's inputs for this head.
+  for (int e = tid; e < n * DK; e += kGdnThreads) {
+    const int i = e / DK, a = e % DK;
+    const int64_t src = (static_cast<int64_t>(i) * P.hk + qh) * DK + a;
+    kf[e] = ld_io<BF>(T.k, src);
+    qs[e] = P.scale * ld_io<BF>(T.q, src);
+  }
+  for (int e = tid; e < n * kGdnCols; e += kGdnThreads) {
+    const int i = e / kGdnCols, c = e % kGdnCols;
+    vl[e] = ld_io<BF>(T.v, (static_cast<int64_t>(i) * P.hv + h) * P.dv + cg * kGdnCols + c);
+  }
+  for (int e = tid; e < n; e += kGdnThreads) {
+    al[e] = ld_io<BF>(T.alpha, static_cast<int64_t>(e) * P.hv + h);
+    be[e] = ld_io<BF>(T.beta, static_cast<int64_t>(e) * P.hv + h);
+    int d = 0;
+    for (int x = T.parent[e]; x >= 0; x = T.parent[x]) ++d;
+    dep[e] = d;
+    int x = e;
+    for (int k = d; k >= 0; --k) {
+      anc[e * kMaxNodes + k] = static_cast<int8_t>(x);
+      x = T.parent[x];
+    }
+  }
+  // Keep what commit needs: alpha of this head, k of this q/k head (raw bits).
+  if (cg == 0) {
+    io_t<BF> *ap = static_cast<io_t<BF> *>(T.a_pend);
+    const io_t<BF> *as = static_cast<const io_t<BF> *>(T.alpha);
+    for (int e = tid; e < n; e += kGdnThreads)
+      ap[static_cast<int64_t>(e) * P.hv + h] = as[static_cast<int64_t>(e) * P.hv + h];
+    if (h % ratio == 0) {
+      io_t<BF> *kp = static_cast<io_t<BF> *>(T.k_pend);
+      const io_t<BF> *ks = static_cast<const io_t<BF> *>(T.k);
+      for (int e = tid; e < n * DK; e += kGdnThreads) {
+        const int i = e / DK, a = e % DK;
+        const int64_t idx = (static_cast<int64_t>(i) * P.hk + qh) * DK + a;
+        kp[idx] = ks[idx];
+      }
+    }
+  }
+  __syncthreads();
+
+  float base[R], cur[R];
+  {
+    const float *sb = T.state + (static_cast<int64_t>(h) * P.dv + col) * DK + g * R;
+#pragma unroll
+    for (int a = 0; a < R; a += 4) {
+      const float4 x = *reinterpret_cast<const float4 *>(sb + a);
+      base[a] = x.x;
+      base[a + 1] = x.y;
+      base[a + 2] = x.z;
+      base[a + 3] = x.w;
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < R; ++a) cur[a] = base[a];
+
+  int cur_node = -1;
+  for (int i = 0; i < n; ++i) {
+    const int p = T.parent[i];
+    if (p != cur_node) {
+      // Restore the parent's state: replay its root path's rank-1 steps from
+      // the committed state with the same write as the step below.
+#pragma unroll
+      for (int a = 0; a < R; ++a) cur[a] = base[a];
+      if (p >= 0) {
+        const int dp = dep[p];
+        for (int d = 0; d <= dp; ++d) {
+          const int j = anc[p * kMaxNodes + d];
+          const float aj = al[j], uj = ul[j * kGdnCols + lc];
+          const float *kj = kf + j * DK + g * R;
+#pragma unroll
+          for (int a = 0; a < R; ++a) cur[a] = fmaf(kj[a], uj, aj * cur[a]);
+        }
+      }
+    }
+    const float *ki = kf + i * DK + g * R;
+    const float *qi = qs + i * DK + g * R;
+    const float ai = al[i], bi = be[i], vi = vl[i * kGdnCols + lc];
+    float A[R];
+    float r = 0.0f;
+#pragma unroll
+    for (int a = 0; a < R; ++a) {
+      A[a] = ai * cur[a];
+      r = fmaf(A[a], ki[a], r);
+    }
+    r = rowsum16(r);
+    const float u = bi * (vi - r);
+#pragma unroll
+    for (int a = 0; a < R; ++a) cur[a] = fmaf(ki[a], u, A[a]);
+    float o = 0.0f;
+#pragma unroll
+    for (int a = 0; a < R; ++a) o = fmaf(cur[a], qi[a], o);
+    o = rowsum16(o);
+    if (g == 0) {
+      ul[i * kGdnCols + lc] = u;
+      ol[i * kGdnCols + lc] = o;
+    }
+    cur_node = i;
+  }
+  __syncthreads();
+  for (int e = tid; e < n * kGdnCols; e += kGdnThreads) {
+    const int i = e / kGdnCols, c = e % kGdnCols;
+    const int64_t idx = (static_cast<int64_t>(i) * P.hv + h) * P.dv + cg * kGdnCols + c;
+    st_io<BF>(T.o, idx, ol[e]);
+    T.u_pend[idx] = ul[e];
+  }
+}
+
+// ============================================================================ attention
+
+template <bool BF, int D>
+struct AttnCfg {
+  static constexpr int ESZ = BF ? 2 : 4;
+  static constexpr int KQ = BF ? D / 32 : D / 4;  // k-steps of the score MFMA
+  static constexpr int DB = D / 16;               // 16-wide value blocks
+  static constexpr int ROWB = D * ESZ;            // bytes per cache row
+  static constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
+  // LDS tile: bf16 keys [64][D] (16-byte chunks XOR-swizzled by key), bf16 values
+  // transposed [D][64] (8-byte chunks XOR-swizzled by d); f32 keys [64][D+1],
+  // f32 values [64][D].
+  static constexpr int K_BYTES = BF ? 64 * D * 2 : 64 * (D + 1) * 4;
+  static constexpr int V_BYTES = BF ? D * 64 * 2 : 64 * D * 4;
+  static constexpr int TILE_BYTES = K_BYTES + V_BYTES;
+  static constexpr int KSW = (CPR > 16 ? 16 : CPR) - 1;
+  // register staging of one tile
+  static constexpr int NK = 64 * CPR;                        // key chunks
+  static constexpr int KPT = (NK + kAttnThreads - 1) / kAttnThreads;
+  static constexpr int NV = BF ? 16 * (D / 8) : 64 * CPR;    // bf16: 4 keys x 8 d units
+  static constexpr int VPT = (NV + kAttnThreads - 1) / kAttnThreads;
+  static constexpr int VCH = BF ? 4 : 1;                     // chunks per value unit
+};
+
+template <bool BF, int D>
+struct TileStage {
+  using C = AttnCfg<BF, D>;
+  uint4 k[C::KPT];
+  uint4 v[C::VPT][C::VCH];
+
+  // Rows [tb, tb+64) of one head; rows at or past `lim` read as zeros.
+  __device__ __forceinline__ void load(const unsigned char *kh, const unsigned char *vh,
+                                       int64_t tb, int64_t lim) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int x = 0; x < C::KPT; ++x) {
+      const int c = tid + x * kAttnThreads;
+      const int key = c / C::CPR, cc = c % C::CPR;
+      const int64_t pos = tb + key;
+      if (c < C::NK && pos < lim)
+        k[x] = *reinterpret_cast<const uint4 *>(kh + pos * C::ROWB + cc * 16);
+      else
+        k[x] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int x = 0; x < C::VPT; ++x) {
+      const int u = tid + x * kAttnThreads;
+      if constexpr (BF) {
+        const int kq = u % 16, dc = u / 16;  // keys 4kq..4kq+3, d 8dc..8dc+7
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const int64_t pos = tb + 4 * kq + y;
+          if (u < C::NV && pos < lim)
+            v[x][y] = *reinterpret_cast<const uint4 *>(vh + pos * C::ROWB + dc * 16);
+          else
+            v[x][y] = make_uint4(0, 0, 0, 0);
+        }
+      } else {
+        const int key = u / C::CPR, cc = u % C::CPR;
+        const int64_t pos = tb + key;
+        if (u < C::NV && pos < lim)
+          v[x][0] = *reinterpret_cast<const uint4 *>(vh + pos * C::ROWB + cc * 16);
+        else
+          v[x][0] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(unsigned char *lk, unsigned char *lv) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int x = 0; x < C::KPT; ++x) {
+      const int c = tid + x * kAttnThreads;
+      if (c >= C::NK) continue;
+      const int key = c / C::CPR, cc = c % C::CPR;
+      if constexpr (BF) {
+        *reinterpret_cast<uint4 *>(lk + key * C::ROWB + ((cc ^ (key & C::KSW)) * 16)) = k[x];
+      } else {
+        float *dst = reinterpret_cast<float *>(lk) + key * (D + 1) + cc * 4;
+        dst[0] = __uint_as_float(k[x].x);
+        dst[1] = __uint_as_float(k[x].y);
+        dst[2] = __uint_as_float(k[x].z);
+        dst[3] = __uint_as_float(k[x].w);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < C::VPT; ++x) {
+      const int u = tid + x * kAttnThreads;
+      if (u >= C::NV) continue;
+      if constexpr (BF) {
+        const int kq = u % 16, dc = u / 16;
+        const uint32_t w[4][4] = {{v[x][0].x, v[x][0].y, v[x][0].z, v[x][0].w},
+                                  {v[x][1].x, v[x][1].y, v[x][1].z, v[x][1].w},
+                                  {v[x][2].x, v[x][2].y, v[x][2].z, v[x][2].w},
+                                  {v[x][3].x, v[x][3].y, v[x][3].z, v[x][3].w}};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // d = 8dc + 2e (low halves) and 8dc + 2e + 1 (high halves) of keys 4kq..4kq+3
+          const int d0 = 8 * dc + 2 * e, d1 = d0 + 1;
+          uint2 lo, hi;
+          lo.x = (w[0][e] & 0xFFFFu) | (w[1][e] << 16);
+          lo.y = (w[2][e] & 0xFFFFu) | (w[3][e] << 16);
+          hi.x = (w[0][e] >> 16) | (w[1][e] & 0xFFFF0000u);
+          hi.y = (w[2][e] >> 16) | (w[3][e] & 0xFFFF0000u);
+          *reinterpret_cast<uint2 *>(lv + d0 * 128 + ((kq ^ (d0 & 15)) * 8)) = lo;
+          *reinterpret_cast<uint2 *>(lv + d1 * 128 + ((kq ^ (d1 & 15)) * 8)) = hi;
+        }
+      } else {
+        const int key = u / C::CPR, cc = u % C::CPR;
+        *reinterpret_cast<uint4 *>(lv + key * C::ROWB + cc * 16) = v[x][0];
+      }
+    }
+  }
+};
+
+// Online-softmax state of the 16 rows of one wave.  Lane (g, n) holds row n;
+// acc[db][i] is output element d = 16 db + 4 g + i of that row.
+template <int D>
+struct RowState {
+  floatx4 acc[D / 16];
+  float m, l;
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) acc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    l = 0.0f;
+  }
+};
+
+// One tile of kTile keys at absolute position tb, already in LDS, for the 16 rows
+// of this wave.  MASK: keys past `pos` (the wave's node position) are masked; the
+// tile builder left exact zeros in their K and V slots.
+template <bool BF, int D, bool MASK>
+__device__ __forceinline__ void attn_tile(RowState<D> &st, const void *qreg,
+                                          const unsigned char *lk, const unsigned char *lv,
+                                          int64_t tb, int64_t pos, float c2) {
+  using C = AttnCfg<BF, D>;
+  const int lane = threadIdx.x & 63, g = lane >> 4, ln = lane & 15;
+  floatx4 s[4];
+  // ---- scores S^T = K Q^T: lane (g, n) gets keys 16 kb + 4 g + i of row n
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    s[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int key = 16 * kb + ln;  // A-operand key of this lane
+#pragma unroll
+    for (int kk = 0; kk < C::KQ; ++kk) {
+      if constexpr (BF) {
+        const bf16x8 *qb = static_cast<const bf16x8 *>(qreg);
+        const int cc = 4 * kk + g;
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8 *>(lk + key * C::ROWB + ((cc ^ (key & C::KSW)) * 16));
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[kk], s[kb], 0, 0, 0);
+      } else {
+        const float *qf = static_cast<const float *>(qreg);
+        const float a = reinterpret_cast<const float *>(lk)[key * (D + 1) + 4 * kk + g];
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qf[kk], s[kb], 0, 0, 0);
+      }
+    }
+  }
+  // ---- online softmax in base 2
+  float z[4][4];
+  float mt = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = s[kb][i] * c2;
+      if constexpr (MASK) {
+        if (tb + 16 * kb + 4 * g + i > pos) x = -INFINITY;
+      }
+      z[kb][i] = x;
+      mt = fmaxf(mt, x);
+    }
+  mt = fmaxf(mt, __shfl_xor(mt, 16));
+  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  const float mn = fmaxf(st.m, mt);
+  const float corr = exp2_fast(st.m - mn);
+  float lt = 0.0f;
+  float p[4][4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float e = exp2_fast(z[kb][i] - mn);
+      if constexpr (BF) e = static_cast<float>(static_cast<__bf16>(e));
+      p[kb][i] = e;
+      lt = lt + e;
+    }
+  lt = lt + __shfl_xor(lt, 16);
+  lt = lt + __shfl_xor(lt, 32);
+  st.l = st.l * corr + lt;
+  st.m = mn;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) st.acc[db] = st.acc[db] * corr;
+
+  // ---- O^T += V^T P^T
+  if constexpr (BF) {
+#pragma unroll
+    for (int kk2 = 0; kk2 < 2; ++kk2) {
+      bf16x8 b;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        b[i] = static_cast<__bf16>(p[2 * kk2][i]);
+        b[4 + i] = static_cast<__bf16>(p[2 * kk2 + 1][i]);
+      }
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const int d = 16 * db + ln;
+        const uint2 lo =
+            *reinterpret_cast<const uint2 *>(lv + d * 128 + (((8 * kk2 + g) ^ (d & 15)) * 8));
+        const uint2 hi =
+            *reinterpret_cast<const uint2 *>(lv + d * 128 + (((8 * kk2 + 4 + g) ^ (d & 15)) * 8));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, st.acc[db], 0, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int d = 16 * db + ln;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = reinterpret_cast<const float *>(lv)[(16 * kb + 4 * g + i) * D + d];
+          st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, p[kb][i], st.acc[db], 0, 0, 0);
+        }
+    }
+  }
+}
+
+// Rewrite the LDS tile rows at positions [max(L, tb), tb + kTile) for one node:
+// position L + d holds the node's ancestor at depth d while d <= depth, zeros after.
+// Rows below L (committed) are left as loaded.
+template <bool BF, int D>
+__device__ __forceinline__ void build_node_rows(unsigned char *lk, unsigned char *lv,
+                                                const unsigned char *kt, const unsigned char *vt,
+                                                int hkv, int h, const int8_t *anc, int depth,
+                                                int64_t tb, int64_t L) {
+  using C = AttnCfg<BF, D>;
+  const int k0 = static_cast<int>(L > tb ? L - tb : 0);  // first key slot at or past L
+  const int nk = kTile - k0;
+  const int tid = threadIdx.x;
+  // keys: 16-byte chunks
+  for (int c = tid; c < nk * C::CPR; c += kAttnThreads) {
+    const int key = k0 + c / C::CPR, cc = c % C::CPR;
+    const int64_t d = tb + key - L;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (d <= depth)
+      x = *reinterpret_cast<const uint4 *>(
+          kt + (static_cast<int64_t>(anc[d]) * hkv + h) * C::ROWB + cc * 16);
+    if constexpr (BF) {
+      *reinterpret_cast<uint4 *>(lk + key * C::ROWB + ((cc ^ (key & C::KSW)) * 16)) = x;
+    } else {
+      float *dst = reinterpret_cast<float *>(lk) + key * (D + 1) + cc * 4;
+      dst[0] = __uint_as_float(x.x);
+      dst[1] = __uint_as_float(x.y);
+      dst[2] = __uint_as_float(x.z);
+      dst[3] = __uint_as_float(x.w);
+    }
+  }
+  // values
+  if constexpr (BF) {
+    for (int c = tid; c < nk * D; c += kAttnThreads) {
+      const int key = k0 + c / D, dd = c % D;
+      const int64_t d = tb + key - L;
+      uint16_t x = 0;
+      if (d <= depth)
+        x = reinterpret_cast<const uint16_t *>(vt)[(static_cast<int64_t>(anc[d]) * hkv + h) * D + dd];
+      reinterpret_cast<uint16_t *>(lv)[dd * 64 + (((key >> 2) ^ (dd & 15)) * 4) + (key & 3)] = x;
+    }
+  } else {
+    for (int c = tid; c < nk * C::CPR; c += kAttnThreads) {
+      const int key = k0 + c / C::CPR, cc = c % C::CPR;
+      const int64_t d = tb + key - L;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (d <= depth)
+        x = *reinterpret_cast<const uint4 *>(
+            vt + (static_cast<int64_t>(anc[d]) * hkv + h) * C::ROWB + cc * 16);
+      *reinterpret_cast<uint4 *>(lv + key * C::ROWB + cc * 16) = x;
+    }
+  }
+}
+
+// Q operand of one wave: lane (g, n) holds row n; rows past `rows` are zero.
+template <bool BF, int D>
+struct QRegs {
+  using C = AttnCfg<BF, D>;
+  typename std::conditional<BF, bf16x8, float>::type q[C::KQ];
+  // row_ptr: start of row n's D elements (nullptr for a padding row)
+  __device__ __forceinline__ void load(const void *row_ptr) {
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int kk = 0; kk < C::KQ; ++kk) {
+      if constexpr (BF) {
+        if (row_ptr)
+          q[kk] = *reinterpret_cast<const bf16x8 *>(static_cast<const uint16_t *>(row_ptr) +
+                                                    32 * kk + 8 * g);
+        else
+          q[kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      } else {
+        q[kk] = row_ptr ? static_cast<const float *>(row_ptr)[4 * kk + g] : 0.0f;
+      }
+    }
+  }
+};
+
+template <int D>
+__device__ __forceinline__ void write_partial(const RowState<D> &st, float *acc_row, float *ml_row) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+    *reinterpret_cast<floatx4 *>(acc_row + 16 * db + 4 * g) = st.acc[db];
+  if (g == 0) {
+    ml_row[0] = st.m;
+    ml_row[1] = st.l;
+  }
+}
+
+// Shared item: kv head h, committed split s, row group rg; every (node, q head)
+// row of the group sees every key of the split.
+template <bool BF, int D>
+__device__ __forceinline__ void attn_shared_item(const AttnLaunch &P, const AttnTree &T, int it,
+                                              unsigned char *lk, unsigned char *lv) {
+  using C = AttnCfg<BF, D>;
+  const int G = P.hq / P.hkv;
+  const int M = T.n * G;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15;
+  const int split_tiles = T.split / kTile;
+  const int rg = it % T.row_groups;
+  const int rest = it / T.row_groups;
+  const int s = rest % T.n_shared;
+  const int h = rest / T.n_shared;
+  const int r = (rg * kAttnWaves + wave) * 16 + ln;  // this lane's row
+  const bool wave_on = (rg * kAttnWaves + wave) * 16 < M;
+  RowState<D> st;
+  QRegs<BF, D> qr;
+  TileStage<BF, D> stage;
+  const void *qrow = nullptr;
+  if (r < M) {
+    const int node = r / G, j = h * G + r % G;
+    qrow = static_cast<const unsigned char *>(T.q) +
+           (static_cast<int64_t>(node) * P.hq + j) * C::ROWB;
+  }
+  qr.load(qrow);
+  st.reset();
+  const unsigned char *kh = static_cast<const unsigned char *>(T.kc) +
+                            static_cast<int64_t>(h) * T.cap * C::ROWB;
+  const unsigned char *vh = static_cast<const unsigned char *>(T.vc) +
+                            static_cast<int64_t>(h) * T.cap * C::ROWB;
+  const int64_t t0 = static_cast<int64_t>(s) * split_tiles;
+  stage.load(kh, vh, t0 * kTile, T.L);
+  for (int tt = 0; tt < split_tiles; ++tt) {
+    __syncthreads();
+    stage.store(lk, lv);
+    __syncthreads();
+    if (tt + 1 < split_tiles) stage.load(kh, vh, (t0 + tt + 1) * kTile, T.L);
+    if (wave_on) attn_tile<BF, D, false>(st, qr.q, lk, lv, (t0 + tt) * kTile, 0, P.c2);
+  }
+  if (r < M) {
+    const int64_t prow = (static_cast<int64_t>(h) * T.nsplit_cap + s) * T.rows_cap + r;
+    write_partial<D>(st, T.part_acc + prow * D, T.part_ml + prow * 2);
+  }
+}
+
+// Tail item: kv head h, nodes ng*8 .. ng*8+7 (one per wave); every position from
+// the first split not wholly below L up to each node's own position.  Tiles wholly
+// below L are shared by the group's waves; a tile holding positions >= L is rebuilt
+// in LDS for one node at a time (its ancestors, zeros past its position) and run
+// by that node's wave alone.
+template <bool BF, int D>
+__device__ __forceinline__ void attn_tail_item(const AttnLaunch &P, const AttnTree &T, int item,
+                                               unsigned char *a_lds) {
+  using C = AttnCfg<BF, D>;
+  unsigned char *lk = a_lds;
+  unsigned char *lv = a_lds + C::K_BYTES;
+  const int G = P.hq / P.hkv;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15;
+  const int split_tiles = T.split / kTile;
+  const int ngroups = (T.n + kAttnWaves - 1) / kAttnWaves;
+  const int h = item / ngroups, ng = item % ngroups;
+  const int node = ng * kAttnWaves + wave;
+  const bool node_on = node < T.n;
+  int8_t *anc_all = reinterpret_cast<int8_t *>(a_lds + C::TILE_BYTES);
+  const unsigned char *kt = static_cast<const unsigned char *>(T.kt);
+  const unsigned char *vt = static_cast<const unsigned char *>(T.vt);
+
+  // Group 0 stages the tree rows into the cache's pending rows [L, L+n), in
+  // tree-index order (commit gathers the accepted ones from there).
+  if (ng == 0) {
+    unsigned char *kcd = static_cast<unsigned char *>(T.kc) +
+                         (static_cast<int64_t>(h) * T.cap + T.L) * C::ROWB;
+    unsigned char *vcd = static_cast<unsigned char *>(T.vc) +
+                         (static_cast<int64_t>(h) * T.cap + T.L) * C::ROWB;
+    for (int c = tid; c < T.n * C::CPR; c += kAttnThreads) {
+      const int i = c / C::CPR, cc = c % C::CPR;
+      const int64_t src = (static_cast<int64_t>(i) * P.hkv + h) * C::ROWB + cc * 16;
+      *reinterpret_cast<uint4 *>(kcd + static_cast<int64_t>(i) * C::ROWB + cc * 16) =
+          *reinterpret_cast<const uint4 *>(kt + src);
+      *reinterpret_cast<uint4 *>(vcd + static_cast<int64_t>(i) * C::ROWB + cc * 16) =
+          *reinterpret_cast<const uint4 *>(vt + src);
+    }
+  }
+  // Ancestor table of every node of the group, by depth.
+  if (tid < kAttnWaves) {
+    const int x0 = ng * kAttnWaves + tid;
+    if (x0 < T.n) {
+      int x = x0;
+      for (int d = T.depth[x0]; d >= 0; --d) {
+        anc_all[tid * kMaxNodes + d] = static_cast<int8_t>(x);
+        x = T.parent[x];
+      }
+    }
+  }
+  int64_t pos_max = 0;
+  for (int w = 0; w < kAttnWaves; ++w) {
+    const int x = ng * kAttnWaves + w;
+    if (x < T.n) pos_max = max(pos_max, T.L + static_cast<int64_t>(T.depth[x]));
+  }
+  const int64_t pos = node_on ? T.L + T.depth[node] : 0;
+  RowState<D> st;
+  QRegs<BF, D> qr;
+  TileStage<BF, D> stage;
+  const void *qrow = nullptr;
+  if (node_on && ln < G)
+    qrow = static_cast<const unsigned char *>(T.q) +
+           (static_cast<int64_t>(node) * P.hq + h * G + ln) * C::ROWB;
+  qr.load(qrow);
+  st.reset();
+
+  const unsigned char *kh = static_cast<const unsigned char *>(T.kc) +
+                            static_cast<int64_t>(h) * T.cap * C::ROWB;
+  const unsigned char *vh = static_cast<const unsigned char *>(T.vc) +
+                            static_cast<int64_t>(h) * T.cap * C::ROWB;
+  const int64_t t_first = static_cast<int64_t>(T.n_shared) * split_tiles;
+  const int64_t t_last = pos_max / kTile;
+  const int64_t my_last = pos / kTile;
+  stage.load(kh, vh, t_first * kTile, T.L);
+  for (int64_t tt = t_first; tt <= t_last; ++tt) {
+    const int64_t tb = tt * kTile;
+    __syncthreads();
+    stage.store(lk, lv);
+    __syncthreads();
+    if (tt + 1 <= t_last) stage.load(kh, vh, (tt + 1) * kTile, T.L);
+    if (tb + kTile <= T.L) {
+      if (node_on && tt <= my_last) attn_tile<BF, D, false>(st, qr.q, lk, lv, tb, 0, P.c2);
+    } else {
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const int x = ng * kAttnWaves + w;
+        if (x >= T.n || tt > (T.L + T.depth[x]) / kTile) continue;  // uniform over the group
+        build_node_rows<BF, D>(lk, lv, kt, vt, P.hkv, h, anc_all + w * kMaxNodes, T.depth[x],
+                               tb, T.L);
+        __syncthreads();
+        if (wave == w) attn_tile<BF, D, true>(st, qr.q, lk, lv, tb, pos, P.c2);
+        __syncthreads();
+      }
+    }
+    if (node_on && tt <= my_last) {
+      const bool split_end = ((tt + 1) % split_tiles) == 0;
+      if (split_end || tt == my_last) {
+        if (ln < G) {
+          const int s = static_cast<int>(tt / split_tiles);
+          const int64_t prow =
+              (static_cast<int64_t>(h) * T.nsplit_cap + s) * T.rows_cap + node * G + ln;
+          write_partial<D>(st, T.part_acc + prow * D, T.part_ml + prow * 2);
+        }
+        st.reset();
+      }
+    }
+  }
+}
+
+template <bool BF, int D>
+__global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(const AttnLaunch P) {
+  using C = AttnCfg<BF, D>;
+  extern __shared__ __align__(16) unsigned char a_lds[];
+  const int bid = blockIdx.x;
+  int t = 0;
+  while (t + 1 < P.n_trees && bid >= P.t[t + 1].item_begin) ++t;
+  const AttnTree &T = P.t[t];
+  const int item = bid - T.item_begin;
+  if (item >= T.n_tail_items)
+    attn_shared_item<BF, D>(P, T, item - T.n_tail_items, a_lds, a_lds + C::K_BYTES);
+  else
+    attn_tail_item<BF, D>(P, T, item, a_lds);
+}
+
+// Fold the split partials of one (node, q head) row in ascending split order.
+template <bool BF, int D>
+__global__ __launch_bounds__(kFoldThreads) void attn_fold_kernel(const FoldLaunch P) {
+  constexpr int E = D / kFoldThreads;
+  const int bid = blockIdx.x;
+  int t = 0;
+  while (t + 1 < P.n_trees && bid >= P.t[t + 1].row_begin) ++t;
+  const FoldTree &T = P.t[t];
+  const int local = bid - T.row_begin;
+  const int node = local / P.hq, j = local % P.hq;
+  const int G = P.hq / P.hkv, h = j / G;
+  const int r = node * G + (j - h * G);
+  const int64_t pos = T.L + T.depth[node];
+  const int s_last = static_cast<int>(pos / T.split);
+  const int tid = threadIdx.x;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  float mr = -INFINITY, l = 0.0f;
+  for (int s = 0; s <= s_last; ++s) {
+    const int64_t prow = (static_cast<int64_t>(h) * T.nsplit_cap + s) * T.rows_cap + r;
+    const float ms = T.part_ml[prow * 2], ls = T.part_ml[prow * 2 + 1];
+    const float *pa = T.part_acc + prow * D + tid * E;
+    float x[E];
+    if constexpr (E == 4) {
+      const float4 v = *reinterpret_cast<const float4 *>(pa);
+      x[0] = v.x;
+      x[1] = v.y;
+      x[2] = v.z;
+      x[3] = v.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = pa[e];
+    }
+    const float mn = fmaxf(mr, ms);
+    const float a = exp2_fast(mr - mn), b = exp2_fast(ms - mn);
+    l = l * a + ls * b;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = acc[e] * a + x[e] * b;
+    mr = mn;
+  }
+  const int64_t o0 = (static_cast<int64_t>(node) * P.hq + j) * D + tid * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e) st_io<BF>(T.o, o0 + e, acc[e] / l);
+}
+
+// ============================================================================ commit
+
+template <bool BF, int DK>
+__global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch P) {
+  constexpr int R = DK / 16;
+  const int bid = blockIdx.x, tid = threadIdx.x;
+  if (bid < P.gdn_blocks) {
+    const int cgroups = P.dv / kGdnCols;
+    const int per_layer = P.hv * cgroups;
+    const int lg = bid / per_layer, local = bid % per_layer;
+    const int h = local / cgroups, cg = local % cgroups;
+    const int qh = h / (P.hv / P.hk);
+    const int wave = tid >> 6, lane = tid & 63;
+    const int col = cg * kGdnCols + wave * 4 + (lane >> 4);
+    const int g = lane & 15;
+    float *sp = P.state + ((static_cast<int64_t>(lg) * P.hv + h) * P.dv + col) * DK + g * R;
+    float cur[R];
+#pragma unroll
+    for (int a = 0; a < R; ++a) cur[a] = sp[a];
+    for (int d = 0; d < P.m; ++d) {
+      const int j = P.path[d];
+      const int64_t nb = static_cast<int64_t>(lg) * P.max_nodes + j;
+      const float u = P.u_pend[(nb * P.hv + h) * P.dv + col];
+      const float al = ld_io<BF>(P.a_pend, nb * P.hv + h);
+      const int64_t kb = (nb * P.hk + qh) * DK + g * R;
+#pragma unroll
+      for (int a = 0; a < R; ++a) cur[a] = fmaf(ld_io<BF>(P.k_pend, kb + a), u, al * cur[a]);
+    }
+#pragma unroll
+    for (int a = 0; a < R; ++a) sp[a] = cur[a];
+    return;
+  }
+  // K/V gather: row L+d <- row L+path[d] of one (attention layer, kv head).
+  // Rows are staged through LDS because a destination row may be another
+  // destination's source.
+  extern __shared__ __align__(16) uint4 c_lds[];
+  const int kb = bid - P.gdn_blocks;
+  const int la = kb / P.hkv, hh = kb % P.hkv;
+  const int esz = BF ? 2 : 4;
+  const int cpr = P.D * esz / 16;
+  for (int which = 0; which < 2; ++which) {
+    unsigned char *base = static_cast<unsigned char *>(which == 0 ? P.kc : P.vc) +
+                          ((static_cast<int64_t>(la) * P.hkv + hh) * P.cap + P.L) * P.D * esz;
+    for (int c = tid; c < P.m * cpr; c += kGdnThreads) {
+      const int d = c / cpr, cc = c % cpr;
+      c_lds[c] = *reinterpret_cast<const uint4 *>(base + static_cast<int64_t>(P.path[d]) * P.D * esz +
+                                                  cc * 16);
+    }
+    __syncthreads();
+    for (int c = tid; c < P.m * cpr; c += kGdnThreads) {
+      const int d = c / cpr, cc = c % cpr;
+      *reinterpret_cast<uint4 *>(base + static_cast<int64_t>(d) * P.D * esz + cc * 16) = c_lds[c];
+    }
+    __syncthreads();
+  }
+}
+
+template <typename K>
+hipError_t set_lds(K kernel, size_t bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+}
+
+}  // namespace
+
+size_t gdn_lds_bytes(int dk, int n_max) {
+  return gdn_lds_floats(dk, n_max) * sizeof(float) + static_cast<size_t>(n_max) * kMaxNodes;
+}
+
+size_t attn_lds_bytes(int D, int bf16, int n_max) {
+  const size_t tile = bf16 ? (D == 256 ? AttnCfg<true, 256>::TILE_BYTES : AttnCfg<true, 64>::TILE_BYTES)
+                           : AttnCfg<false, 64>::TILE_BYTES;
+  (void)n_max;
+  return tile + kAttnWaves * kMaxNodes;
+}
+
+size_t commit_lds_bytes(int D, int bf16, int m) {
+  return static_cast<size_t>(m) * D * (bf16 ? 2 : 4);
+}
+
+hipError_t launch_gdn_tree(const GdnLaunch &a, int dk, int bf16, hipStream_t s) {
+  const int blocks = a.t[a.n_trees - 1].wg_begin + a.hv * (a.dv / kGdnCols);
+  const size_t lds = gdn_lds_bytes(dk, a.n_max);
+#define HDT_GDN(BF, DK)                                                                   \
+  do {                                                                                    \
+    (void)set_lds(gdn_tree_kernel<BF, DK>, lds);                                                \
+    hipLaunchKernelGGL((gdn_tree_kernel<BF, DK>), dim3(blocks), dim3(kGdnThreads), lds, s, a); \
+  } while (0)
+  if (bf16) {
+    if (dk == 128) HDT_GDN(true, 128); else HDT_GDN(true, 64);
+  } else {
+    if (dk == 128) HDT_GDN(false, 128); else HDT_GDN(false, 64);
+  }
+#undef HDT_GDN
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_split(const AttnLaunch &a, int D, int bf16, int n_blocks, hipStream_t s) {
+  const size_t lds = attn_lds_bytes(D, bf16, a.n_max);
+#define HDT_ATTN(BF, DD)                                                                   \
+  do {                                                                                     \
+    (void)set_lds(attn_split_kernel<BF, DD>, lds);                                               \
+    hipLaunchKernelGGL((attn_split_kernel<BF, DD>), dim3(n_blocks), dim3(kAttnThreads), lds, s, a); \
+  } while (0)
+  if (bf16) {
+    if (D == 256) HDT_ATTN(true, 256); else HDT_ATTN(true, 64);
+  } else {
+    HDT_ATTN(false, 64);
+  }
+#undef HDT_ATTN
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fold(const FoldLaunch &a, int D, int bf16, int n_blocks, hipStream_t s) {
+  if (bf16) {
+    if (D == 256)
+      hipLaunchKernelGGL((attn_fold_kernel<true, 256>), dim3(n_blocks), dim3(kFoldThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_fold_kernel<true, 64>), dim3(n_blocks), dim3(kFoldThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_fold_kernel<false, 64>), dim3(n_blocks), dim3(kFoldThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(const CommitLaunch &a, int dk, int bf16, int n_blocks, hipStream_t s) {
+  const size_t lds = commit_lds_bytes(a.D, bf16, a.m);
+#define HDT_COMMIT(BF, DK)                                                                 \
+  do {                                                                                     \
+    (void)set_lds(commit_kernel<BF, DK>, lds);                                                   \
+    hipLaunchKernelGGL((commit_kernel<BF, DK>), dim3(n_blocks), dim3(kGdnThreads), lds, s, a); \
+  } while (0)
+  if (bf16) {
+    if (dk == 128) HDT_COMMIT(true, 128); else HDT_COMMIT(true, 64);
+  } else {
+    if (dk == 128) HDT_COMMIT(false, 128); else HDT_COMMIT(false, 64);
+  }
+#undef HDT_COMMIT
+  return hipGetLastError();
+}
+
+}  // namespace hdt

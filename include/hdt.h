@@ -1,0 +1,231 @@
+/*
+ * hdt.h - C ABI of the tree-verify library (libhdt.so) for AMD MI355X (gfx950).
+ *
+ * The library verifies a merged draft tree through a stack of Gated DeltaNet
+ * (GDN) and attention layers in one pass, then keeps or drops the result.  It
+ * is called once per step, never once per operator, and activations stay on
+ * the device: the step-granular flat C ABI described in "How ignis serves a
+ * request" ("The shape of the process").  The verbs follow the hot verbs of
+ * "Adding a model" (step 4 of "The adapter path in ten steps"): forward_tree,
+ * forward_block, commit_tree, rollback_to, kv.length and reset.
+ *
+ * Conventions for every call:
+ *  - Device pointers are HIP device memory owned by the caller; the library
+ *    never frees them.  Host pointers are read during the call only.
+ *  - A stream argument is a hipStream_t passed as void* (NULL = the default
+ *    stream).  Work is enqueued asynchronously on it; nothing waits for the GPU.
+ *  - Every argument and ordering check runs on the host before anything is
+ *    enqueued.  A call that returns an error changed nothing: no slot state,
+ *    length or pending round moved, and no kernel was launched.
+ *  - hdt_last_error() returns a text for the last failed call on that engine.
+ *  - An engine is not thread-safe: use one per thread or serialise calls.
+ *  - No C++ exception crosses this interface.
+ *
+ * Tree convention (the pages give the tree as "one tree" per round, section
+ * 2.6 "The decode loop" of "One request, end to end"; the array form is ours):
+ *  parent[0] = -1 (node 0 is the root: the model's own token from the last
+ *  round, not yet in the cache) and 0 <= parent[i] < i.  Node i sits at
+ *  position L + depth(i), L being the slot's committed length, and sees every
+ *  committed row plus its ancestors-or-self.  At most HDT_MAX_NODES nodes.
+ */
+#ifndef HDT_H
+#define HDT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HDT_MAX_NODES 64 /* nodes per tree (ancestor masks are 64-bit)   */
+#define HDT_MAX_TREES 8  /* trees (slots) in one joint forward_tree call */
+
+typedef enum {
+  HDT_OK = 0,
+  HDT_E_INVALID = -1,     /* bad argument, descriptor or shape            */
+  HDT_E_TREE = -2,        /* parent array is not a valid tree             */
+  HDT_E_PATH = -3,        /* commit path is not a root path of the tree   */
+  HDT_E_CAPACITY = -4,    /* the slot's buffers cannot hold the rows      */
+  HDT_E_ORDER = -5,       /* verb out of sequence (pending round rules)   */
+  HDT_E_HIP = -6,         /* a HIP runtime call failed                    */
+  HDT_E_UNSUPPORTED = -7  /* valid request this build does not implement  */
+} hdt_status;
+
+typedef enum { HDT_F32 = 0, HDT_BF16 = 1 } hdt_dtype;
+
+/*
+ * Model descriptor, fixed at hdt_create.
+ *  layer_kind: host array of n_layers entries, 0 = GDN, 1 = attention ("Adding
+ *    a model", "What is still specific to Qwen3.8": a hybrid of Gated DeltaNet
+ *    and attention layers).  Layers run in index order.
+ *  GDN: gdn_hk query/key heads, gdn_hv value heads (gdn_hv % gdn_hk == 0; v head
+ *    h reads q/k head h / (gdn_hv / gdn_hk)); gdn_dk = gdn_dv in {64, 128}
+ *    (state heads of 128 by 128 in the pages); gdn_dv % 16 == 0.
+ *  Attention: attn_hq query heads, attn_hkv kv heads (q head j reads kv head
+ *    j / (attn_hq / attn_hkv), at most 16 q heads per kv head), head dim attn_d
+ *    in {64, 256}.
+ *  io_dtype: storage of q, k, v, gates, outputs and the K/V cache (HDT_BF16,
+ *    or HDT_F32 with attn_d = 64).  The GDN state is always float32.
+ *  gdn_scale: readout scale s in o = S^T (s q); <= 0 selects 1/sqrt(gdn_dk).
+ *  attn_scale: softmax scale; <= 0 selects 1/sqrt(attn_d).
+ *  max_nodes: largest tree any call will pass (1..HDT_MAX_NODES); sizes the
+ *    library's own scratch.
+ */
+typedef struct {
+  int32_t n_layers;
+  const uint8_t *layer_kind;
+  int32_t gdn_hk, gdn_hv, gdn_dk, gdn_dv;
+  int32_t attn_hq, attn_hkv, attn_d;
+  int32_t io_dtype;
+  float gdn_scale, attn_scale;
+  int32_t max_nodes;
+} hdt_model_desc;
+
+/*
+ * One slot: a sequence with its own recurrent state and K/V views ("Adding a
+ * model", "The model layer: architecture registry and per-model state": state
+ * sections copied whole, K and V views indexed by token position; "Parallel
+ * requests": each slot has its own KV and recurrent state).  All device memory,
+ * owned by the caller:
+ *  gdn_state: float32 [n_gdn][gdn_hv][gdn_dv][gdn_dk]; element S[a][c] of a head
+ *    (a over the key dim, c over the value dim) is at [c][a] (value-major).
+ *  k_cache, v_cache: io_dtype [n_attn][attn_hkv][capacity][attn_d], row t =
+ *    token position t.
+ *  n_gdn / n_attn count the layers of each kind, in layer order.
+ *  capacity: rows per head in the caches; a tree of n nodes needs
+ *    length + n <= capacity.
+ *  length: committed rows at creation.
+ */
+typedef struct {
+  float *gdn_state;
+  void *k_cache;
+  void *v_cache;
+  int64_t capacity;
+  int64_t length;
+} hdt_slot_desc;
+
+/*
+ * Per-layer inputs and output of one tree, all device pointers in io_dtype,
+ * n = the tree's node count:
+ *  GDN layer:       q, k [n][gdn_hk][gdn_dk]; v [n][gdn_hv][gdn_dv];
+ *                   alpha, beta [n][gdn_hv] (decay and write strength, values in
+ *                   (0,1)); o [n][gdn_hv][gdn_dv] out.
+ *  attention layer: q [n][attn_hq][attn_d]; k, v [n][attn_hkv][attn_d] (the
+ *                   tree's own rows, already rotated); alpha, beta unused;
+ *                   o [n][attn_hq][attn_d] out.
+ * Inputs are read during the pass only; the library copies what commit needs.
+ */
+typedef struct {
+  const void *q, *k, *v, *alpha, *beta;
+  void *o;
+} hdt_layer_io;
+
+/* One tree of a forward_tree call.  parent and io are HOST arrays (io has
+ * n_layers entries). */
+typedef struct {
+  int32_t slot;
+  int32_t n_nodes;
+  const int32_t *parent;
+  const hdt_layer_io *io;
+} hdt_tree;
+
+typedef struct hdt_engine hdt_engine;
+
+/*
+ * Create an engine over n_slots caller-owned slots.  Validates every field;
+ * allocates nothing on the device (scratch is allocated on the current HIP
+ * device at the first call that launches work).  *out is NULL on failure.
+ */
+hdt_status hdt_create(const hdt_model_desc *desc, int32_t n_slots, const hdt_slot_desc *slots,
+                      hdt_engine **out);
+
+/* Free the engine and its scratch (not the caller's buffers).  Waits for the
+ * device first.  NULL is a no-op. */
+void hdt_destroy(hdt_engine *eng);
+
+/*
+ * forward_tree ("Adding a model", step 4; "One request, end to end", 2.6): verify
+ * n_trees trees (distinct slots, none with a pending round) in one pass through
+ * every layer.  Per GDN layer, each value head advances its recurrent state
+ * along every root-to-node path and writes S_i^T (s q_i) for every node; per
+ * attention layer, every (node, q head) row attends to the committed rows and
+ * its ancestors-or-self.  Writes each layer's o; stages each attention layer's
+ * tree rows into the slot's cache rows [L, L+n) in tree-index order; keeps what
+ * commit needs.  Committed state and rows below L are left unchanged.
+ * Afterwards each slot has a pending round.  Several trees in one call give
+ * every row the same bits as verifying each tree alone ("Parallel requests",
+ * "On Flash-Next": the joint pass equals each lone verify bit for bit).
+ * Errors: HDT_E_INVALID, HDT_E_TREE, HDT_E_CAPACITY, HDT_E_ORDER, HDT_E_HIP.
+ */
+hdt_status hdt_forward_tree(hdt_engine *eng, int32_t n_trees, const hdt_tree *trees,
+                            void *stream);
+
+/* forward_block: forward_tree of one chain of n nodes (parent[i] = i - 1). */
+hdt_status hdt_forward_block(hdt_engine *eng, int32_t slot, int32_t n, const hdt_layer_io *io,
+                             void *stream);
+
+/*
+ * commit_tree ("One request, end to end", 2.6: commit the accepted path's KV
+ * rows and recurrent state): path is a HOST array of m >= 1 node indices with
+ * path[0] = 0 and parent[path[d]] = path[d-1].  For every attention layer,
+ * cache row L+d takes the pending row of path[d] (a bit copy); for every GDN
+ * layer the committed state becomes the state of node path[m-1], with the same
+ * bits the pass computed.  Then length += m and the pending round ends.
+ * Errors: HDT_E_INVALID, HDT_E_PATH, HDT_E_ORDER (no pending round), HDT_E_HIP.
+ */
+hdt_status hdt_commit_tree(hdt_engine *eng, int32_t slot, const int32_t *path, int32_t m,
+                           void *stream);
+
+/*
+ * rollback_to(n): keep exactly n tokens.  n = length drops the pending round
+ * (or does nothing when none is pending).  length < n <= length + c, c being
+ * the pending tree's leading chain (nodes 0..c-1 with parent[i] = i-1), keeps
+ * that chain prefix: the same as hdt_commit_tree with path 0..n-length-1.
+ * n < length needs state anchors this library does not keep: HDT_E_UNSUPPORTED.
+ * Other n: HDT_E_INVALID.
+ */
+hdt_status hdt_rollback_to(hdt_engine *eng, int32_t slot, int64_t n, void *stream);
+
+/* kv.length: committed rows of a slot (host value, no device access). */
+hdt_status hdt_kv_length(const hdt_engine *eng, int32_t slot, int64_t *out);
+
+/* reset: set a slot's committed length (0..capacity) and drop any pending
+ * round.  The caller owns the state and cache contents. */
+hdt_status hdt_reset(hdt_engine *eng, int32_t slot, int64_t length);
+
+/*
+ * Tree metadata on the host, as the kernels use it: depth[n]; mask[n] with bit
+ * j set when node j is an ancestor-or-self of node i; anc[n][HDT_MAX_NODES]
+ * with anc[i][d] the ancestor of i at depth d (-1 beyond depth(i));
+ * pos[n] = L + depth.  Any output may be NULL.  No engine, no device.
+ * Errors: HDT_E_TREE.
+ */
+hdt_status hdt_tree_meta(int32_t n, const int32_t *parent, int64_t L, int32_t *depth,
+                         uint64_t *mask, int32_t *anc, int64_t *pos);
+
+/*
+ * Attention split size of a slot: the resident keys are cut into splits of this
+ * many positions anchored at position 0, each reduced on its own and folded in
+ * ascending order.  It depends only on the slot's capacity, so a row's bits
+ * depend only on its inputs.  Errors: HDT_E_INVALID.
+ */
+hdt_status hdt_split_size(const hdt_engine *eng, int32_t slot, int64_t *out);
+
+/*
+ * Kernel timing for measurement.  hdt_profile(eng, 1) starts recording a HIP
+ * event pair around every launch on the launch stream; hdt_profile_read waits
+ * for the recorded events and returns, for kernel class `kind` (0 = GDN tree
+ * walk, 1 = attention split pass, 2 = attention fold, 3 = commit), the summed
+ * milliseconds and the launch count since the last read; then clears them.
+ */
+hdt_status hdt_profile(hdt_engine *eng, int32_t enable);
+hdt_status hdt_profile_read(hdt_engine *eng, int32_t kind, double *ms, int64_t *launches);
+
+/* Text of the last error on this engine ("" when none); never NULL. */
+const char *hdt_last_error(const hdt_engine *eng);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HDT_H */

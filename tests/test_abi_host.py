@@ -1,0 +1,141 @@
+"""The C ABI on the host (no GPU): the library loads, exports what include/hdt.h declares,
+computes tree metadata bit for bit like the oracle, and refuses bad calls with the right
+status while changing nothing.  No call here reaches a HIP runtime function."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+hdt = pytest.importorskip("hybrid_deltanet_tree_amd")
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "hdt.h")
+FAKE = 1 << 20  # a 16-byte-aligned address that is never dereferenced on the host
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:hdt_status|void|const char \*)\s*(hdt_\w+)\(", src,
+                                 re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(hdt.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(hdt.EXPORTED)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_tree_meta_matches_oracle(seed):
+    parent = synth.random_tree(seed, "abi/meta", 64 if seed % 2 else 17, 20)
+    d0, m0, a0, p0 = oracle.tree_meta(parent, L=12345)
+    d1, m1, a1, p1 = hdt.tree_meta(parent, L=12345)
+    assert list(d0) == d1
+    assert [int(x) for x in m0] == m1
+    assert [list(r) for r in a0] == a1
+    assert list(p0) == p1
+
+
+@pytest.mark.parametrize("bad", [[0], [-1, 1], [-1, 0, 3], [-1, -1], [-1, 0, -2]])
+def test_tree_meta_rejects(bad):
+    with pytest.raises(hdt.HdtError) as e:
+        hdt.tree_meta(bad)
+    assert e.value.status == -2
+
+
+def make_engine(**kw):
+    args = dict(gdn_hk=2, gdn_hv=4, gdn_dk=64, gdn_dv=64, attn_hq=4, attn_hkv=2, attn_d=64,
+                io_dtype=hdt.HDT_BF16, max_nodes=8,
+                slots=[dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=1000, length=100),
+                       dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=300, length=295)])
+    kinds = kw.pop("layer_kind", [0, 0, 0, 1])
+    args.update(kw)
+    return hdt.Engine(kinds, **args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(layer_kind=[0, 2]), -1),
+    (dict(gdn_dk=96, gdn_dv=96), -7),
+    (dict(gdn_hv=3), -1),
+    (dict(max_nodes=0), -1),
+    (dict(max_nodes=65), -1),
+    (dict(attn_d=128), -7),
+    (dict(attn_hq=5), -1),
+    (dict(attn_hq=34, attn_hkv=2), -7),
+    (dict(io_dtype=hdt.HDT_F32, attn_d=256), -7),
+    (dict(io_dtype=7), -1),
+    (dict(slots=[dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=10, length=11)]), -1),
+    (dict(slots=[dict(gdn_state=0, k_cache=FAKE, v_cache=FAKE, capacity=10, length=1)]), -1),
+    (dict(slots=[dict(gdn_state=FAKE + 4, k_cache=FAKE, v_cache=FAKE, capacity=10, length=1)]), -1),
+    (dict(slots=[]), -1),
+])
+def test_create_rejects(kw, status):
+    with pytest.raises(hdt.HdtError) as e:
+        make_engine(**kw)
+    assert e.value.status == status
+
+
+def fake_layers(n_layers=4):
+    return [dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, o=FAKE) for _ in range(n_layers)]
+
+
+@pytest.mark.parametrize("trees,status", [
+    ([], -1),
+    ([(0, [-1, 0], fake_layers())] * 9, -1),
+    ([(2, [-1, 0], fake_layers())], -1),
+    ([(0, [-1, 0], fake_layers()), (0, [-1], fake_layers())], -1),
+    ([(0, list(range(-1, 8)), fake_layers())], -1),
+    ([(0, [-1, 1], fake_layers())], -2),
+    ([(0, [0, 0], fake_layers())], -2),
+    ([(1, [-1, 0, 1, 2, 3, 4], fake_layers())], -4),
+    ([(0, [-1], [dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE)] * 4)], -1),
+    ([(0, [-1], fake_layers()[:3] + [dict(q=FAKE + 2, k=FAKE, v=FAKE, o=FAKE)])], -1),
+])
+def test_forward_tree_rejects_and_changes_nothing(trees, status):
+    e = make_engine()
+    with pytest.raises(hdt.HdtError) as err:
+        e.forward_tree(trees)
+    assert err.value.status == status
+    assert e.last_error()
+    assert e.kv_length(0) == 100 and e.kv_length(1) == 295
+    # nothing pending: commit is out of order, rollback to the length is a no-op
+    with pytest.raises(hdt.HdtError) as err:
+        e.commit_tree(0, [0])
+    assert err.value.status == -5
+    e.rollback_to(0, 100)
+    assert e.kv_length(0) == 100
+
+
+def test_sequencing_rules_without_pending_round():
+    e = make_engine()
+    with pytest.raises(hdt.HdtError) as err:
+        e.rollback_to(0, 99)
+    assert err.value.status == -7
+    with pytest.raises(hdt.HdtError) as err:
+        e.rollback_to(0, 101)
+    assert err.value.status == -5
+    with pytest.raises(hdt.HdtError) as err:
+        e.reset(0, 1001)
+    assert err.value.status == -1
+    e.reset(0, 7)
+    assert e.kv_length(0) == 7
+    with pytest.raises(hdt.HdtError):
+        e.kv_length(5)
+
+
+def test_split_size_depends_on_capacity_only():
+    e = make_engine()
+    assert e.split_size(0) == 256 and e.split_size(1) == 256
+    big = [dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=65536 + 1024, length=65536),
+           dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=262144 + 1024, length=0)]
+    e2 = make_engine(attn_hkv=4, attn_hq=24, attn_d=256, slots=big)
+    assert e2.split_size(0) == 1024 and e2.split_size(1) == 4096
+    e2.reset(0, 5)
+    assert e2.split_size(0) == 1024
