@@ -228,6 +228,7 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
         g.n = tr.n_nodes;
         g.wg_begin = wg;
         std::memcpy(g.parent, par[t], kMaxNodes);
+        std::memcpy(g.depth, dep[t], kMaxNodes);
         wg += m.gdn_hv * (m.gdn_dv / kGdnCols);
       }
       ProfScope p(e, stream, 0);
@@ -268,9 +269,10 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
         x.nsplit_cap = s.nsplit_cap;
         x.rows_cap = m.max_nodes * G;
         x.item_begin = items;
-        x.n_tail_items = m.attn_hkv * ((tr.n_nodes + kAttnWaves - 1) / kAttnWaves);
-        const int blocks16 = (tr.n_nodes * G + 15) / 16;
-        x.row_groups = (blocks16 + kAttnWaves - 1) / kAttnWaves;
+        const int tn = attn_nodes_per_tail(bf), rpi = attn_rows_per_item(bf);
+        x.tail_nodes = tn;
+        x.n_tail_items = m.attn_hkv * ((tr.n_nodes + tn - 1) / tn);
+        x.row_groups = (tr.n_nodes * G + rpi - 1) / rpi;
         std::memcpy(x.parent, par[t], kMaxNodes);
         std::memcpy(x.depth, dep[t], kMaxNodes);
         items += x.n_tail_items + m.attn_hkv * x.n_shared * x.row_groups;

@@ -68,6 +68,15 @@ __device__ __forceinline__ float dpp(float x) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+// Workgroup barrier that waits only for this wave's LDS operations: vector-memory
+// loads still in flight stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Sum over the 16 lanes of a DPP row; every lane of the row gets the same bits
 // (each stage adds the same two partials in either order).
 __device__ __forceinline__ float rowsum16(float x) {
@@ -78,19 +87,83 @@ __device__ __forceinline__ float rowsum16(float x) {
   return x;
 }
 
+// Three independent rowsum16 reductions, interleaved stage by stage.
+__device__ __forceinline__ void rowsum16x3(float &a, float &b, float &c) {
+  a = a + dpp<0xB1>(a);
+  b = b + dpp<0xB1>(b);
+  c = c + dpp<0xB1>(c);
+  a = a + dpp<0x4E>(a);
+  b = b + dpp<0x4E>(b);
+  c = c + dpp<0x4E>(c);
+  a = a + dpp<0x141>(a);
+  b = b + dpp<0x141>(b);
+  c = c + dpp<0x141>(c);
+  a = a + dpp<0x140>(a);
+  b = b + dpp<0x140>(b);
+  c = c + dpp<0x140>(c);
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ============================================================================ GDN
 
 // LDS layout of the GDN walk (floats, then bytes): k[n][dk], s*q[n][dk],
-// v[n][16], alpha[n], beta[n], u[n][16], o[n][16], depth[n] (int), anc[n][64] (int8).
+// v[n][16], alpha[n], beta[n], u[n][16], o[n][16], depth[n] and parent[n] (int),
+// anc[n][64] (int8).
 __host__ __device__ constexpr size_t gdn_lds_floats(int dk, int n) {
-  return static_cast<size_t>(n) * (2 * dk + 3 * kGdnCols + 3);
+  return static_cast<size_t>(n) * (2 * dk + 3 * kGdnCols + 4);
+}
+
+// Sum of x[a] * y[a] over a lane's R elements in a fixed pairwise order.
+template <int R>
+__device__ __forceinline__ float lane_dot(const float *x, const float *y) {
+  float s[R / 2];
+#pragma unroll
+  for (int j = 0; j < R / 2; ++j) s[j] = fmaf(x[2 * j], y[2 * j], x[2 * j + 1] * y[2 * j + 1]);
+#pragma unroll
+  for (int w = R / 4; w >= 1; w /= 2)
+#pragma unroll
+    for (int j = 0; j < w; ++j) s[j] = s[2 * j] + s[2 * j + 1];
+  return s[0];
+}
+
+template <int R>
+__device__ __forceinline__ void lds_row(const float *src, float *dst) {
+#pragma unroll
+  for (int a = 0; a < R; a += 4) {
+    const float4 x = *reinterpret_cast<const float4 *>(src + a);
+    dst[a] = x.x;
+    dst[a + 1] = x.y;
+    dst[a + 2] = x.z;
+    dst[a + 3] = x.w;
+  }
+}
+
+template <bool BF>
+__device__ __forceinline__ void unpack16(const uint4 &c, float *out) {
+  if constexpr (BF) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      out[2 * e] = __uint_as_float(w[e] << 16);
+      out[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+  } else {
+    out[0] = __uint_as_float(c.x);
+    out[1] = __uint_as_float(c.y);
+    out[2] = __uint_as_float(c.z);
+    out[3] = __uint_as_float(c.w);
+  }
 }
 
 template <bool BF, int DK>
 __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P) {
-  constexpr int R = DK / 16;  // key rows per lane; 16 lanes hold one value column
+  constexpr int R = DK / 16;                 // key rows per lane; 16 lanes hold one value column
+  constexpr int ESZ = BF ? 2 : 4;
+  constexpr int EPC = 16 / ESZ;              // elements per 16-byte chunk
+  constexpr int CPR = DK / EPC;              // chunks per q/k row
+  constexpr int MAXC = (kMaxNodes * CPR + kGdnThreads - 1) / kGdnThreads;
+  constexpr int VCH = kGdnCols / EPC;        // chunks of one node's 16 value columns
   extern __shared__ __align__(16) float g_lds[];
   const int bid = blockIdx.x;
   int t = 0;
@@ -105,8 +178,8 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
   float *be = al + nm;
   float *ul = be + nm;
   float *ol = ul + nm * kGdnCols;
-  int *dep = reinterpret_cast<int *>(ol + nm * kGdnCols);
-  int8_t *anc = reinterpret_cast<int8_t *>(dep + nm);
+  int *dep = reinterpret_cast<int *>(ol + nm * kGdnCols);  // depth[n], then parent[n]
+  int8_t *anc = reinterpret_cast<int8_t *>(dep + 2 * nm);
 
   const int cgroups = P.dv / kGdnCols;
   const int local = bid - T.wg_begin;
@@ -117,65 +190,122 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
   const int g = lane & 15;                // key rows [g*R, g*R+R)
   const int col = cg * kGdnCols + lc;
 
-  // Stage the tree's inputs for this head.
-  for (int e = tid; e < n * DK; e += kGdnThreads) {
-    const int i = e / DK, a = e % DK;
-    const int64_t src = (static_cast<int64_t>(i) * P.hk + qh) * DK + a;
-    kf[e] = ld_io<BF>(T.k, src);
-    qs[e] = P.scale * ld_io<BF>(T.q, src);
+  // ---- issue every load of the prologue before using any of them (tree first)
+  int par_i = -1, dep_i = 0;
+  if (tid < n) {
+    par_i = T.parent[tid];
+    dep_i = T.depth[tid];
   }
-  for (int e = tid; e < n * kGdnCols; e += kGdnThreads) {
-    const int i = e / kGdnCols, c = e % kGdnCols;
-    vl[e] = ld_io<BF>(T.v, (static_cast<int64_t>(i) * P.hv + h) * P.dv + cg * kGdnCols + c);
-  }
-  for (int e = tid; e < n; e += kGdnThreads) {
-    al[e] = ld_io<BF>(T.alpha, static_cast<int64_t>(e) * P.hv + h);
-    be[e] = ld_io<BF>(T.beta, static_cast<int64_t>(e) * P.hv + h);
-    int d = 0;
-    for (int x = T.parent[e]; x >= 0; x = T.parent[x]) ++d;
-    dep[e] = d;
-    int x = e;
-    for (int k = d; k >= 0; --k) {
-      anc[e * kMaxNodes + k] = static_cast<int8_t>(x);
-      x = T.parent[x];
+  float base[R];
+  lds_row<R>(T.state + (static_cast<int64_t>(h) * P.dv + col) * DK + g * R, base);
+  const unsigned char *kb = static_cast<const unsigned char *>(T.k);
+  const unsigned char *qb = static_cast<const unsigned char *>(T.q);
+  uint4 kc[MAXC], qc[MAXC];
+  const int nch = n * CPR;
+#pragma unroll
+  for (int x = 0; x < MAXC; ++x) {
+    const int c = tid + x * kGdnThreads;
+    if (c < nch) {
+      const int i = c / CPR, cc = c % CPR;
+      const int64_t off = (static_cast<int64_t>(i) * P.hk + qh) * DK * ESZ + cc * 16;
+      kc[x] = *reinterpret_cast<const uint4 *>(kb + off);
+      qc[x] = *reinterpret_cast<const uint4 *>(qb + off);
     }
   }
-  // Keep what commit needs: alpha of this head, k of this q/k head (raw bits).
-  if (cg == 0) {
-    io_t<BF> *ap = static_cast<io_t<BF> *>(T.a_pend);
-    const io_t<BF> *as = static_cast<const io_t<BF> *>(T.alpha);
-    for (int e = tid; e < n; e += kGdnThreads)
-      ap[static_cast<int64_t>(e) * P.hv + h] = as[static_cast<int64_t>(e) * P.hv + h];
-    if (h % ratio == 0) {
-      io_t<BF> *kp = static_cast<io_t<BF> *>(T.k_pend);
-      const io_t<BF> *ks = static_cast<const io_t<BF> *>(T.k);
-      for (int e = tid; e < n * DK; e += kGdnThreads) {
-        const int i = e / DK, a = e % DK;
-        const int64_t idx = (static_cast<int64_t>(i) * P.hk + qh) * DK + a;
-        kp[idx] = ks[idx];
+  uint4 vc = make_uint4(0, 0, 0, 0);
+  if (tid < n * VCH) {
+    const int i = tid / VCH, cc = tid % VCH;
+    vc = *reinterpret_cast<const uint4 *>(
+        static_cast<const unsigned char *>(T.v) +
+        ((static_cast<int64_t>(i) * P.hv + h) * P.dv + cg * kGdnCols) * ESZ + cc * 16);
+  }
+  io_t<BF> araw{}, braw{};
+  if (tid < n) {
+    araw = static_cast<const io_t<BF> *>(T.alpha)[static_cast<int64_t>(tid) * P.hv + h];
+    braw = static_cast<const io_t<BF> *>(T.beta)[static_cast<int64_t>(tid) * P.hv + h];
+  }
+
+  // ---- tree metadata (ancestor table walked in LDS) and LDS staging
+  if (tid < n) {
+    dep[tid] = dep_i;
+    dep[nm + tid] = par_i;
+  }
+  lds_barrier();
+  if (tid < n) {
+    int x = tid;
+    for (int k = dep_i; k >= 0; --k) {
+      anc[tid * kMaxNodes + k] = static_cast<int8_t>(x);
+      x = dep[nm + x];
+    }
+  }
+  const bool keep_k = (cg == 0) && (h % ratio == 0);
+#pragma unroll
+  for (int x = 0; x < MAXC; ++x) {
+    const int c = tid + x * kGdnThreads;
+    if (c < nch) {
+      const int i = c / CPR, cc = c % CPR;
+      float kv[EPC], qv[EPC];
+      unpack16<BF>(kc[x], kv);
+      unpack16<BF>(qc[x], qv);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        kf[i * DK + cc * EPC + e] = kv[e];
+        qs[i * DK + cc * EPC + e] = P.scale * qv[e];
       }
+      if (keep_k)  // commit replays the accepted path with these exact k bits
+        *reinterpret_cast<uint4 *>(static_cast<unsigned char *>(T.k_pend) +
+                                   (static_cast<int64_t>(i) * P.hk + qh) * DK * ESZ + cc * 16) = kc[x];
     }
+  }
+  if (tid < n * VCH) {
+    const int i = tid / VCH, cc = tid % VCH;
+    float vv[EPC];
+    unpack16<BF>(vc, vv);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) vl[i * kGdnCols + cc * EPC + e] = vv[e];
+  }
+  if (tid < n) {
+    if constexpr (BF) {
+      al[tid] = __uint_as_float(static_cast<uint32_t>(araw) << 16);
+      be[tid] = __uint_as_float(static_cast<uint32_t>(braw) << 16);
+    } else {
+      al[tid] = araw;
+      be[tid] = braw;
+    }
+    if (cg == 0) static_cast<io_t<BF> *>(T.a_pend)[static_cast<int64_t>(tid) * P.hv + h] = araw;
   }
   __syncthreads();
 
-  float base[R], cur[R];
-  {
-    const float *sb = T.state + (static_cast<int64_t>(h) * P.dv + col) * DK + g * R;
-#pragma unroll
-    for (int a = 0; a < R; a += 4) {
-      const float4 x = *reinterpret_cast<const float4 *>(sb + a);
-      base[a] = x.x;
-      base[a + 1] = x.y;
-      base[a + 2] = x.z;
-      base[a + 3] = x.w;
-    }
-  }
+  // ---- walk the nodes in index order (parents first).  Per node, from the
+  // parent's state P:  A = alpha P;  r = k^T A;  u = beta (v - r);  S = A + k u^T;
+  // o = S^T (s q) taken as A^T (s q) + u (k . s q), so the readout does not wait
+  // for the state write.  Every dot product is a lane_dot then a rowsum16.
+  float cur[R];
 #pragma unroll
   for (int a = 0; a < R; ++a) cur[a] = base[a];
-
   int cur_node = -1;
+  float kn[R], qn[R];
+  lds_row<R>(kf + g * R, kn);
+  lds_row<R>(qs + g * R, qn);
+  float an = al[0], bn = be[0], vn = vl[lc];
+  int pn = dep[nm + 0];
   for (int i = 0; i < n; ++i) {
-    const int p = T.parent[i];
+    float ki[R], qi[R];
+#pragma unroll
+    for (int a = 0; a < R; ++a) {
+      ki[a] = kn[a];
+      qi[a] = qn[a];
+    }
+    const float ai = an, bi = bn, vi = vn;
+    const int p = pn;
+    if (i + 1 < n) {  // next node's operands, in flight during this step
+      lds_row<R>(kf + (i + 1) * DK + g * R, kn);
+      lds_row<R>(qs + (i + 1) * DK + g * R, qn);
+      an = al[i + 1];
+      bn = be[i + 1];
+      vn = vl[(i + 1) * kGdnCols + lc];
+      pn = dep[nm + i + 1];
+    }
     if (p != cur_node) {
       // Restore the parent's state: replay its root path's rank-1 steps from
       // the committed state with the same write as the step below.
@@ -183,36 +313,40 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
       for (int a = 0; a < R; ++a) cur[a] = base[a];
       if (p >= 0) {
         const int dp = dep[p];
+        const int8_t *path = anc + p * kMaxNodes;
+        int j = path[0];
+        float kj[R];
+        lds_row<R>(kf + j * DK + g * R, kj);
+        float aj = al[j], uj = ul[j * kGdnCols + lc];
         for (int d = 0; d <= dp; ++d) {
-          const int j = anc[p * kMaxNodes + d];
-          const float aj = al[j], uj = ul[j * kGdnCols + lc];
-          const float *kj = kf + j * DK + g * R;
+          float kk[R];
 #pragma unroll
-          for (int a = 0; a < R; ++a) cur[a] = fmaf(kj[a], uj, aj * cur[a]);
+          for (int a = 0; a < R; ++a) kk[a] = kj[a];
+          const float ak = aj, uk = uj;
+          if (d < dp) {
+            j = path[d + 1];
+            lds_row<R>(kf + j * DK + g * R, kj);
+            aj = al[j];
+            uj = ul[j * kGdnCols + lc];
+          }
+#pragma unroll
+          for (int a = 0; a < R; ++a) cur[a] = fmaf(kk[a], uk, ak * cur[a]);
         }
       }
     }
-    const float *ki = kf + i * DK + g * R;
-    const float *qi = qs + i * DK + g * R;
-    const float ai = al[i], bi = be[i], vi = vl[i * kGdnCols + lc];
     float A[R];
-    float r = 0.0f;
 #pragma unroll
-    for (int a = 0; a < R; ++a) {
-      A[a] = ai * cur[a];
-      r = fmaf(A[a], ki[a], r);
-    }
-    r = rowsum16(r);
+    for (int a = 0; a < R; ++a) A[a] = ai * cur[a];
+    float r = lane_dot<R>(A, ki);
+    float oa = lane_dot<R>(A, qi);
+    float kq = lane_dot<R>(ki, qi);
+    rowsum16x3(r, oa, kq);
     const float u = bi * (vi - r);
 #pragma unroll
     for (int a = 0; a < R; ++a) cur[a] = fmaf(ki[a], u, A[a]);
-    float o = 0.0f;
-#pragma unroll
-    for (int a = 0; a < R; ++a) o = fmaf(cur[a], qi[a], o);
-    o = rowsum16(o);
     if (g == 0) {
       ul[i * kGdnCols + lc] = u;
-      ol[i * kGdnCols + lc] = o;
+      ol[i * kGdnCols + lc] = fmaf(u, kq, oa);
     }
     cur_node = i;
   }
@@ -628,14 +762,17 @@ __device__ __forceinline__ void attn_tail_item(const AttnLaunch &P, const AttnTr
           *reinterpret_cast<const uint4 *>(vt + src);
     }
   }
-  // Ancestor table of every node of the group, by depth.
+  // Ancestor table of every node of the group, by depth (parents walked in LDS).
+  int8_t *par_l = anc_all + kAttnWaves * kMaxNodes;
+  if (tid < T.n) par_l[tid] = T.parent[tid];
+  __syncthreads();
   if (tid < kAttnWaves) {
     const int x0 = ng * kAttnWaves + tid;
     if (x0 < T.n) {
       int x = x0;
       for (int d = T.depth[x0]; d >= 0; --d) {
         anc_all[tid * kMaxNodes + d] = static_cast<int8_t>(x);
-        x = T.parent[x];
+        x = par_l[x];
       }
     }
   }
@@ -712,10 +849,468 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(const AttnLaun
     attn_tail_item<BF, D>(P, T, item, a_lds);
 }
 
-// Fold the split partials of one (node, q head) row in ascending split order.
+// ============================================================================ attention, bf16
+//
+// Workgroup of kAttn2Waves waves, one per SIMD; each wave owns up to kAttn2Blocks
+// blocks of 16 (node, q head) rows, so every K and V operand read from LDS feeds
+// several MFMAs.  K and V tiles go from HBM straight into LDS (buffer loads to
+// LDS, 16 bytes a lane, no staging registers) in their cache layout [key][D],
+// each LDS row padded by 32 bytes so that rows at one column fall on different
+// banks while every operand address stays affine.  The buffer resource of a head
+// covers rows [0, L): rows at or past L read as zeros, and the padding slots are
+// issued out of range so they move no data.  The V operand of O^T = V^T P^T is read
+// with the LDS transpose read (ds_read_b64_tr_b16): in each 16-lane group, lane p
+// addresses key 4e + p/4 at columns 16 db + 4 (p % 4), and lane m receives
+// V[key_e][16 db + m] for e = 0..3.  Two LDS stages alternate: tile t+1 is in
+// flight while tile t is computed.
+
+template <int D>
+struct Attn2Cfg {
+  static constexpr int ROWB = D * 2;                 // bytes per cache row
+  static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+  static constexpr int SPR = CPR + 2;                // 16-byte LDS slots per row (2 of padding)
+  static constexpr int LROW = SPR * 16;              // bytes per LDS row
+  static constexpr int TILE = 64 * LROW;             // bytes of one K (or V) tile in LDS
+  static constexpr int STAGE = 2 * TILE;             // K then V
+  static constexpr int SLOTS = 2 * 64 * SPR;         // slots of one stage
+  static constexpr int INSTR = SLOTS / 64;           // wave-wide loads per stage
+  static constexpr int IPW = INSTR / kAttn2Waves;    // per wave
+  static constexpr int KQ = D / 32;
+  static constexpr int DB = D / 16;
+  static_assert(SLOTS % 64 == 0 && INSTR % kAttn2Waves == 0, "stage must split evenly");
+};
+
+typedef __attribute__((address_space(3))) void *lds_void_ptr;
+
+// The bf16 attention keeps a row's running max until a tile's max exceeds it by
+// more than this (base-2 units): probabilities then stay below 2^kLazyMax.
+constexpr float kLazyMax = 8.0f;
+
+// Issue this wave's share of the loads of one tile (rows [tb, tb+64) of one head)
+// into an LDS stage.  kres / vres cover the head's rows [0, L).
+template <int D>
+__device__ __forceinline__ void dma_tile(unsigned char *stage, __amdgpu_buffer_rsrc_t kres,
+                                         __amdgpu_buffer_rsrc_t vres, int64_t tb) {
+  using C = Attn2Cfg<D>;
+  static_assert((64 * C::SPR) % 64 == 0, "a wave-wide load never straddles K and V");
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int x = 0; x < C::IPW; ++x) {
+    const int ins = wave * C::IPW + x;           // wave-wide load index within the stage
+    const int which = ins / C::SPR;              // 0 = K, 1 = V (uniform over the wave)
+    const int rs = (ins % C::SPR) * 64 + lane;   // slot within the K (or V) tile
+    const int key = rs / C::SPR, c = rs % C::SPR;
+    const uint32_t off = c < C::CPR ? static_cast<uint32_t>((tb + key) * C::ROWB + c * 16)
+                                    : 0xFFFFFFF0u;  // padding: out of range, zero, no traffic
+    // One wave-wide load: lane l's 16 bytes land at LDS (M0 + 16 l).  Issued from
+    // inline assembly so the compiler does not fence every later LDS read on it;
+    // the caller waits with wait_vm before the barrier that publishes the tile.
+    const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) unsigned char *)(stage + ins * 1024)));
+    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :
+                 : "v"(off), "s"(m0), "s"(which ? vres : kres)
+                 : "memory", "m0");
+  }
+}
+
+// Workgroup barrier without a memory fence: the compiler may not move memory
+// accesses across it, and the hardware does not wait for outstanding loads.
+__device__ __forceinline__ void bare_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Wait until at most n of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void *base, int64_t rows, int rowb) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                           static_cast<int>(rows * rowb), 0x00020000);
+}
+
+template <int D, int NB>
+struct Rows2 {
+  floatx4 acc[NB][D / 16];
+  float m[NB], l[NB];
+  bf16x8 q[NB][D / 32];
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) acc[b][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+      m[b] = -INFINITY;
+      l[b] = 0.0f;
+    }
+  }
+  // row_ptr[b]: start of lane row n of block b (nullptr: padding row, zeros)
+  __device__ __forceinline__ void load_q(const unsigned char *const *row_ptr) {
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk)
+        q[b][kk] = row_ptr[b] ? *reinterpret_cast<const bf16x8 *>(row_ptr[b] + (32 * kk + 8 * g) * 2)
+                              : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+};
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+// Transposed read of 4 keys x 16 columns of V (see the section comment).
+__device__ __forceinline__ shortx4 ds_read_tr(const unsigned char *p) {
+  typedef __attribute__((address_space(3))) shortx4 *lds_v4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4)((__attribute__((address_space(3))) unsigned char *)(p)));
+}
+
+// One tile (64 keys at absolute position tb) for the first nb of the NB row blocks
+// of this wave.  MASK: keys past `pos` (the wave's node position) are masked; the
+// tile builder left exact zeros in their K and V slots.
+template <int D, int NB, bool MASK>
+__device__ __forceinline__ void attn2_tile(Rows2<D, NB> &st, const unsigned char *lk,
+                                           const unsigned char *lv, int64_t tb, int64_t pos,
+                                           float c2) {
+  using C = Attn2Cfg<D>;
+  const int lane = threadIdx.x & 63, g = lane >> 4, ln = lane & 15;
+  floatx4 s[NB][4];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) s[b][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // ---- scores S^T = K Q^T: lane (g, n) gets keys 16 kb + 4 g + i of row n
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int key = 16 * kb + ln;
+#pragma unroll
+    for (int kk = 0; kk < C::KQ; ++kk) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(lk + key * C::LROW + (4 * kk + g) * 16);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        s[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, st.q[b][kk], s[b][kb], 0, 0, 0);
+    }
+  }
+  // ---- online softmax in base 2, per block.  The running max only moves when a
+  // tile exceeds it by more than kLazyMax, so probabilities stay below 2^kLazyMax
+  // and the accumulators are rescaled rarely (they live in accumulation registers,
+  // where a rescale costs a read, a multiply and a write per element).
+  bf16x8 pb[NB][2];
+  bool any_corr = false;
+  float corr[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float z[4][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = s[b][kb][i] * c2;
+        if constexpr (MASK) {
+          if (tb + 16 * kb + 4 * g + i > pos) x = -INFINITY;
+        }
+        z[kb][i] = x;
+        mt = fmaxf(mt, x);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const bool move = mt > st.m[b] + kLazyMax;  // always true on a row's first tile
+    const float mn = move ? mt : st.m[b];
+    corr[b] = (move && st.m[b] != -INFINITY) ? exp2_fast(st.m[b] - mn) : 1.0f;
+    any_corr = any_corr || corr[b] != 1.0f;
+    float lt = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 e = static_cast<__bf16>(exp2_fast(z[kb][i] - mn));
+        lt = lt + static_cast<float>(e);
+        pb[b][kb >> 1][4 * (kb & 1) + i] = e;
+      }
+    lt = lt + __shfl_xor(lt, 16);
+    lt = lt + __shfl_xor(lt, 32);
+    st.l[b] = st.l[b] * corr[b] + lt;
+    st.m[b] = mn;
+  }
+  if (__any(any_corr)) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) st.acc[b][db] = st.acc[b][db] * corr[b];
+  }
+  // ---- O^T += V^T P^T
+  const int trow = 4 * g + (ln >> 2);  // key of this lane's transposed read, + 32 kk2 (+16)
+  const int tcol4 = 4 * (ln & 3);      // column offset within the 16 columns of block db
+#pragma unroll
+  for (int kk2 = 0; kk2 < 2; ++kk2) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int col = 16 * db + tcol4;
+      const int k0 = 32 * kk2 + trow, k1 = k0 + 16;
+      const shortx4 lo = ds_read_tr(lv + k0 * C::LROW + col * 2);
+      const shortx4 hi = ds_read_tr(lv + k1 * C::LROW + col * 2);
+      const bf16x8 a = __builtin_bit_cast(
+          bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1],
+                                                             hi[2], hi[3]});
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        st.acc[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[b][kk2], st.acc[b][db], 0, 0, 0);
+    }
+  }
+}
+
+template <int D, int NB>
+__device__ __forceinline__ void write_partial2(const Rows2<D, NB> &st, int b, float *acc_row,
+                                               float *ml_row) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+    *reinterpret_cast<floatx4 *>(acc_row + 16 * db + 4 * g) = st.acc[b][db];
+  if (g == 0) {
+    ml_row[0] = st.m[b];
+    ml_row[1] = st.l[b];
+  }
+}
+
+// Rewrite the LDS tile rows at positions [max(L, tb), tb + 64) for one node: its
+// ancestor's K and V rows while the depth lasts, zeros after.  Rows below L keep
+// what was loaded.
+template <int D>
+__device__ __forceinline__ void build_node_rows2(unsigned char *stage, const unsigned char *kt,
+                                                 const unsigned char *vt, int hkv, int h,
+                                                 const int8_t *anc, int depth, int64_t tb, int64_t L) {
+  using C = Attn2Cfg<D>;
+  const int k0 = static_cast<int>(L > tb ? L - tb : 0);
+  const int nk = 64 - k0;
+  for (int c = threadIdx.x; c < 2 * nk * C::CPR; c += kAttn2Threads) {
+    const int which = c / (nk * C::CPR);
+    const int key = k0 + (c % (nk * C::CPR)) / C::CPR, cc = c % C::CPR;
+    const int64_t d = tb + key - L;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (d <= depth)
+      x = *reinterpret_cast<const uint4 *>((which ? vt : kt) +
+                                           (static_cast<int64_t>(anc[d]) * hkv + h) * C::ROWB + cc * 16);
+    *reinterpret_cast<uint4 *>(stage + which * C::TILE + key * C::LROW + cc * 16) = x;
+  }
+}
+
+template <int D>
+struct Attn2Lds {
+  unsigned char *s0, *s1;
+  int8_t *anc;
+  int8_t *par;
+};
+
+template <int D>
+__device__ __forceinline__ void attn2_shared_item(const AttnLaunch &P, const AttnTree &T, int it,
+                                                  const Attn2Lds<D> &S) {
+  using C = Attn2Cfg<D>;
+  constexpr int NB = kAttn2Blocks;
+  const int G = P.hq / P.hkv;
+  const int M = T.n * G;
+  const int wave = threadIdx.x >> 6, ln = threadIdx.x & 15;
+  const int split_tiles = T.split / kTile;
+  const int rg = it % T.row_groups;
+  const int rest = it / T.row_groups;
+  const int s = rest % T.n_shared;
+  const int h = rest / T.n_shared;
+  const int blk0 = (rg * kAttn2Waves + wave) * NB;  // first 16-row block of this wave
+  const bool wave_on = blk0 * 16 < M;
+  Rows2<D, NB> st;
+  const unsigned char *qrow[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int r = (blk0 + b) * 16 + ln;
+    qrow[b] = nullptr;
+    if (r < M) {
+      const int node = r / G, j = h * G + r % G;
+      qrow[b] = static_cast<const unsigned char *>(T.q) + (static_cast<int64_t>(node) * P.hq + j) * C::ROWB;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t kres =
+      head_rsrc(static_cast<const unsigned char *>(T.kc) + static_cast<int64_t>(h) * T.cap * C::ROWB, T.L, C::ROWB);
+  const __amdgpu_buffer_rsrc_t vres =
+      head_rsrc(static_cast<const unsigned char *>(T.vc) + static_cast<int64_t>(h) * T.cap * C::ROWB, T.L, C::ROWB);
+  const int64_t t0 = static_cast<int64_t>(s) * split_tiles;
+  // Barriers here are bare s_barrier: LDS is written only by the tile loads, whose
+  // completion each wave establishes with its own vmcnt wait; a fenced barrier would
+  // also wait for the load in flight to the other stage.  The first tile loads while
+  // Q arrives.
+  dma_tile<D>(S.s0, kres, vres, t0 * kTile);
+  if (wave_on) st.load_q(qrow);
+  wait_vm<0>();  // Q and tile 0 are in
+  st.reset();
+  for (int tt = 0; tt < split_tiles; tt += 2) {
+    // even tile in stage 0; tile tt+1 goes to stage 1 meanwhile
+    bare_barrier();  // stage 1 is no longer read (tile tt-1)
+    if (tt + 1 < split_tiles) {
+      dma_tile<D>(S.s1, kres, vres, (t0 + tt + 1) * kTile);
+      wait_vm<C::IPW>();
+    } else {
+      wait_vm<0>();
+    }
+    bare_barrier();  // tile tt is in stage 0 for every wave
+    if (wave_on) attn2_tile<D, NB, false>(st, S.s0, S.s0 + C::TILE, (t0 + tt) * kTile, 0, P.c2);
+    if (tt + 1 >= split_tiles) break;
+    // odd tile in stage 1; tile tt+2 goes to stage 0 meanwhile
+    bare_barrier();  // stage 0 is no longer read
+    if (tt + 2 < split_tiles) {
+      dma_tile<D>(S.s0, kres, vres, (t0 + tt + 2) * kTile);
+      wait_vm<C::IPW>();
+    } else {
+      wait_vm<0>();
+    }
+    bare_barrier();
+    if (wave_on) attn2_tile<D, NB, false>(st, S.s1, S.s1 + C::TILE, (t0 + tt + 1) * kTile, 0, P.c2);
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int r = (blk0 + b) * 16 + ln;
+    if (r < M) {
+      const int64_t prow = (static_cast<int64_t>(h) * T.nsplit_cap + s) * T.rows_cap + r;
+      write_partial2<D, NB>(st, b, T.part_acc + prow * D, T.part_ml + prow * 2);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void attn2_tail_item(const AttnLaunch &P, const AttnTree &T, int item,
+                                                const Attn2Lds<D> &S) {
+  using C = Attn2Cfg<D>;
+  const int G = P.hq / P.hkv;
+  const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 15;
+  const int split_tiles = T.split / kTile;
+  const int ngroups = (T.n + kAttn2Waves - 1) / kAttn2Waves;
+  const int h = item / ngroups, ng = item % ngroups;
+  const int node = ng * kAttn2Waves + wave;
+  const bool node_on = node < T.n;
+  int8_t *anc_all = S.anc;
+  const unsigned char *kt = static_cast<const unsigned char *>(T.kt);
+  const unsigned char *vt = static_cast<const unsigned char *>(T.vt);
+  if (ng == 0) {  // stage the tree rows into the cache's pending rows [L, L+n)
+    unsigned char *kcd = static_cast<unsigned char *>(T.kc) + (static_cast<int64_t>(h) * T.cap + T.L) * C::ROWB;
+    unsigned char *vcd = static_cast<unsigned char *>(T.vc) + (static_cast<int64_t>(h) * T.cap + T.L) * C::ROWB;
+    for (int c = tid; c < T.n * C::CPR; c += kAttn2Threads) {
+      const int i = c / C::CPR, cc = c % C::CPR;
+      const int64_t src = (static_cast<int64_t>(i) * P.hkv + h) * C::ROWB + cc * 16;
+      *reinterpret_cast<uint4 *>(kcd + static_cast<int64_t>(i) * C::ROWB + cc * 16) =
+          *reinterpret_cast<const uint4 *>(kt + src);
+      *reinterpret_cast<uint4 *>(vcd + static_cast<int64_t>(i) * C::ROWB + cc * 16) =
+          *reinterpret_cast<const uint4 *>(vt + src);
+    }
+  }
+  if (tid < T.n) S.par[tid] = T.parent[tid];
+  __syncthreads();
+  if (tid < kAttn2Waves) {  // ancestor table of the group's nodes, parents walked in LDS
+    const int x0 = ng * kAttn2Waves + tid;
+    if (x0 < T.n) {
+      int x = x0;
+      for (int d = T.depth[x0]; d >= 0; --d) {
+        anc_all[tid * kMaxNodes + d] = static_cast<int8_t>(x);
+        x = S.par[x];
+      }
+    }
+  }
+  int64_t pos_max = 0;
+  for (int w = 0; w < kAttn2Waves; ++w) {
+    const int x = ng * kAttn2Waves + w;
+    if (x < T.n) pos_max = max(pos_max, T.L + static_cast<int64_t>(T.depth[x]));
+  }
+  const int64_t pos = node_on ? T.L + T.depth[node] : 0;
+  Rows2<D, 1> st;
+  const unsigned char *qrow[1] = {nullptr};
+  if (node_on && ln < G)
+    qrow[0] = static_cast<const unsigned char *>(T.q) + (static_cast<int64_t>(node) * P.hq + h * G + ln) * C::ROWB;
+  if (node_on) st.load_q(qrow);
+  wait_vm<0>();
+  st.reset();
+  const __amdgpu_buffer_rsrc_t kres =
+      head_rsrc(static_cast<const unsigned char *>(T.kc) + static_cast<int64_t>(h) * T.cap * C::ROWB, T.L, C::ROWB);
+  const __amdgpu_buffer_rsrc_t vres =
+      head_rsrc(static_cast<const unsigned char *>(T.vc) + static_cast<int64_t>(h) * T.cap * C::ROWB, T.L, C::ROWB);
+  const int64_t t_first = static_cast<int64_t>(T.n_shared) * split_tiles;
+  const int64_t t_last = pos_max / kTile;
+  const int64_t my_last = pos / kTile;
+  for (int64_t tt = t_first; tt <= t_last; ++tt) {
+    const int64_t tb = tt * kTile;
+    __syncthreads();  // the previous tile is no longer read
+    dma_tile<D>(S.s0, kres, vres, tb);
+    wait_vm<0>();
+    __syncthreads();
+    if (tb + kTile <= T.L) {
+      if (node_on && tt <= my_last) attn2_tile<D, 1, false>(st, S.s0, S.s0 + C::TILE, tb, 0, P.c2);
+    } else {
+      for (int w = 0; w < kAttn2Waves; ++w) {
+        const int x = ng * kAttn2Waves + w;
+        if (x >= T.n || tt > (T.L + T.depth[x]) / kTile) continue;  // uniform over the group
+        build_node_rows2<D>(S.s0, kt, vt, P.hkv, h, anc_all + w * kMaxNodes, T.depth[x], tb, T.L);
+        __syncthreads();
+        if (wave == w) attn2_tile<D, 1, true>(st, S.s0, S.s0 + C::TILE, tb, pos, P.c2);
+        __syncthreads();
+      }
+    }
+    if (node_on && tt <= my_last) {
+      const bool split_end = ((tt + 1) % split_tiles) == 0;
+      if (split_end || tt == my_last) {
+        if (ln < G) {
+          const int s = static_cast<int>(tt / split_tiles);
+          const int64_t prow = (static_cast<int64_t>(h) * T.nsplit_cap + s) * T.rows_cap + node * G + ln;
+          write_partial2<D, 1>(st, 0, T.part_acc + prow * D, T.part_ml + prow * 2);
+        }
+        st.reset();
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kAttn2Threads) void attn2_split_kernel(const AttnLaunch P) {
+  using C = Attn2Cfg<D>;
+  __shared__ __align__(16) unsigned char stage0[C::STAGE];
+  __shared__ __align__(16) unsigned char stage1[C::STAGE];
+  __shared__ int8_t anc[kAttn2Waves * kMaxNodes];
+  __shared__ int8_t par[kMaxNodes];
+  const Attn2Lds<D> S{stage0, stage1, anc, par};
+  const int bid = blockIdx.x;
+  int t = 0;
+  while (t + 1 < P.n_trees && bid >= P.t[t + 1].item_begin) ++t;
+  const AttnTree &T = P.t[t];
+  const int item = bid - T.item_begin;
+  if (item >= T.n_tail_items)
+    attn2_shared_item<D>(P, T, item - T.n_tail_items, S);
+  else
+    attn2_tail_item<D>(P, T, item, S);
+}
+
+// Fold the split partials of one (node, q head) row.  The row's S splits are cut
+// into kFoldWaves contiguous ranges; each wave folds its range in ascending order
+// (kFoldBatch loads in flight), then the range results are folded in ascending
+// order.  The structure depends only on S, i.e. on the row's position.
+constexpr int kFoldWaves = kFoldThreads / 64;
+constexpr int kFoldBatch = 8;
+
+struct FoldAcc {
+  float m, l;
+  __device__ __forceinline__ void add(float ms, float ls, float *acc, const float *x, int E) {
+    const float mn = fmaxf(m, ms);
+    const float a = exp2_fast(m - mn), b = exp2_fast(ms - mn);
+    l = l * a + ls * b;
+    for (int e = 0; e < E; ++e) acc[e] = acc[e] * a + x[e] * b;
+    m = mn;
+  }
+};
+
 template <bool BF, int D>
 __global__ __launch_bounds__(kFoldThreads) void attn_fold_kernel(const FoldLaunch P) {
-  constexpr int E = D / kFoldThreads;
+  constexpr int E = D / 64;  // elements per lane
+  __shared__ float w_ml[kFoldWaves][2];
+  __shared__ __align__(16) float w_acc[kFoldWaves][D];
   const int bid = blockIdx.x;
   int t = 0;
   while (t + 1 < P.n_trees && bid >= P.t[t + 1].row_begin) ++t;
@@ -725,37 +1320,63 @@ __global__ __launch_bounds__(kFoldThreads) void attn_fold_kernel(const FoldLaunc
   const int G = P.hq / P.hkv, h = j / G;
   const int r = node * G + (j - h * G);
   const int64_t pos = T.L + T.depth[node];
-  const int s_last = static_cast<int>(pos / T.split);
-  const int tid = threadIdx.x;
+  const int S = static_cast<int>(pos / T.split) + 1;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int per = (S + kFoldWaves - 1) / kFoldWaves;
+  const int lo = min(S, wave * per), hi = min(S, lo + per);
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-  float mr = -INFINITY, l = 0.0f;
-  for (int s = 0; s <= s_last; ++s) {
-    const int64_t prow = (static_cast<int64_t>(h) * T.nsplit_cap + s) * T.rows_cap + r;
-    const float ms = T.part_ml[prow * 2], ls = T.part_ml[prow * 2 + 1];
-    const float *pa = T.part_acc + prow * D + tid * E;
-    float x[E];
-    if constexpr (E == 4) {
-      const float4 v = *reinterpret_cast<const float4 *>(pa);
-      x[0] = v.x;
-      x[1] = v.y;
-      x[2] = v.z;
-      x[3] = v.w;
-    } else {
+  FoldAcc f{-INFINITY, 0.0f};
+  const int64_t row0 = static_cast<int64_t>(h) * T.nsplit_cap * T.rows_cap + r;
+  for (int s0 = lo; s0 < hi; s0 += kFoldBatch) {
+    float ms[kFoldBatch], ls[kFoldBatch], x[kFoldBatch][E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) x[e] = pa[e];
+    for (int b = 0; b < kFoldBatch; ++b) {
+      if (s0 + b < hi) {
+        const int64_t prow = row0 + static_cast<int64_t>(s0 + b) * T.rows_cap;
+        ms[b] = T.part_ml[prow * 2];
+        ls[b] = T.part_ml[prow * 2 + 1];
+        const float *pa = T.part_acc + prow * D + lane * E;
+        if constexpr (E == 4) {
+          const float4 v = *reinterpret_cast<const float4 *>(pa);
+          x[b][0] = v.x;
+          x[b][1] = v.y;
+          x[b][2] = v.z;
+          x[b][3] = v.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) x[b][e] = pa[e];
+        }
+      }
     }
-    const float mn = fmaxf(mr, ms);
-    const float a = exp2_fast(mr - mn), b = exp2_fast(ms - mn);
-    l = l * a + ls * b;
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = acc[e] * a + x[e] * b;
-    mr = mn;
+    for (int b = 0; b < kFoldBatch; ++b)
+      if (s0 + b < hi) f.add(ms[b], ls[b], acc, x[b], E);
   }
-  const int64_t o0 = (static_cast<int64_t>(node) * P.hq + j) * D + tid * E;
+  if (lane == 0) {
+    w_ml[wave][0] = f.m;
+    w_ml[wave][1] = f.l;
+  }
 #pragma unroll
-  for (int e = 0; e < E; ++e) st_io<BF>(T.o, o0 + e, acc[e] / l);
+  for (int e = 0; e < E; ++e) w_acc[wave][lane * E + e] = acc[e];
+  __syncthreads();
+  if (wave != 0) return;
+  float out[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) out[e] = 0.0f;
+  FoldAcc tot{-INFINITY, 0.0f};
+  for (int w = 0; w < kFoldWaves; ++w) {
+    const int lw = min(S, w * per);
+    if (lw >= min(S, lw + per)) continue;  // empty range
+    float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = w_acc[w][lane * E + e];
+    tot.add(w_ml[w][0], w_ml[w][1], out, x, E);
+  }
+  const int64_t o0 = (static_cast<int64_t>(node) * P.hq + j) * D + lane * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e) st_io<BF>(T.o, o0 + e, out[e] / tot.l);
 }
 
 // ============================================================================ commit
@@ -763,8 +1384,14 @@ __global__ __launch_bounds__(kFoldThreads) void attn_fold_kernel(const FoldLaunc
 template <bool BF, int DK>
 __global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch P) {
   constexpr int R = DK / 16;
+  constexpr int ESZ = BF ? 2 : 4;
+  constexpr int KW = R * ESZ / 4;    // 32-bit words of a lane's k slice (2, 4 or 8)
+  constexpr int B = 8;               // path steps whose operands are in flight together
   const int bid = blockIdx.x, tid = threadIdx.x;
   if (bid < P.gdn_blocks) {
+    // Committed state of one (GDN layer, value head, 16 columns): replay the
+    // accepted path's rank-1 steps fmaf(k, u, alpha * S) with the bits the pass
+    // used, so the result equals the pass's state of the path's last node.
     const int cgroups = P.dv / kGdnCols;
     const int per_layer = P.hv * cgroups;
     const int lg = bid / per_layer, local = bid % per_layer;
@@ -775,19 +1402,60 @@ __global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch 
     const int g = lane & 15;
     float *sp = P.state + ((static_cast<int64_t>(lg) * P.hv + h) * P.dv + col) * DK + g * R;
     float cur[R];
+    lds_row<R>(sp, cur);
+    const int64_t lbase = static_cast<int64_t>(lg) * P.max_nodes;
+    for (int d0 = 0; d0 < P.m; d0 += B) {
+      uint32_t kw[B][KW];
+      float u[B];
+      io_t<BF> araw[B];
 #pragma unroll
-    for (int a = 0; a < R; ++a) cur[a] = sp[a];
-    for (int d = 0; d < P.m; ++d) {
-      const int j = P.path[d];
-      const int64_t nb = static_cast<int64_t>(lg) * P.max_nodes + j;
-      const float u = P.u_pend[(nb * P.hv + h) * P.dv + col];
-      const float al = ld_io<BF>(P.a_pend, nb * P.hv + h);
-      const int64_t kb = (nb * P.hk + qh) * DK + g * R;
+      for (int b = 0; b < B; ++b) {
+        if (d0 + b < P.m) {
+          const int64_t nb = lbase + P.path[d0 + b];
+          const unsigned char *kp = static_cast<const unsigned char *>(P.k_pend) +
+                                    ((nb * P.hk + qh) * DK + g * R) * ESZ;
+          if constexpr (KW % 4 == 0) {
 #pragma unroll
-      for (int a = 0; a < R; ++a) cur[a] = fmaf(ld_io<BF>(P.k_pend, kb + a), u, al * cur[a]);
+            for (int c = 0; c < KW; c += 4) {
+              const uint4 x = *reinterpret_cast<const uint4 *>(kp + 4 * c);
+              kw[b][c] = x.x;
+              kw[b][c + 1] = x.y;
+              kw[b][c + 2] = x.z;
+              kw[b][c + 3] = x.w;
+            }
+          } else {
+            const uint2 x = *reinterpret_cast<const uint2 *>(kp);
+            kw[b][0] = x.x;
+            kw[b][1] = x.y;
+          }
+          u[b] = P.u_pend[(nb * P.hv + h) * P.dv + col];
+          araw[b] = static_cast<const io_t<BF> *>(P.a_pend)[nb * P.hv + h];
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        if (d0 + b < P.m) {
+          float kj[R];
+#pragma unroll
+          for (int a = 0; a < R; ++a) {
+            if constexpr (BF)
+              kj[a] = __uint_as_float((a & 1) ? (kw[b][a / 2] & 0xFFFF0000u) : (kw[b][a / 2] << 16));
+            else
+              kj[a] = __uint_as_float(kw[b][a]);
+          }
+          float al;
+          if constexpr (BF)
+            al = __uint_as_float(static_cast<uint32_t>(araw[b]) << 16);
+          else
+            al = araw[b];
+#pragma unroll
+          for (int a = 0; a < R; ++a) cur[a] = fmaf(kj[a], u[b], al * cur[a]);
+        }
+      }
     }
 #pragma unroll
-    for (int a = 0; a < R; ++a) sp[a] = cur[a];
+    for (int a = 0; a < R; a += 4)
+      *reinterpret_cast<float4 *>(sp + a) = make_float4(cur[a], cur[a + 1], cur[a + 2], cur[a + 3]);
     return;
   }
   // K/V gather: row L+d <- row L+path[d] of one (attention layer, kv head).
@@ -828,11 +1496,13 @@ size_t gdn_lds_bytes(int dk, int n_max) {
 }
 
 size_t attn_lds_bytes(int D, int bf16, int n_max) {
-  const size_t tile = bf16 ? (D == 256 ? AttnCfg<true, 256>::TILE_BYTES : AttnCfg<true, 64>::TILE_BYTES)
-                           : AttnCfg<false, 64>::TILE_BYTES;
   (void)n_max;
-  return tile + kAttnWaves * kMaxNodes;
+  if (bf16) return 0;  // static LDS: two stages and the ancestor table
+  return AttnCfg<false, 64>::TILE_BYTES + kAttnWaves * kMaxNodes + kMaxNodes;
 }
+
+int attn_rows_per_item(int bf16) { return bf16 ? kAttn2Waves * kAttn2Blocks * 16 : kAttnWaves * 16; }
+int attn_nodes_per_tail(int bf16) { return bf16 ? kAttn2Waves : kAttnWaves; }
 
 size_t commit_lds_bytes(int D, int bf16, int m) {
   return static_cast<size_t>(m) * D * (bf16 ? 2 : 4);
@@ -857,17 +1527,15 @@ hipError_t launch_gdn_tree(const GdnLaunch &a, int dk, int bf16, hipStream_t s) 
 
 hipError_t launch_attn_split(const AttnLaunch &a, int D, int bf16, int n_blocks, hipStream_t s) {
   const size_t lds = attn_lds_bytes(D, bf16, a.n_max);
-#define HDT_ATTN(BF, DD)                                                                   \
-  do {                                                                                     \
-    (void)set_lds(attn_split_kernel<BF, DD>, lds);                                               \
-    hipLaunchKernelGGL((attn_split_kernel<BF, DD>), dim3(n_blocks), dim3(kAttnThreads), lds, s, a); \
-  } while (0)
   if (bf16) {
-    if (D == 256) HDT_ATTN(true, 256); else HDT_ATTN(true, 64);
+    if (D == 256)
+      hipLaunchKernelGGL((attn2_split_kernel<256>), dim3(n_blocks), dim3(kAttn2Threads), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn2_split_kernel<64>), dim3(n_blocks), dim3(kAttn2Threads), 0, s, a);
   } else {
-    HDT_ATTN(false, 64);
+    (void)set_lds(attn_split_kernel<false, 64>, lds);
+    hipLaunchKernelGGL((attn_split_kernel<false, 64>), dim3(n_blocks), dim3(kAttnThreads), lds, s, a);
   }
-#undef HDT_ATTN
   return hipGetLastError();
 }
 

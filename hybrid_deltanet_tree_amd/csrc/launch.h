@@ -15,11 +15,14 @@ namespace hdt {
 constexpr int kMaxNodes = 64;
 constexpr int kMaxTrees = 8;
 constexpr int kTile = 64;          // attention keys per tile, anchored at absolute positions
-constexpr int kAttnWaves = 8;      // waves per attention workgroup
+constexpr int kAttnWaves = 8;      // waves per attention workgroup (float32 storage)
 constexpr int kAttnThreads = kAttnWaves * 64;
+constexpr int kAttn2Waves = 4;     // bf16 storage: waves per workgroup, one per SIMD
+constexpr int kAttn2Threads = kAttn2Waves * 64;
+constexpr int kAttn2Blocks = 2;    // bf16 storage: 16-row blocks per wave
 constexpr int kGdnThreads = 256;   // 4 waves x 4 value columns x 16 lanes per column
 constexpr int kGdnCols = 16;       // value columns per GDN workgroup
-constexpr int kFoldThreads = 64;
+constexpr int kFoldThreads = 256;  // 4 waves per output row
 
 // ---------------------------------------------------------------- GDN tree walk
 struct GdnTree {
@@ -32,6 +35,7 @@ struct GdnTree {
   int32_t n;
   int32_t wg_begin;                      // first workgroup of this tree
   int8_t parent[kMaxNodes];
+  int8_t depth[kMaxNodes];
 };
 
 struct GdnLaunch {
@@ -61,6 +65,7 @@ struct AttnTree {
   int32_t nsplit_cap, rows_cap;
   int32_t item_begin;                     // first block of this tree
   int32_t n_tail_items;                   // hkv * node groups
+  int32_t tail_nodes;                     // nodes per tail item (one per wave)
   int32_t row_groups;                     // row groups per shared split
   int8_t parent[kMaxNodes];
   int8_t depth[kMaxNodes];
@@ -116,6 +121,10 @@ hipError_t launch_commit(const CommitLaunch &a, int dk, int bf16, int n_blocks, 
 // Dynamic LDS bytes each kernel asks for (the host checks them against the device).
 size_t gdn_lds_bytes(int dk, int n_max);
 size_t attn_lds_bytes(int D, int bf16, int n_max);
+// Work decomposition of the attention split pass for a storage dtype: rows per
+// shared item and nodes per tail item.
+int attn_rows_per_item(int bf16);
+int attn_nodes_per_tail(int bf16);
 size_t commit_lds_bytes(int D, int bf16, int m);
 
 }  // namespace hdt

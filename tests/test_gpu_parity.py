@@ -52,6 +52,24 @@ def test_forward_matches_oracle(wname, L):
         gu.check_layer(inst, 0, l, got[l])
 
 
+def test_bf16_small_heads():
+    # bf16 storage with d_k = d_v = 64 and D = 64: the narrow-slice code paths
+    w = synth.Workload("bf16_64", [0, 1, 0, 1], 2, 4, 64, 64, 4, 2, 64, "bf16", [700], 12, "draft")
+    inst = Instance(w, SEED)
+    eng = inst.engine()
+    run_verify(inst, eng)
+    got = gu.outputs(inst, 0)
+    for l in range(4):
+        gu.check_layer(inst, 0, l, got[l])
+    path = synth.accepted_path(SEED, "bf16_64/path", inst.trees[0])
+    eng.commit_tree(0, path, gu.stream())
+    gu.sync()
+    for gi, l in enumerate((0, 2)):
+        h = inst.host[0][l]
+        ref = oracle.gdn_commit(path, inst.h_state[0][gi], h["k"], h["v"], h["alpha"], h["beta"])
+        assert gu.rel_err(inst.state[0][gi].cpu().numpy(), ref) <= gu.TOL_F32
+
+
 def test_forward_matches_oracle_sharp_softmax():
     # unnormalised q, k: a peaked softmax exercises the running max and rescaling
     inst = Instance(MINI, SEED, lengths=[777], sharp=True)
