@@ -8,6 +8,13 @@ then commit_tree of a seeded accepted path.  The default workload is the 64-laye
 timed region.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload stack_65k] [--no-cpu-baseline]
+
+HBM traffic of the split kernel comes from two rocprofv3 counter passes over the
+bench (FETCH_SIZE, then WRITE_SIZE), scaled by what the same counters read for a
+plain device-to-device copy of known size:
+
+  python bench.py --copy-calibration            # run under rocprofv3 --pmc, twice
+  python bench.py --traffic-from F W CF CW      # the four counter CSVs -> profiles/
 """
 import argparse
 import json
@@ -20,6 +27,65 @@ sys.path.insert(0, ROOT)
 
 METRIC = "64-layer tree-verify ms at 65k ctx, 16-node tree; achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
+SPLIT_KERNEL = "attn2_split_kernel"
+COPY_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_split_stack65k_traffic.json")
+
+
+def kernels_digest():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "hybrid_deltanet_tree_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
+
+
+def copy_calibration():
+    """Plain device-to-device copies of COPY_BYTES: the reference for the counters."""
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {COPY_BYTES} bytes 4 times")
+
+
+def counter_means(csv_path, counter, match):
+    """Mean per-dispatch value of `counter` over the dispatches whose kernel name
+    contains `match` (rocprofv3 counter-collection CSV)."""
+    import csv
+    vals = {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter and match in row["Kernel_Name"]:
+                vals[row["Dispatch_Id"]] = vals.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"{csv_path}: no {counter} values for kernels matching {match!r}")
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+def traffic_from(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """Write the split kernel's measured HBM bytes per launch, scaled by the copy factor."""
+    f_k, n_f = counter_means(fetch_csv, "FETCH_SIZE", SPLIT_KERNEL)
+    w_k, n_w = counter_means(write_csv, "WRITE_SIZE", SPLIT_KERNEL)
+    cf_k, _ = counter_means(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
+    cw_k, _ = counter_means(copy_write_csv, "WRITE_SIZE", "copyBuffer")
+    f_scale = COPY_BYTES / (cf_k * 1024.0)
+    w_scale = COPY_BYTES / (cw_k * 1024.0)
+    rec = {"kernel": SPLIT_KERNEL, "kernels_sha256": kernels_digest(),
+           "fetch_kib_per_dispatch": round(f_k, 1), "write_kib_per_dispatch": round(w_k, 1),
+           "dispatches": [n_f, n_w],
+           "copy_fetch_kib": round(cf_k, 1), "copy_write_kib": round(cw_k, 1),
+           "copy_bytes": COPY_BYTES, "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "fetch_bytes_per_launch": int(f_k * 1024 * f_scale),
+           "write_bytes_per_launch": int(w_k * 1024 * w_scale)}
+    rec["bytes_per_launch"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def algorithmic_bytes(w, L, n):
@@ -81,12 +147,20 @@ def main():
     ap.add_argument("--workload", default="stack_65k")
     ap.add_argument("--seed", type=int, default=20261202)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this path has no multi-GPU mode (--gpus {args.gpus} "
               "requested). The sharding plan is described in the design notes.", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     import synth
     from synth.device import Instance
@@ -156,13 +230,10 @@ def main():
                       "launches_per_step": prof[k][1] // args.steps}
                for k, name in ((0, "gdn_tree"), (1, "attn_split"), (2, "attn_fold"), (3, "commit"))}
 
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "attn_split_stack65k_traffic.json")
-    if os.path.exists(tfile):
-        import hashlib
-        rec = json.load(open(tfile))
-        src = open(os.path.join(ROOT, "hybrid_deltanet_tree_amd", "csrc", "kernels.hip"), "rb").read()
-        if rec.get("kernels_sha256") == hashlib.sha256(src).hexdigest():
+    traffic = None   # measured bytes are stale once the kernels change
+    if args.workload == "stack_65k" and os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("kernels_sha256") == kernels_digest():
             traffic = rec.get("bytes_per_launch")
 
     out = {
@@ -189,7 +260,7 @@ def main():
                    "algorithmic_bytes": int(verify_bytes), "achieved_gbps": round(verify_gbps, 1),
                    "frac_of_peak": round(verify_gbps / PEAK_HBM_GBS, 4), "mean_context": round(Lm, 1)},
         "kernels": kernels,
-        "roofline": {"bound": "hbm", "kernel": "attn_split_kernel", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": SPLIT_KERNEL, "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": int(split_b)},
         "setup_s": round(t_setup, 1),

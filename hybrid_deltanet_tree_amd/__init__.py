@@ -25,6 +25,12 @@ STATUS = {0: "HDT_OK", -1: "HDT_E_INVALID", -2: "HDT_E_TREE", -3: "HDT_E_PATH",
           -4: "HDT_E_CAPACITY", -5: "HDT_E_ORDER", -6: "HDT_E_HIP", -7: "HDT_E_UNSUPPORTED"}
 KIND_GDN, KIND_ATTN_SPLIT, KIND_ATTN_FOLD, KIND_COMMIT = 0, 1, 2, 3
 
+# PyTorch owns the device memory and the streams, so libhdt must run on the same
+# HIP runtime instance.  PyTorch ships its own libamdhip64 under the same soname;
+# importing it first makes the loader resolve libhdt's dependency to that copy
+# instead of mapping a second runtime (which then fails to open the device).
+import torch  # noqa: E402,F401  (load order only)
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: run __graft_entry__.build() (or "
                       "python hybrid_deltanet_tree_amd/build.py) first")

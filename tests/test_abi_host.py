@@ -139,3 +139,11 @@ def test_split_size_depends_on_capacity_only():
     assert e2.split_size(0) == 1024 and e2.split_size(1) == 4096
     e2.reset(0, 5)
     assert e2.split_size(0) == 1024
+
+
+def test_one_hip_runtime_in_process():
+    # libhdt and PyTorch must share one HIP runtime: two mapped copies of
+    # libamdhip64 mean device pointers and streams cross runtime instances.
+    with open("/proc/self/maps") as f:
+        paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    assert len(paths) == 1, paths
