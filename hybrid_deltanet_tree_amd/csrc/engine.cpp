@@ -25,8 +25,9 @@ using namespace hdt;
 namespace {
 
 constexpr int kSplitCUs = 256;      // splits are sized so one layer spreads over this many items
-constexpr int64_t kSplitMin = 256;  // smallest split, in keys
+constexpr int64_t kSplitMin = 256;  // float32 attention: smallest split, in keys
 constexpr int64_t kSplitMax = 16384;
+constexpr int64_t kKvSplitMin = 128;  // bf16 attention: smallest split (> kKvTile - 1 + kMaxNodes - 1)
 
 struct SlotState {
   hdt_slot_desc d{};
@@ -35,8 +36,11 @@ struct SlotState {
   float *u_pend = nullptr;
   void *k_pend = nullptr;
   void *a_pend = nullptr;
-  float *part_acc = nullptr;
-  float *part_ml = nullptr;
+  float *part_acc = nullptr;  // float32 attention: partials [hkv][nsplit][rows][D]
+  float *part_ml = nullptr;   // [hkv][nsplit][rows][2]
+  void *part_o = nullptr;     // bf16 attention: normalised fp16 partials [hkv][nsplit][rows][D]
+  float *carry_acc = nullptr; // bf16 attention: state of split n_full below tb0 [hkv][rows][D]
+  float *carry_ml = nullptr;  // [hkv][rows][2]
   bool pending = false;
   int32_t n = 0;
   int32_t chain = 0;
@@ -90,10 +94,19 @@ int64_t pow2_floor(int64_t x) {
   return p;
 }
 
-// Split size of a slot: a power of two between kSplitMin and kSplitMax chosen so
-// that a full cache gives about kSplitCUs (kv head, split) items.  It depends on
-// the capacity alone, never on the current length.
-int32_t split_for(int64_t capacity, int32_t hkv) {
+// Split size of a slot.  It depends on the capacity alone, never on the current
+// length, so a row's fold structure is fixed for the life of the slot.
+//  float32 storage: a power of two between kSplitMin and kSplitMax chosen so that
+//    a full cache gives about kSplitCUs (kv head, split) items;
+//  bf16 storage: the smallest multiple of kKvTile (at least kKvSplitMin) for which
+//    a full cache gives at most kSplitCUs (kv head, split) items, one wave of
+//    workgroups over the chip.
+int32_t split_for(int64_t capacity, int32_t hkv, bool bf16) {
+  if (bf16) {
+    int64_t s = (capacity * hkv + kSplitCUs - 1) / kSplitCUs;
+    s = (s + kKvTile - 1) / kKvTile * kKvTile;
+    return static_cast<int32_t>(std::max(kKvSplitMin, s));
+  }
   int64_t s = pow2_floor(std::max<int64_t>(1, capacity * hkv / kSplitCUs));
   s = std::max(kSplitMin, std::min(kSplitMax, s));
   return static_cast<int32_t>(s);
@@ -139,9 +152,18 @@ hdt_status ensure_alloc(hdt_engine *e) {
     if (e->n_attn > 0) {
       const size_t rows = nm * G;
       const size_t base = static_cast<size_t>(m.attn_hkv) * s.nsplit_cap * rows;
-      if (hipMalloc(&s.part_acc, base * m.attn_d * sizeof(float)) != hipSuccess ||
-          hipMalloc(&s.part_ml, base * 2 * sizeof(float)) != hipSuccess)
+      const size_t carry = static_cast<size_t>(m.attn_hkv) * rows;
+      if (m.io_dtype == HDT_BF16) {
+        const size_t blocks = static_cast<size_t>(m.attn_hkv) * s.nsplit_cap * ((rows + 15) / 16);
+        if (hipMalloc(&s.part_o, blocks * 16 * m.attn_d * 2) != hipSuccess ||
+            hipMalloc(&s.part_ml, base * 2 * sizeof(float)) != hipSuccess ||
+            hipMalloc(&s.carry_acc, carry * m.attn_d * sizeof(float)) != hipSuccess ||
+            hipMalloc(&s.carry_ml, carry * 2 * sizeof(float)) != hipSuccess)
+          return fail(e, HDT_E_HIP, "hipMalloc of the attention partials failed");
+      } else if (hipMalloc(&s.part_acc, base * m.attn_d * sizeof(float)) != hipSuccess ||
+                 hipMalloc(&s.part_ml, base * 2 * sizeof(float)) != hipSuccess) {
         return fail(e, HDT_E_HIP, "hipMalloc of the attention partials failed");
+      }
     }
   }
   e->allocated = true;
@@ -155,21 +177,23 @@ void free_scratch(hdt_engine *e) {
     (void)hipFree(s.a_pend);
     (void)hipFree(s.part_acc);
     (void)hipFree(s.part_ml);
+    (void)hipFree(s.part_o);
+    (void)hipFree(s.carry_acc);
+    (void)hipFree(s.carry_ml);
     s.u_pend = nullptr;
-    s.k_pend = s.a_pend = nullptr;
-    s.part_acc = s.part_ml = nullptr;
+    s.k_pend = s.a_pend = s.part_o = nullptr;
+    s.part_acc = s.part_ml = s.carry_acc = s.carry_ml = nullptr;
   }
   e->allocated = false;
 }
 
-// Records an event pair around one launch when profiling is on.
+// When profiling is on, hands one launch an event pair that its dispatch records
+// (kernel start and end), and keeps the pair for hdt_profile_read.
 struct ProfScope {
   hdt_engine *e;
-  hipStream_t s;
-  int kind;
   EventPair ev{};
   bool on = false;
-  ProfScope(hdt_engine *e_, hipStream_t s_, int k) : e(e_), s(s_), kind(k) {
+  ProfScope(hdt_engine *e_, int k) : e(e_) {
     if (!e->profiling) return;
     if (!e->ev_pool.empty()) {
       ev = e->ev_pool.back();
@@ -178,14 +202,85 @@ struct ProfScope {
       return;
     }
     ev.kind = k;
-    on = hipEventRecord(ev.a, s) == hipSuccess;
+    on = true;
+  }
+  KernelEvents events() const {
+    KernelEvents k;
+    if (on) {
+      k.start = ev.a;
+      k.stop = ev.b;
+    }
+    return k;
   }
   ~ProfScope() {
-    if (!on) return;
-    (void)hipEventRecord(ev.b, s);
-    e->ev_live.push_back(ev);
+    if (on) e->ev_live.push_back(ev);
   }
 };
+
+// One attention layer with bf16 storage: the split pass over the committed rows,
+// then the tree pass (tree tiles, fold, output, pending rows).
+hdt_status launch_kv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
+                           const int8_t (*par)[kMaxNodes], const int8_t (*dep)[kMaxNodes], int l, int ki,
+                           hipStream_t stream) {
+  const hdt_model_desc &m = e->desc;
+  const int G = m.attn_hq / m.attn_hkv;
+  KvLaunch a;
+  std::memset(&a, 0, sizeof a);
+  a.n_trees = n_trees;
+  a.hq = m.attn_hq;
+  a.hkv = m.attn_hkv;
+  a.c2 = m.attn_scale * 1.4426950408889634f;
+  // Split-pass shape: 8 waves of one 16-row block (up to 128 rows per item, two
+  // waves per SIMD), or 4 waves of three blocks when a tree has 129..192 rows.
+  int max_blocks = 1;
+  for (int t = 0; t < n_trees; ++t) max_blocks = std::max(max_blocks, (trees[t].n_nodes * G + 15) / 16);
+  const int waves = (max_blocks > 8 && max_blocks <= 12) ? 4 : 8;
+  const int nb = waves == 4 ? 3 : 1;
+  int32_t items_a = 0, items_b = 0;
+  for (int t = 0; t < n_trees; ++t) {
+    const hdt_tree &tr = trees[t];
+    SlotState &s = e->slots[tr.slot];
+    const hdt_layer_io &io = tr.io[l];
+    KvTree &x = a.t[t];
+    const size_t view = static_cast<size_t>(m.attn_hkv) * s.d.capacity * m.attn_d * 2;
+    x.q = io.q;
+    x.kt = io.k;
+    x.vt = io.v;
+    x.kc = static_cast<char *>(s.d.k_cache) + static_cast<size_t>(ki) * view;
+    x.vc = static_cast<char *>(s.d.v_cache) + static_cast<size_t>(ki) * view;
+    x.o = io.o;
+    x.part_o = s.part_o;
+    x.part_ml = s.part_ml;
+    x.carry_acc = s.carry_acc;
+    x.carry_ml = s.carry_ml;
+    x.L = s.d.length;
+    x.cap = s.d.capacity;
+    x.n = tr.n_nodes;
+    x.split = s.split;
+    x.nsplit_cap = s.nsplit_cap;
+    x.rows_cap = m.max_nodes * G;
+    x.n_full = static_cast<int32_t>(s.d.length / s.split);
+    const int64_t tb0 = s.d.length / kKvTile * kKvTile;
+    x.carry_tiles = static_cast<int32_t>((tb0 - static_cast<int64_t>(x.n_full) * s.split) / kKvTile);
+    const int blocks = (tr.n_nodes * G + 15) / 16;
+    x.row_groups = (blocks + waves * nb - 1) / (waves * nb);
+    x.a_per_head = (x.n_full + (x.carry_tiles > 0 ? 1 : 0)) * x.row_groups;
+    x.a_begin = items_a;
+    items_a += m.attn_hkv * x.a_per_head;
+    x.b_begin = items_b;
+    items_b += m.attn_hkv * tr.n_nodes * kKvQuarters;
+    std::memcpy(x.parent, par[t], kMaxNodes);
+    std::memcpy(x.depth, dep[t], kMaxNodes);
+  }
+  if (items_a > 0) {
+    ProfScope p(e, 1);
+    hdt_status st = check_hip(e, launch_kv_split(a, m.attn_d, waves, nb, items_a, stream, p.events()),
+                              "attention split launch");
+    if (st != HDT_OK) return st;
+  }
+  ProfScope p(e, 2);
+  return check_hip(e, launch_kv_tree(a, m.attn_d, items_b, stream, p.events()), "attention tree launch");
+}
 
 hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, const int8_t (*par)[kMaxNodes],
                           const int8_t (*dep)[kMaxNodes], hipStream_t stream) {
@@ -231,8 +326,12 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
         std::memcpy(g.depth, dep[t], kMaxNodes);
         wg += m.gdn_hv * (m.gdn_dv / kGdnCols);
       }
-      ProfScope p(e, stream, 0);
-      hdt_status st = check_hip(e, launch_gdn_tree(a, m.gdn_dk, bf, stream), "GDN tree launch");
+      ProfScope p(e, 0);
+      hdt_status st =
+          check_hip(e, launch_gdn_tree(a, m.gdn_dk, bf, stream, p.events()), "GDN tree launch");
+      if (st != HDT_OK) return st;
+    } else if (bf) {
+      hdt_status st = launch_kv_layer(e, n_trees, trees, par, dep, l, ki, stream);
       if (st != HDT_OK) return st;
     } else {
       AttnLaunch a;
@@ -291,14 +390,14 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
         rows += tr.n_nodes * m.attn_hq;
       }
       {
-        ProfScope p(e, stream, 1);
-        hdt_status st = check_hip(e, launch_attn_split(a, m.attn_d, bf, items, stream),
+        ProfScope p(e, 1);
+        hdt_status st = check_hip(e, launch_attn_split(a, m.attn_d, bf, items, stream, p.events()),
                                   "attention split launch");
         if (st != HDT_OK) return st;
       }
       {
-        ProfScope p(e, stream, 2);
-        hdt_status st = check_hip(e, launch_attn_fold(f, m.attn_d, bf, rows, stream),
+        ProfScope p(e, 2);
+        hdt_status st = check_hip(e, launch_attn_fold(f, m.attn_d, bf, rows, stream, p.events()),
                                   "attention fold launch");
         if (st != HDT_OK) return st;
       }
@@ -334,9 +433,9 @@ hdt_status do_commit(hdt_engine *e, int32_t slot, const int32_t *path, int32_t m
   for (int d = 0; d < m_len; ++d) c.path[d] = static_cast<int8_t>(path[d]);
   const int blocks = c.gdn_blocks + (e->n_attn > 0 ? e->n_attn * m.attn_hkv : 0);
   if (blocks > 0) {
-    ProfScope p(e, stream, 3);
+    ProfScope p(e, 3);
     const int dk = e->n_gdn > 0 ? m.gdn_dk : 64;
-    hdt_status st = check_hip(e, launch_commit(c, dk, m.io_dtype == HDT_BF16, blocks, stream),
+    hdt_status st = check_hip(e, launch_commit(c, dk, m.io_dtype == HDT_BF16, blocks, stream, p.events()),
                               "commit launch");
     if (st != HDT_OK) return st;
   }
@@ -371,6 +470,8 @@ hdt_status hdt_create(const hdt_model_desc *desc, int32_t n_slots, const hdt_slo
     if (m.attn_hkv < 1 || m.attn_hq < m.attn_hkv || m.attn_hq % m.attn_hkv != 0)
       return HDT_E_INVALID;
     if (m.attn_hq / m.attn_hkv > 16) return HDT_E_UNSUPPORTED;
+    // bf16 storage: one fold thread per (q head, column pair) of a quarter row block
+    if (m.io_dtype == HDT_BF16 && (m.attn_hq / m.attn_hkv) * (m.attn_d / 8) > 192) return HDT_E_UNSUPPORTED;
     if (m.attn_d != 64 && m.attn_d != 256) return HDT_E_UNSUPPORTED;
     if (m.io_dtype == HDT_F32 && m.attn_d != 64) return HDT_E_UNSUPPORTED;
   }
@@ -378,6 +479,9 @@ hdt_status hdt_create(const hdt_model_desc *desc, int32_t n_slots, const hdt_slo
     const hdt_slot_desc &s = slots[i];
     if (s.capacity < 1 || s.length < 0 || s.length > s.capacity) return HDT_E_INVALID;
     if (s.capacity > (int64_t(1) << 31)) return HDT_E_UNSUPPORTED;
+    // buffer resources address one kv head's rows with 32-bit byte offsets
+    if (n_attn > 0 && s.capacity * m.attn_d * (m.io_dtype == HDT_BF16 ? 2 : 4) > INT32_MAX)
+      return HDT_E_UNSUPPORTED;
     if (n_gdn > 0 && (!s.gdn_state || !aligned16(s.gdn_state))) return HDT_E_INVALID;
     if (n_attn > 0 && (!s.k_cache || !s.v_cache || !aligned16(s.k_cache) || !aligned16(s.v_cache)))
       return HDT_E_INVALID;
@@ -398,7 +502,7 @@ hdt_status hdt_create(const hdt_model_desc *desc, int32_t n_slots, const hdt_slo
   for (int i = 0; i < n_slots; ++i) {
     SlotState &s = e->slots[i];
     s.d = slots[i];
-    s.split = split_for(s.d.capacity, std::max(1, m.attn_hkv));
+    s.split = split_for(s.d.capacity, std::max(1, m.attn_hkv), m.io_dtype == HDT_BF16);
     s.nsplit_cap = static_cast<int32_t>((s.d.capacity + s.split - 1) / s.split);
   }
   *out = e;

@@ -5,9 +5,11 @@
 //                     ("Adding a model", "What is still specific to Qwen3.8":
 //                     state heads of 128 by 128; the step is the published gated
 //                     delta rule).
-//  attn_split_kernel  one attention layer: ancestor-masked GQA over the committed
-//                     rows plus the tree's own rows ("One request, end to end",
-//                     2.6), as per-split partial softmax results.
+//  attn_split_kernel  one attention layer with float32 storage (the small
+//                     parity configuration): ancestor-masked GQA over the
+//                     committed rows plus the tree's own rows ("One request, end
+//                     to end", 2.6), as per-split partial softmax results.
+//                     bf16 storage runs the kernels of kv_attention.hip.
 //  attn_fold_kernel   folds a row's split partials in ascending split order.
 //  commit_kernel      commit_tree: replays the accepted path's rank-1 steps into
 //                     every GDN layer's committed state and gathers the path's
@@ -25,57 +27,12 @@
 //    absolute positions; each tile is reduced by the same MFMA sequence whatever
 //    other rows share the instruction; masked key slots hold exact zeros; splits
 //    fold in ascending order.
-#include "launch.h"
-
-#include <type_traits>
+#include "common.h"
 
 #pragma clang fp contract(off)
 
 namespace hdt {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-template <bool BF>
-using io_t = typename std::conditional<BF, uint16_t, float>::type;
-
-template <bool BF>
-__device__ __forceinline__ float ld_io(const void *p, int64_t i) {
-  if constexpr (BF) {
-    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(p)[i]) << 16);
-  } else {
-    return static_cast<const float *>(p)[i];
-  }
-}
-
-__device__ __forceinline__ uint16_t bf16_bits(float f) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
-}
-
-template <bool BF>
-__device__ __forceinline__ void st_io(void *p, int64_t i, float v) {
-  if constexpr (BF) {
-    static_cast<uint16_t *>(p)[i] = bf16_bits(v);
-  } else {
-    static_cast<float *>(p)[i] = v;
-  }
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-
-// Workgroup barrier that waits only for this wave's LDS operations: vector-memory
-// loads still in flight stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 // Sum over the 16 lanes of a DPP row; every lane of the row gets the same bits
 // (each stage adds the same two partials in either order).
@@ -102,8 +59,6 @@ __device__ __forceinline__ void rowsum16x3(float &a, float &b, float &c) {
   b = b + dpp<0x140>(b);
   c = c + dpp<0x140>(c);
 }
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ============================================================================ GDN
 
@@ -849,445 +804,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(const AttnLaun
     attn_tail_item<BF, D>(P, T, item, a_lds);
 }
 
-// ============================================================================ attention, bf16
-//
-// Workgroup of kAttn2Waves waves, one per SIMD; each wave owns up to kAttn2Blocks
-// blocks of 16 (node, q head) rows, so every K and V operand read from LDS feeds
-// several MFMAs.  K and V tiles go from HBM straight into LDS (buffer loads to
-// LDS, 16 bytes a lane, no staging registers) in their cache layout [key][D],
-// each LDS row padded by 32 bytes so that rows at one column fall on different
-// banks while every operand address stays affine.  The buffer resource of a head
-// covers rows [0, L): rows at or past L read as zeros, and the padding slots are
-// issued out of range so they move no data.  The V operand of O^T = V^T P^T is read
-// with the LDS transpose read (ds_read_b64_tr_b16): in each 16-lane group, lane p
-// addresses key 4e + p/4 at columns 16 db + 4 (p % 4), and lane m receives
-// V[key_e][16 db + m] for e = 0..3.  Two LDS stages alternate: tile t+1 is in
-// flight while tile t is computed.
-
-template <int D>
-struct Attn2Cfg {
-  static constexpr int ROWB = D * 2;                 // bytes per cache row
-  static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
-  static constexpr int SPR = CPR + 2;                // 16-byte LDS slots per row (2 of padding)
-  static constexpr int LROW = SPR * 16;              // bytes per LDS row
-  static constexpr int TILE = 64 * LROW;             // bytes of one K (or V) tile in LDS
-  static constexpr int STAGE = 2 * TILE;             // K then V
-  static constexpr int SLOTS = 2 * 64 * SPR;         // slots of one stage
-  static constexpr int INSTR = SLOTS / 64;           // wave-wide loads per stage
-  static constexpr int IPW = INSTR / kAttn2Waves;    // per wave
-  static constexpr int KQ = D / 32;
-  static constexpr int DB = D / 16;
-  static_assert(SLOTS % 64 == 0 && INSTR % kAttn2Waves == 0, "stage must split evenly");
-};
-
-typedef __attribute__((address_space(3))) void *lds_void_ptr;
-
-// The bf16 attention keeps a row's running max until a tile's max exceeds it by
-// more than this (base-2 units): probabilities then stay below 2^kLazyMax.
-constexpr float kLazyMax = 8.0f;
-
-// Issue this wave's share of the loads of one tile (rows [tb, tb+64) of one head)
-// into an LDS stage.  kres / vres cover the head's rows [0, L).
-template <int D>
-__device__ __forceinline__ void dma_tile(unsigned char *stage, __amdgpu_buffer_rsrc_t kres,
-                                         __amdgpu_buffer_rsrc_t vres, int64_t tb) {
-  using C = Attn2Cfg<D>;
-  static_assert((64 * C::SPR) % 64 == 0, "a wave-wide load never straddles K and V");
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int x = 0; x < C::IPW; ++x) {
-    const int ins = wave * C::IPW + x;           // wave-wide load index within the stage
-    const int which = ins / C::SPR;              // 0 = K, 1 = V (uniform over the wave)
-    const int rs = (ins % C::SPR) * 64 + lane;   // slot within the K (or V) tile
-    const int key = rs / C::SPR, c = rs % C::SPR;
-    const uint32_t off = c < C::CPR ? static_cast<uint32_t>((tb + key) * C::ROWB + c * 16)
-                                    : 0xFFFFFFF0u;  // padding: out of range, zero, no traffic
-    // One wave-wide load: lane l's 16 bytes land at LDS (M0 + 16 l).  Issued from
-    // inline assembly so the compiler does not fence every later LDS read on it;
-    // the caller waits with wait_vm before the barrier that publishes the tile.
-    const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-        (__attribute__((address_space(3))) unsigned char *)(stage + ins * 1024)));
-    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-                 :
-                 : "v"(off), "s"(m0), "s"(which ? vres : kres)
-                 : "memory", "m0");
-  }
-}
-
-// Workgroup barrier without a memory fence: the compiler may not move memory
-// accesses across it, and the hardware does not wait for outstanding loads.
-__device__ __forceinline__ void bare_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// Wait until at most n of this wave's vector-memory operations are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N < 64, "vmcnt has 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void *base, int64_t rows, int rowb) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
-                                           static_cast<int>(rows * rowb), 0x00020000);
-}
-
-template <int D, int NB>
-struct Rows2 {
-  floatx4 acc[NB][D / 16];
-  float m[NB], l[NB];
-  bf16x8 q[NB][D / 32];
-  __device__ __forceinline__ void reset() {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) acc[b][db] = floatx4{0.f, 0.f, 0.f, 0.f};
-      m[b] = -INFINITY;
-      l[b] = 0.0f;
-    }
-  }
-  // row_ptr[b]: start of lane row n of block b (nullptr: padding row, zeros)
-  __device__ __forceinline__ void load_q(const unsigned char *const *row_ptr) {
-    const int g = (threadIdx.x & 63) >> 4;
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk)
-        q[b][kk] = row_ptr[b] ? *reinterpret_cast<const bf16x8 *>(row_ptr[b] + (32 * kk + 8 * g) * 2)
-                              : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  }
-};
-
-typedef short shortx4 __attribute__((ext_vector_type(4)));
-
-// Transposed read of 4 keys x 16 columns of V (see the section comment).
-__device__ __forceinline__ shortx4 ds_read_tr(const unsigned char *p) {
-  typedef __attribute__((address_space(3))) shortx4 *lds_v4;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_v4)((__attribute__((address_space(3))) unsigned char *)(p)));
-}
-
-// One tile (64 keys at absolute position tb) for the first nb of the NB row blocks
-// of this wave.  MASK: keys past `pos` (the wave's node position) are masked; the
-// tile builder left exact zeros in their K and V slots.
-template <int D, int NB, bool MASK>
-__device__ __forceinline__ void attn2_tile(Rows2<D, NB> &st, const unsigned char *lk,
-                                           const unsigned char *lv, int64_t tb, int64_t pos,
-                                           float c2) {
-  using C = Attn2Cfg<D>;
-  const int lane = threadIdx.x & 63, g = lane >> 4, ln = lane & 15;
-  floatx4 s[NB][4];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) s[b][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  // ---- scores S^T = K Q^T: lane (g, n) gets keys 16 kb + 4 g + i of row n
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const int key = 16 * kb + ln;
-#pragma unroll
-    for (int kk = 0; kk < C::KQ; ++kk) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(lk + key * C::LROW + (4 * kk + g) * 16);
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-        s[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, st.q[b][kk], s[b][kb], 0, 0, 0);
-    }
-  }
-  // ---- online softmax in base 2, per block.  The running max only moves when a
-  // tile exceeds it by more than kLazyMax, so probabilities stay below 2^kLazyMax
-  // and the accumulators are rescaled rarely (they live in accumulation registers,
-  // where a rescale costs a read, a multiply and a write per element).
-  bf16x8 pb[NB][2];
-  bool any_corr = false;
-  float corr[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    float z[4][4];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = s[b][kb][i] * c2;
-        if constexpr (MASK) {
-          if (tb + 16 * kb + 4 * g + i > pos) x = -INFINITY;
-        }
-        z[kb][i] = x;
-        mt = fmaxf(mt, x);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const bool move = mt > st.m[b] + kLazyMax;  // always true on a row's first tile
-    const float mn = move ? mt : st.m[b];
-    corr[b] = (move && st.m[b] != -INFINITY) ? exp2_fast(st.m[b] - mn) : 1.0f;
-    any_corr = any_corr || corr[b] != 1.0f;
-    float lt = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const __bf16 e = static_cast<__bf16>(exp2_fast(z[kb][i] - mn));
-        lt = lt + static_cast<float>(e);
-        pb[b][kb >> 1][4 * (kb & 1) + i] = e;
-      }
-    lt = lt + __shfl_xor(lt, 16);
-    lt = lt + __shfl_xor(lt, 32);
-    st.l[b] = st.l[b] * corr[b] + lt;
-    st.m[b] = mn;
-  }
-  if (__any(any_corr)) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) st.acc[b][db] = st.acc[b][db] * corr[b];
-  }
-  // ---- O^T += V^T P^T
-  const int trow = 4 * g + (ln >> 2);  // key of this lane's transposed read, + 32 kk2 (+16)
-  const int tcol4 = 4 * (ln & 3);      // column offset within the 16 columns of block db
-#pragma unroll
-  for (int kk2 = 0; kk2 < 2; ++kk2) {
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-      const int col = 16 * db + tcol4;
-      const int k0 = 32 * kk2 + trow, k1 = k0 + 16;
-      const shortx4 lo = ds_read_tr(lv + k0 * C::LROW + col * 2);
-      const shortx4 hi = ds_read_tr(lv + k1 * C::LROW + col * 2);
-      const bf16x8 a = __builtin_bit_cast(
-          bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1],
-                                                             hi[2], hi[3]});
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-        st.acc[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[b][kk2], st.acc[b][db], 0, 0, 0);
-    }
-  }
-}
-
-template <int D, int NB>
-__device__ __forceinline__ void write_partial2(const Rows2<D, NB> &st, int b, float *acc_row,
-                                               float *ml_row) {
-  const int g = (threadIdx.x & 63) >> 4;
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-    *reinterpret_cast<floatx4 *>(acc_row + 16 * db + 4 * g) = st.acc[b][db];
-  if (g == 0) {
-    ml_row[0] = st.m[b];
-    ml_row[1] = st.l[b];
-  }
-}
-
-// Rewrite the LDS tile rows at positions [max(L, tb), tb + 64) for one node: its
-// ancestor's K and V rows while the depth lasts, zeros after.  Rows below L keep
-// what was loaded.
-template <int D>
-__device__ __forceinline__ void build_node_rows2(unsigned char *stage, const unsigned char *kt,
-                                                 const unsigned char *vt, int hkv, int h,
-                                                 const int8_t *anc, int depth, int64_t tb, int64_t L) {
-  using C = Attn2Cfg<D>;
-  const int k0 = static_cast<int>(L > tb ? L - tb : 0);
-  const int nk = 64 - k0;
-  for (int c = threadIdx.x; c < 2 * nk * C::CPR; c += kAttn2Threads) {
-    const int which = c / (nk * C::CPR);
-    const int key = k0 + (c % (nk * C::CPR)) / C::CPR, cc = c % C::CPR;
-    const int64_t d = tb + key - L;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (d <= depth)
-      x = *reinterpret_cast<const uint4 *>((which ? vt : kt) +
-                                           (static_cast<int64_t>(anc[d]) * hkv + h) * C::ROWB + cc * 16);
-    *reinterpret_cast<uint4 *>(stage + which * C::TILE + key * C::LROW + cc * 16) = x;
-  }
-}
-
-template <int D>
-struct Attn2Lds {
-  unsigned char *s0, *s1;
-  int8_t *anc;
-  int8_t *par;
-};
-
-template <int D>
-__device__ __forceinline__ void attn2_shared_item(const AttnLaunch &P, const AttnTree &T, int it,
-                                                  const Attn2Lds<D> &S) {
-  using C = Attn2Cfg<D>;
-  constexpr int NB = kAttn2Blocks;
-  const int G = P.hq / P.hkv;
-  const int M = T.n * G;
-  const int wave = threadIdx.x >> 6, ln = threadIdx.x & 15;
-  const int split_tiles = T.split / kTile;
-  const int rg = it % T.row_groups;
-  const int rest = it / T.row_groups;
-  const int s = rest % T.n_shared;
-  const int h = rest / T.n_shared;
-  const int blk0 = (rg * kAttn2Waves + wave) * NB;  // first 16-row block of this wave
-  const bool wave_on = blk0 * 16 < M;
-  Rows2<D, NB> st;
-  const unsigned char *qrow[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int r = (blk0 + b) * 16 + ln;
-    qrow[b] = nullptr;
-    if (r < M) {
-      const int node = r / G, j = h * G + r % G;
-      qrow[b] = static_cast<const unsigned char *>(T.q) + (static_cast<int64_t>(node) * P.hq + j) * C::ROWB;
-    }
-  }
-  const __amdgpu_buffer_rsrc_t kres =
-      head_rsrc(static_cast<const unsigned char *>(T.kc) + static_cast<int64_t>(h) * T.cap * C::ROWB, T.L, C::ROWB);
-  const __amdgpu_buffer_rsrc_t vres =
-      head_rsrc(static_cast<const unsigned char *>(T.vc) + static_cast<int64_t>(h) * T.cap * C::ROWB, T.L, C::ROWB);
-  const int64_t t0 = static_cast<int64_t>(s) * split_tiles;
-  // Barriers here are bare s_barrier: LDS is written only by the tile loads, whose
-  // completion each wave establishes with its own vmcnt wait; a fenced barrier would
-  // also wait for the load in flight to the other stage.  The first tile loads while
-  // Q arrives.
-  dma_tile<D>(S.s0, kres, vres, t0 * kTile);
-  if (wave_on) st.load_q(qrow);
-  wait_vm<0>();  // Q and tile 0 are in
-  st.reset();
-  for (int tt = 0; tt < split_tiles; tt += 2) {
-    // even tile in stage 0; tile tt+1 goes to stage 1 meanwhile
-    bare_barrier();  // stage 1 is no longer read (tile tt-1)
-    if (tt + 1 < split_tiles) {
-      dma_tile<D>(S.s1, kres, vres, (t0 + tt + 1) * kTile);
-      wait_vm<C::IPW>();
-    } else {
-      wait_vm<0>();
-    }
-    bare_barrier();  // tile tt is in stage 0 for every wave
-    if (wave_on) attn2_tile<D, NB, false>(st, S.s0, S.s0 + C::TILE, (t0 + tt) * kTile, 0, P.c2);
-    if (tt + 1 >= split_tiles) break;
-    // odd tile in stage 1; tile tt+2 goes to stage 0 meanwhile
-    bare_barrier();  // stage 0 is no longer read
-    if (tt + 2 < split_tiles) {
-      dma_tile<D>(S.s0, kres, vres, (t0 + tt + 2) * kTile);
-      wait_vm<C::IPW>();
-    } else {
-      wait_vm<0>();
-    }
-    bare_barrier();
-    if (wave_on) attn2_tile<D, NB, false>(st, S.s1, S.s1 + C::TILE, (t0 + tt + 1) * kTile, 0, P.c2);
-  }
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int r = (blk0 + b) * 16 + ln;
-    if (r < M) {
-      const int64_t prow = (static_cast<int64_t>(h) * T.nsplit_cap + s) * T.rows_cap + r;
-      write_partial2<D, NB>(st, b, T.part_acc + prow * D, T.part_ml + prow * 2);
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void attn2_tail_item(const AttnLaunch &P, const AttnTree &T, int item,
-                                                const Attn2Lds<D> &S) {
-  using C = Attn2Cfg<D>;
-  const int G = P.hq / P.hkv;
-  const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 15;
-  const int split_tiles = T.split / kTile;
-  const int ngroups = (T.n + kAttn2Waves - 1) / kAttn2Waves;
-  const int h = item / ngroups, ng = item % ngroups;
-  const int node = ng * kAttn2Waves + wave;
-  const bool node_on = node < T.n;
-  int8_t *anc_all = S.anc;
-  const unsigned char *kt = static_cast<const unsigned char *>(T.kt);
-  const unsigned char *vt = static_cast<const unsigned char *>(T.vt);
-  if (ng == 0) {  // stage the tree rows into the cache's pending rows [L, L+n)
-    unsigned char *kcd = static_cast<unsigned char *>(T.kc) + (static_cast<int64_t>(h) * T.cap + T.L) * C::ROWB;
-    unsigned char *vcd = static_cast<unsigned char *>(T.vc) + (static_cast<int64_t>(h) * T.cap + T.L) * C::ROWB;
-    for (int c = tid; c < T.n * C::CPR; c += kAttn2Threads) {
-      const int i = c / C::CPR, cc = c % C::CPR;
-      const int64_t src = (static_cast<int64_t>(i) * P.hkv + h) * C::ROWB + cc * 16;
-      *reinterpret_cast<uint4 *>(kcd + static_cast<int64_t>(i) * C::ROWB + cc * 16) =
-          *reinterpret_cast<const uint4 *>(kt + src);
-      *reinterpret_cast<uint4 *>(vcd + static_cast<int64_t>(i) * C::ROWB + cc * 16) =
-          *reinterpret_cast<const uint4 *>(vt + src);
-    }
-  }
-  if (tid < T.n) S.par[tid] = T.parent[tid];
-  __syncthreads();
-  if (tid < kAttn2Waves) {  // ancestor table of the group's nodes, parents walked in LDS
-    const int x0 = ng * kAttn2Waves + tid;
-    if (x0 < T.n) {
-      int x = x0;
-      for (int d = T.depth[x0]; d >= 0; --d) {
-        anc_all[tid * kMaxNodes + d] = static_cast<int8_t>(x);
-        x = S.par[x];
-      }
-    }
-  }
-  int64_t pos_max = 0;
-  for (int w = 0; w < kAttn2Waves; ++w) {
-    const int x = ng * kAttn2Waves + w;
-    if (x < T.n) pos_max = max(pos_max, T.L + static_cast<int64_t>(T.depth[x]));
-  }
-  const int64_t pos = node_on ? T.L + T.depth[node] : 0;
-  Rows2<D, 1> st;
-  const unsigned char *qrow[1] = {nullptr};
-  if (node_on && ln < G)
-    qrow[0] = static_cast<const unsigned char *>(T.q) + (static_cast<int64_t>(node) * P.hq + h * G + ln) * C::ROWB;
-  if (node_on) st.load_q(qrow);
-  wait_vm<0>();
-  st.reset();
-  const __amdgpu_buffer_rsrc_t kres =
-      head_rsrc(static_cast<const unsigned char *>(T.kc) + static_cast<int64_t>(h) * T.cap * C::ROWB, T.L, C::ROWB);
-  const __amdgpu_buffer_rsrc_t vres =
-      head_rsrc(static_cast<const unsigned char *>(T.vc) + static_cast<int64_t>(h) * T.cap * C::ROWB, T.L, C::ROWB);
-  const int64_t t_first = static_cast<int64_t>(T.n_shared) * split_tiles;
-  const int64_t t_last = pos_max / kTile;
-  const int64_t my_last = pos / kTile;
-  for (int64_t tt = t_first; tt <= t_last; ++tt) {
-    const int64_t tb = tt * kTile;
-    __syncthreads();  // the previous tile is no longer read
-    dma_tile<D>(S.s0, kres, vres, tb);
-    wait_vm<0>();
-    __syncthreads();
-    if (tb + kTile <= T.L) {
-      if (node_on && tt <= my_last) attn2_tile<D, 1, false>(st, S.s0, S.s0 + C::TILE, tb, 0, P.c2);
-    } else {
-      for (int w = 0; w < kAttn2Waves; ++w) {
-        const int x = ng * kAttn2Waves + w;
-        if (x >= T.n || tt > (T.L + T.depth[x]) / kTile) continue;  // uniform over the group
-        build_node_rows2<D>(S.s0, kt, vt, P.hkv, h, anc_all + w * kMaxNodes, T.depth[x], tb, T.L);
-        __syncthreads();
-        if (wave == w) attn2_tile<D, 1, true>(st, S.s0, S.s0 + C::TILE, tb, pos, P.c2);
-        __syncthreads();
-      }
-    }
-    if (node_on && tt <= my_last) {
-      const bool split_end = ((tt + 1) % split_tiles) == 0;
-      if (split_end || tt == my_last) {
-        if (ln < G) {
-          const int s = static_cast<int>(tt / split_tiles);
-          const int64_t prow = (static_cast<int64_t>(h) * T.nsplit_cap + s) * T.rows_cap + node * G + ln;
-          write_partial2<D, 1>(st, 0, T.part_acc + prow * D, T.part_ml + prow * 2);
-        }
-        st.reset();
-      }
-    }
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(kAttn2Threads) void attn2_split_kernel(const AttnLaunch P) {
-  using C = Attn2Cfg<D>;
-  __shared__ __align__(16) unsigned char stage0[C::STAGE];
-  __shared__ __align__(16) unsigned char stage1[C::STAGE];
-  __shared__ int8_t anc[kAttn2Waves * kMaxNodes];
-  __shared__ int8_t par[kMaxNodes];
-  const Attn2Lds<D> S{stage0, stage1, anc, par};
-  const int bid = blockIdx.x;
-  int t = 0;
-  while (t + 1 < P.n_trees && bid >= P.t[t + 1].item_begin) ++t;
-  const AttnTree &T = P.t[t];
-  const int item = bid - T.item_begin;
-  if (item >= T.n_tail_items)
-    attn2_shared_item<D>(P, T, item - T.n_tail_items, S);
-  else
-    attn2_tail_item<D>(P, T, item, S);
-}
-
 // Fold the split partials of one (node, q head) row.  The row's S splits are cut
 // into kFoldWaves contiguous ranges; each wave folds its range in ascending order
 // (kFoldBatch loads in flight), then the range results are folded in ascending
@@ -1497,24 +1013,25 @@ size_t gdn_lds_bytes(int dk, int n_max) {
 
 size_t attn_lds_bytes(int D, int bf16, int n_max) {
   (void)n_max;
-  if (bf16) return 0;  // static LDS: two stages and the ancestor table
+  if (bf16) return 0;  // the kv_* kernels use static LDS only
   return AttnCfg<false, 64>::TILE_BYTES + kAttnWaves * kMaxNodes + kMaxNodes;
 }
 
-int attn_rows_per_item(int bf16) { return bf16 ? kAttn2Waves * kAttn2Blocks * 16 : kAttnWaves * 16; }
-int attn_nodes_per_tail(int bf16) { return bf16 ? kAttn2Waves : kAttnWaves; }
+int attn_rows_per_item(int) { return kAttnWaves * 16; }
+int attn_nodes_per_tail(int) { return kAttnWaves; }
 
 size_t commit_lds_bytes(int D, int bf16, int m) {
   return static_cast<size_t>(m) * D * (bf16 ? 2 : 4);
 }
 
-hipError_t launch_gdn_tree(const GdnLaunch &a, int dk, int bf16, hipStream_t s) {
+hipError_t launch_gdn_tree(const GdnLaunch &a, int dk, int bf16, hipStream_t s, KernelEvents ev) {
   const int blocks = a.t[a.n_trees - 1].wg_begin + a.hv * (a.dv / kGdnCols);
   const size_t lds = gdn_lds_bytes(dk, a.n_max);
 #define HDT_GDN(BF, DK)                                                                   \
   do {                                                                                    \
     (void)set_lds(gdn_tree_kernel<BF, DK>, lds);                                                \
-    hipLaunchKernelGGL((gdn_tree_kernel<BF, DK>), dim3(blocks), dim3(kGdnThreads), lds, s, a); \
+    hipExtLaunchKernelGGL((gdn_tree_kernel<BF, DK>), dim3(blocks), dim3(kGdnThreads), lds, s,     \
+                          ev.start, ev.stop, 0, a);                                               \
   } while (0)
   if (bf16) {
     if (dk == 128) HDT_GDN(true, 128); else HDT_GDN(true, 64);
@@ -1525,38 +1042,32 @@ hipError_t launch_gdn_tree(const GdnLaunch &a, int dk, int bf16, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_attn_split(const AttnLaunch &a, int D, int bf16, int n_blocks, hipStream_t s) {
+hipError_t launch_attn_split(const AttnLaunch &a, int D, int bf16, int n_blocks, hipStream_t s,
+                             KernelEvents ev) {
+  if (bf16 || D != 64) return hipErrorInvalidValue;  // bf16 storage runs the kv_* kernels
   const size_t lds = attn_lds_bytes(D, bf16, a.n_max);
-  if (bf16) {
-    if (D == 256)
-      hipLaunchKernelGGL((attn2_split_kernel<256>), dim3(n_blocks), dim3(kAttn2Threads), 0, s, a);
-    else
-      hipLaunchKernelGGL((attn2_split_kernel<64>), dim3(n_blocks), dim3(kAttn2Threads), 0, s, a);
-  } else {
-    (void)set_lds(attn_split_kernel<false, 64>, lds);
-    hipLaunchKernelGGL((attn_split_kernel<false, 64>), dim3(n_blocks), dim3(kAttnThreads), lds, s, a);
-  }
+  (void)set_lds(attn_split_kernel<false, 64>, lds);
+  hipExtLaunchKernelGGL((attn_split_kernel<false, 64>), dim3(n_blocks), dim3(kAttnThreads), lds, s,
+                        ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fold(const FoldLaunch &a, int D, int bf16, int n_blocks, hipStream_t s) {
-  if (bf16) {
-    if (D == 256)
-      hipLaunchKernelGGL((attn_fold_kernel<true, 256>), dim3(n_blocks), dim3(kFoldThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((attn_fold_kernel<true, 64>), dim3(n_blocks), dim3(kFoldThreads), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((attn_fold_kernel<false, 64>), dim3(n_blocks), dim3(kFoldThreads), 0, s, a);
-  }
+hipError_t launch_attn_fold(const FoldLaunch &a, int D, int bf16, int n_blocks, hipStream_t s,
+                            KernelEvents ev) {
+  if (bf16 || D != 64) return hipErrorInvalidValue;
+  hipExtLaunchKernelGGL((attn_fold_kernel<false, 64>), dim3(n_blocks), dim3(kFoldThreads), 0, s,
+                        ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 
-hipError_t launch_commit(const CommitLaunch &a, int dk, int bf16, int n_blocks, hipStream_t s) {
+hipError_t launch_commit(const CommitLaunch &a, int dk, int bf16, int n_blocks, hipStream_t s,
+                         KernelEvents ev) {
   const size_t lds = commit_lds_bytes(a.D, bf16, a.m);
 #define HDT_COMMIT(BF, DK)                                                                 \
   do {                                                                                     \
     (void)set_lds(commit_kernel<BF, DK>, lds);                                                   \
-    hipLaunchKernelGGL((commit_kernel<BF, DK>), dim3(n_blocks), dim3(kGdnThreads), lds, s, a); \
+    hipExtLaunchKernelGGL((commit_kernel<BF, DK>), dim3(n_blocks), dim3(kGdnThreads), lds, s,     \
+                          ev.start, ev.stop, 0, a);                                                \
   } while (0)
   if (bf16) {
     if (dk == 128) HDT_COMMIT(true, 128); else HDT_COMMIT(true, 64);

@@ -1,0 +1,686 @@
+// kv_attention.hip - one attention layer of the tree verify with bf16 storage, on
+// the CDNA4 (gfx950) matrix cores.
+//
+// Each (node, q head) row attends to every committed row of its kv head and to
+// the tree rows of its ancestors-or-self, node i sitting at position L + depth(i)
+// ("One request, end to end", section 2.6: one forward pass verifies the merged
+// tree; "Adding a model", "The model layer: architecture registry and per-model
+// state": K and V are views indexed by token position).
+//
+// Two kernels per layer:
+//  kv_split_kernel  streams the committed rows.  One workgroup takes one split of
+//                   one kv head for every row of that head (up to kKvWaves * NB * 16
+//                   rows), with kKvTile-key tiles of K and V going straight from HBM
+//                   into a kKvStages-deep LDS ring (buffer_load ... lds), scores
+//                   S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16, and
+//                   an online softmax in base 2.  A split wholly below L leaves one
+//                   normalised fp16 partial per row; the tiles of split L / split
+//                   below tb0 = kKvTile * (L / kKvTile) leave their float32 state.
+//  kv_tree_kernel   one workgroup per (kv head, node, quarter of the output columns):
+//                   wave 0 continues that state through the tiles from tb0 to the
+//                   node's position (rows at or past L are the node's ancestors,
+//                   gathered into LDS by global_load_lds); waves 1-3 fold the
+//                   row's split partials in ascending order meanwhile; then the two
+//                   are combined and the output written.
+//
+// A row's result is a function of its query and of the key/value sequence by
+// absolute position only (the verified row equals the decode step's row, "Adding
+// a model", step 4 of "The adapter path in ten steps"):
+//  - tiles and splits are anchored at absolute positions; a tile is processed by
+//    the same instruction sequence in both kernels, and an MFMA output column
+//    depends on its own row only;
+//  - masked slots hold a finite row (the node's own) and get probability 0;
+//  - the running max moves only when a tile exceeds it by more than kLazyMax, a
+//    rule that depends on the row's scores alone;
+//  - every split but a row's last enters the fold as its normalised fp16 partial,
+//    whichever kernel finished it.  The committed splits fold in chunks of
+//    kFoldChunk (the chunk's max, then weighted sums in ascending split order; the
+//    chunks merge in order), then the split finished in the tree pass if the node's
+//    rows cross into the next split, then the last split's float32 state.
+#include "common.h"
+
+#pragma clang fp contract(off)
+
+namespace hdt {
+namespace {
+
+// Probabilities stay below 2^kLazyMax: the running max moves only when a tile's max
+// exceeds it by more than this (base-2 units).
+constexpr float kLazyMax = 8.0f;
+
+template <int D>
+struct KvCfg {
+  static constexpr int ROWB = D * 2;                 // bytes per row
+  static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+  static constexpr int HALF = kKvTile * ROWB;        // K (or V) part of a tile
+  static constexpr int TILE = 2 * HALF;              // K then V
+  static constexpr int LOADS = TILE / 1024;          // wave-wide 16-byte-per-lane loads per tile
+  static constexpr int RPL = 1024 / ROWB;            // rows per wave-wide load
+  static constexpr int KQ = D / 32;                  // k-steps of the score MFMA
+  static constexpr int DB = D / 16;                  // 16-column blocks of a row
+  static constexpr int QD = D / kKvQuarters;         // output columns per tree-pass block
+  static constexpr int QDB = QD / 16;
+  static_assert(LOADS % 8 == 0 && QD % 16 == 0 && 1024 % ROWB == 0, "tile shape");
+};
+
+// XOR swizzle of the 16-byte chunks of tile row `row`: keeps the score operand
+// reads (16 keys at one chunk) and the transposed value reads (4 keys at two
+// chunks) free of LDS bank conflicts.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 256) {
+    return (2 * row) & 31;
+  } else {
+    return (row >> 1) & (KvCfg<D>::CPR - 1);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ int chunk_off(int row, int c) {
+  return row * KvCfg<D>::ROWB + ((c ^ swz<D>(row)) << 4);
+}
+
+// Online-softmax state of up to NB 16-row blocks of one wave.  Lane (g, n) holds
+// row n of each block; acc[b][j][i] is output column 16 (db0 + j) + 4 g + i.
+template <int D, int NB, int NDB>
+struct KvRows {
+  floatx4 acc[NB][NDB];
+  float m[NB], l[NB];
+  bf16x8 q[NB][D / 32];
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int j = 0; j < NDB; ++j) acc[b][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+      m[b] = -INFINITY;
+      l[b] = 0.0f;
+    }
+  }
+};
+
+// One tile (kKvTile keys from absolute position tb; K then V in `tile`, swizzled)
+// for the NB row blocks of this wave, output columns [16 db0, 16 (db0 + NDB)).
+// MASK: keys past `pos` get probability 0.  Every block is computed (a block with
+// no rows of its own holds copies of real queries and is discarded by the caller),
+// so the instruction stream has no branches; all LDS reads of an operand are
+// issued before the MFMAs that use them, and the value reads before the softmax.
+template <int D, int NB, int NDB, bool MASK>
+__device__ __forceinline__ void kv_tile(KvRows<D, NB, NDB> &st, const unsigned char *tile, int db0,
+                                        int64_t tb, int64_t pos, float c2) {
+  using C = KvCfg<D>;
+  const int lane = threadIdx.x & 63, g = lane >> 4, ln = lane & 15;
+  const unsigned char *lk = tile;
+  const unsigned char *lv = tile + C::HALF;
+  // ---- scores S^T = K Q^T: lane (g, n) gets keys 16 kb + 4 g + i of row n
+  bf16x8 ka[2][C::KQ];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int kk = 0; kk < C::KQ; ++kk)
+      ka[kb][kk] = *reinterpret_cast<const bf16x8 *>(lk + chunk_off<D>(16 * kb + ln, 4 * kk + g));
+  floatx4 s[NB][2];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) s[b][0] = s[b][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < C::KQ; ++kk)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        s[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][kk], st.q[b][kk], s[b][kb], 0, 0, 0);
+  // ---- value operands for O^T += V^T P^T.  The transposed read gives lane (g, m)
+  // the values of keys 4 g + e (lo) and 16 + 4 g + e (hi), e = 0..3, at column
+  // 16 db + m: the same key order as the probabilities below.
+  const int r0 = 4 * g + (ln >> 2);
+  const int half8 = 8 * (ln & 1);
+  bf16x8 va[NDB];
+#pragma unroll
+  for (int j = 0; j < NDB; ++j) {
+    const int c = 2 * (db0 + j) + ((ln & 3) >> 1);
+    const shortx4 lo = ds_read_tr(lv + chunk_off<D>(r0, c) + half8);
+    const shortx4 hi = ds_read_tr(lv + chunk_off<D>(r0 + 16, c) + half8);
+    va[j] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+                                           lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+  }
+  // ---- online softmax, base 2, lazy max
+  bf16x8 pb[NB];
+  float corr[NB];
+  bool any_corr = false;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float z[2][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = s[b][kb][i] * c2;
+        if constexpr (MASK) {
+          if (tb + 16 * kb + 4 * g + i > pos) x = -INFINITY;
+        }
+        z[kb][i] = x;
+        mt = fmaxf(mt, x);
+      }
+    mt = rows4_max(mt);
+    const bool move = mt > st.m[b] + kLazyMax;  // always true on a row's first tile
+    const float mn = move ? mt : st.m[b];
+    corr[b] = (move && st.m[b] != -INFINITY) ? exp2_fast(st.m[b] - mn) : 1.0f;
+    any_corr = any_corr || corr[b] != 1.0f;
+    float lt = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 e = static_cast<__bf16>(exp2_fast(z[kb][i] - mn));
+        lt = lt + static_cast<float>(e);
+        pb[b][4 * kb + i] = e;
+      }
+    lt = rows4_sum(lt);
+    st.l[b] = st.l[b] * corr[b] + lt;
+    st.m[b] = mn;
+  }
+  if (__any(any_corr)) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < NDB; ++j) st.acc[b][j] = st.acc[b][j] * corr[b];
+  }
+#pragma unroll
+  for (int j = 0; j < NDB; ++j)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      st.acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j], pb[b], st.acc[b][j], 0, 0, 0);
+}
+
+// Normalised partial of 4 columns: acc / l rounded to fp16, packed.
+__device__ __forceinline__ uint2 norm_half4(floatx4 acc, float inv_l) {
+  const _Float16 h0 = static_cast<_Float16>(acc[0] * inv_l);
+  const _Float16 h1 = static_cast<_Float16>(acc[1] * inv_l);
+  const _Float16 h2 = static_cast<_Float16>(acc[2] * inv_l);
+  const _Float16 h3 = static_cast<_Float16>(acc[3] * inv_l);
+  uint2 r;
+  r.x = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h0)) |
+        (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
+  r.y = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h2)) |
+        (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h3)) << 16);
+  return r;
+}
+
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu)));
+}
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+// This wave's share (IPW wave-wide loads) of the direct-to-LDS loads of a tile of
+// one kv head.  Lane l of a wave-wide load lands at LDS (M0 + 16 l); the lane picks
+// the global chunk that the swizzle puts there.  The loads are issued from inline
+// assembly so that the compiler does not fence later LDS reads on them; the caller
+// waits with wait_vm before the barrier that publishes the tile.
+template <int D, int W>
+struct KvDma {
+  static constexpr int IPW = KvCfg<D>::LOADS / W;
+  uint32_t off[IPW];  // byte offset of this lane's chunk within the tile's rows
+  int ins0;           // first wave-wide load of this wave (uniform)
+  __device__ __forceinline__ void init() {
+    using C = KvCfg<D>;
+    ins0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * IPW;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int x = 0; x < IPW; ++x) {
+      const int li = (ins0 + x) % (C::LOADS / 2);
+      const int row = li * C::RPL + lane / C::CPR;
+      const int cs = lane % C::CPR;
+      off[x] = static_cast<uint32_t>(row * C::ROWB + ((cs ^ swz<D>(row)) << 4));
+    }
+  }
+  // Rows [tb, tb + kKvTile) into `stage`.
+  __device__ __forceinline__ void issue(unsigned char *stage, __amdgpu_buffer_rsrc_t kres,
+                                        __amdgpu_buffer_rsrc_t vres, int64_t tb) const {
+    using C = KvCfg<D>;
+    const uint32_t base = static_cast<uint32_t>(tb * C::ROWB);
+    const uint32_t lds = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char *)(stage)));
+#pragma unroll
+    for (int x = 0; x < IPW; ++x) {
+      const int ins = ins0 + x;
+      const bool v = ins >= C::LOADS / 2;  // uniform over the wave
+      asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                   :
+                   : "v"(base + off[x]), "s"(lds + ins * 1024), "s"(v ? vres : kres)
+                   : "memory", "m0");
+    }
+  }
+};
+
+// ============================================================================ split pass
+
+// Offset of the 8-byte group (4 columns) that lane `lane` of row block `blk` holds for
+// 16-column block db, in the partials of (kv head h, split s): partials are stored in
+// the MFMA output layout, 512 contiguous bytes per (row block, column block).
+template <int D>
+__device__ __forceinline__ int64_t part_off(const KvTree &T, int h, int s, int blk, int db, int lane) {
+  const int64_t nblk_cap = (T.rows_cap + 15) / 16;
+  return ((((static_cast<int64_t>(h) * T.nsplit_cap + s) * nblk_cap + blk) * KvCfg<D>::DB + db) * 64 + lane) * 8;
+}
+
+// Direct-to-LDS load of query rows [row0, row0 + 16 * nq) of kv head h (row r is q
+// head h * G + r % G of node r / G; rows past the tree's are clamped to its last row)
+// into `dst`, swizzled like a K tile.  Issued by every wave, RPL rows per load.
+template <int D, int W>
+__device__ __forceinline__ void q_dma(unsigned char *dst, __amdgpu_buffer_rsrc_t qres, int row0, int nq, int M,
+                                      int G, int hq, int h) {
+  using C = KvCfg<D>;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int loads = 16 * nq / C::RPL;
+  for (int ins = wave; ins < loads; ins += W) {
+    const int row = ins * C::RPL + lane / C::CPR;
+    const int cs = lane % C::CPR;
+    const int r = min(row0 + row, M - 1);
+    const uint32_t off = static_cast<uint32_t>((static_cast<int64_t>(r / G) * hq + h * G + r % G) * C::ROWB +
+                                               ((cs ^ swz<D>(row)) << 4));
+    const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) unsigned char *)(dst + ins * 1024)));
+    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :
+                 : "v"(off), "s"(m0), "s"(qres)
+                 : "memory", "m0");
+  }
+}
+
+template <int D, int W, int NB>
+__global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
+  using C = KvCfg<D>;
+  constexpr int S = kKvStages;
+  constexpr int IPW = KvDma<D, W>::IPW;
+  // queries of the item (W * NB blocks of 16 rows) sit in the last QS stages until
+  // they are in registers
+  constexpr int QS = (W * NB * 16 * C::ROWB + C::TILE - 1) / C::TILE;
+  static_assert(QS < S, "the queries must leave a stage for the first tile");
+  __shared__ __align__(1024) unsigned char ring[S][C::TILE];
+  const int bid = blockIdx.x;
+  int t = 0;
+  while (t + 1 < P.n_trees && bid >= P.t[t + 1].a_begin) ++t;
+  const KvTree &T = P.t[t];
+  const int local = bid - T.a_begin;
+  const int h = local / T.a_per_head, r = local % T.a_per_head;
+  const int rg = r % T.row_groups, s = r / T.row_groups;
+  const bool carry = s == T.n_full;  // the tiles of split n_full below tb0
+  const int G = P.hq / P.hkv;
+  const int M = T.n * G;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, ln = lane & 15;
+  const int split_tiles = T.split / kKvTile;
+  const int ntiles = carry ? T.carry_tiles : split_tiles;
+  const int64_t tile0 = static_cast<int64_t>(s) * split_tiles;
+  // Row blocks of the item: [rblk0, rblk0 + nblk); wave w takes blocks rblk0 + NB w + k.
+  // Waves past the rows only load.
+  const int rblk0 = rg * W * NB;
+  const int nblk = min(W * NB, (M + 15) / 16 - rblk0);
+  const bool computes = wave * NB < nblk;
+
+  const unsigned char *kc = static_cast<const unsigned char *>(T.kc) + static_cast<int64_t>(h) * T.cap * C::ROWB;
+  const unsigned char *vc = static_cast<const unsigned char *>(T.vc) + static_cast<int64_t>(h) * T.cap * C::ROWB;
+  const __amdgpu_buffer_rsrc_t kres = make_rsrc(kc, T.L * C::ROWB);
+  const __amdgpu_buffer_rsrc_t vres = make_rsrc(vc, T.L * C::ROWB);
+  const __amdgpu_buffer_rsrc_t qres = make_rsrc(T.q, static_cast<int64_t>(T.n) * P.hq * C::ROWB);
+
+  // ---- prologue: queries and the first S - QS tiles in flight together
+  // every computing wave gets NB blocks of real query rows (past the tree's rows,
+  // copies of its last row)
+  KvDma<D, W> dma;
+  dma.init();
+  q_dma<D, W>(ring[S - QS], qres, 16 * rblk0, (nblk + NB - 1) / NB * NB, M, G, P.hq, h);
+  const int first = min(S - QS, ntiles);
+  for (int x = 0; x < first; ++x) dma.issue(ring[x], kres, vres, (tile0 + x) * kKvTile);
+  // this wave's query loads are the oldest; tiles 1 .. first - 1 may stay in flight
+  switch (first - 1) {
+    case 3: wait_vm<3 * IPW>(); break;
+    case 2: wait_vm<2 * IPW>(); break;
+    case 1: wait_vm<IPW>(); break;
+    default: wait_vm<0>(); break;
+  }
+  bare_barrier();  // queries and tile 0 are in LDS
+  KvRows<D, NB, C::DB> st;
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int row = 16 * (NB * wave + k) + ln;
+#pragma unroll
+    for (int kk = 0; kk < C::KQ; ++kk)
+      st.q[k][kk] = *reinterpret_cast<const bf16x8 *>(ring[S - QS] + chunk_off<D>(row, 4 * kk + g));
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // query reads done (lgkmcnt 0)
+  bare_barrier();                      // the query stages are free
+  for (int x = first; x < S - 1 && x < ntiles; ++x) dma.issue(ring[x], kres, vres, (tile0 + x) * kKvTile);
+  st.reset();
+  for (int tt = 0; tt < ntiles; ++tt) {
+    if (tt > 0) {
+      // tiles tt .. tt + ahead are in flight; wait for tile tt
+      const int ahead = min(S - 2, ntiles - 1 - tt);
+      if (ahead >= 3) {
+        wait_vm<3 * IPW>();
+      } else if (ahead == 2) {
+        wait_vm<2 * IPW>();
+      } else if (ahead == 1) {
+        wait_vm<IPW>();
+      } else {
+        wait_vm<0>();
+      }
+      bare_barrier();  // tile tt landed for every wave; tile tt - 1 is no longer read
+    }
+    if (tt + S - 1 < ntiles) dma.issue(ring[(tt + S - 1) % S], kres, vres, (tile0 + tt + S - 1) * kKvTile);
+    if (computes) kv_tile<D, NB, C::DB, false>(st, ring[tt % S], 0, 0, 0, P.c2);
+  }
+  if (!computes) return;
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int blk = rblk0 + NB * wave + k;
+    const int row = 16 * blk + ln;
+    if (!carry) {
+      // normalised fp16 partial in the MFMA output layout: 512 B per column block
+      unsigned char *po = static_cast<unsigned char *>(T.part_o);
+      const float inv_l = 1.0f / st.l[k];
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+        *reinterpret_cast<uint2 *>(po + part_off<D>(T, h, s, blk, db, lane)) = norm_half4(st.acc[k][db], inv_l);
+      if (g == 0 && row < M) {
+        const int64_t prow = (static_cast<int64_t>(h) * T.nsplit_cap + s) * T.rows_cap + row;
+        *reinterpret_cast<float2 *>(T.part_ml + prow * 2) = make_float2(st.m[k], st.l[k]);
+      }
+    } else if (row < M) {
+      const int64_t crow = static_cast<int64_t>(h) * T.rows_cap + row;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+        *reinterpret_cast<floatx4 *>(T.carry_acc + crow * D + 16 * db + 4 * g) = st.acc[k][db];
+      if (g == 0) *reinterpret_cast<float2 *>(T.carry_ml + crow * 2) = make_float2(st.m[k], st.l[k]);
+    }
+  }
+}
+
+// ============================================================================ tree pass
+
+struct Fold2 {
+  float m, l, x0, x1;
+};
+
+__device__ __forceinline__ Fold2 fold_empty() { return Fold2{-INFINITY, 0.0f, 0.0f, 0.0f}; }
+
+// Add a normalised partial (max ms, sum ls, columns o0, o1).
+__device__ __forceinline__ void fold_norm(Fold2 &f, float ms, float ls, float o0, float o1) {
+  const float mn = fmaxf(f.m, ms);
+  const float a = exp2_fast(f.m - mn), b = exp2_fast(ms - mn);
+  const float w = ls * b;
+  f.l = f.l * a + w;
+  f.x0 = f.x0 * a + o0 * w;
+  f.x1 = f.x1 * a + o1 * w;
+  f.m = mn;
+}
+
+// Add an unnormalised state (a folded group, or a row's last split).
+__device__ __forceinline__ void fold_acc(Fold2 &f, const Fold2 &y) {
+  const float mn = fmaxf(f.m, y.m);
+  const float a = exp2_fast(f.m - mn), b = exp2_fast(y.m - mn);
+  f.l = f.l * a + y.l * b;
+  f.x0 = f.x0 * a + y.x0 * b;
+  f.x1 = f.x1 * a + y.x1 * b;
+  f.m = mn;
+}
+
+constexpr int kFoldChunk = 64;          // split partials in flight per fold thread
+constexpr int kFoldThreadsKv = kKvThreads - 64;
+
+template <int D>
+__global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
+  using C = KvCfg<D>;
+  constexpr int QD = C::QD, QDB = C::QDB, HP = QD / 2;
+  constexpr int MAX_TILES = 3;  // (kKvTile - 1 + kMaxNodes - 1) / kKvTile + 1
+  static_assert((kKvTile - 1 + kMaxNodes - 1) / kKvTile + 1 <= MAX_TILES, "tree tiles");
+  __shared__ __align__(1024) unsigned char tiles[MAX_TILES][C::TILE];
+  __shared__ __align__(16) float x_o[16][QD];   // finished split n_full (crossing), fp16 values
+  __shared__ float x_ml[16][2];
+  __shared__ __align__(16) float f_acc[16][QD];  // the row's last split, float32 state
+  __shared__ float f_ml[16][2];
+  const int bid = blockIdx.x;
+  int t = 0;
+  while (t + 1 < P.n_trees && bid >= P.t[t + 1].b_begin) ++t;
+  const KvTree &T = P.t[t];
+  const int local = bid - T.b_begin;
+  const int qd = local % kKvQuarters, rest = local / kKvQuarters;
+  const int node = rest % T.n, h = rest / T.n;
+  const int G = P.hq / P.hkv;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, ln = lane & 15;
+  const int dep = T.depth[node];
+  const int64_t L = T.L, pos = L + dep;
+  const int64_t tb0 = (L / kKvTile) * kKvTile;
+  const int ntree = static_cast<int>((pos / kKvTile) * kKvTile - tb0) / kKvTile + 1;
+  const bool crossing = pos / T.split > T.n_full;  // at most one boundary: split > 94
+  const unsigned char *kt = static_cast<const unsigned char *>(T.kt);
+  const unsigned char *vt = static_cast<const unsigned char *>(T.vt);
+  const unsigned char *kc = static_cast<const unsigned char *>(T.kc) + static_cast<int64_t>(h) * T.cap * C::ROWB;
+  const unsigned char *vc = static_cast<const unsigned char *>(T.vc) + static_cast<int64_t>(h) * T.cap * C::ROWB;
+
+  if (wave == 0) {
+    // ---- ancestors: lane d holds the node's ancestor at depth d (the node itself
+    // past its depth, the filler of masked slots)
+    const int par_v = lane < T.n ? T.parent[lane] : -1;
+    int anc_v = node;
+    {
+      int x = node;
+      for (int d = dep; d >= 0; --d) {
+        if (lane == d) anc_v = x;
+        if (d > 0) x = __builtin_amdgcn_readlane(par_v, x);
+      }
+    }
+    // ---- gather the node's tiles into LDS: committed rows below L, then the
+    // ancestors' tree rows, then the filler.  A wave-wide load covers kKvTile-row
+    // slices of RPL rows; the row's source is uniform over its CPR lanes.
+    for (int tt = 0; tt < ntree; ++tt) {
+      const int64_t tb = tb0 + static_cast<int64_t>(kKvTile) * tt;
+#pragma unroll
+      for (int li = 0; li < C::LOADS / 2; ++li) {
+        const int row = li * C::RPL + lane / C::CPR;
+        const int cs = lane % C::CPR;
+        const int64_t p = tb + row;
+        // the tree row of position p >= L: ancestor at depth p - L, or the node
+        int x = node;
+#pragma unroll
+        for (int rr = 0; rr < C::RPL; ++rr) {
+          const int64_t pr = tb + li * C::RPL + rr;  // uniform
+          if (pr >= L && pr <= pos) {
+            const int a = __builtin_amdgcn_readlane(anc_v, static_cast<int>(pr - L));
+            if (lane / C::CPR == rr) x = a;
+          }
+        }
+        const int64_t off_c = static_cast<int64_t>((cs ^ swz<D>(row)) << 4);
+        const unsigned char *ksrc, *vsrc;
+        if (p < L) {
+          ksrc = kc + p * C::ROWB + off_c;
+          vsrc = vc + p * C::ROWB + off_c;
+        } else {
+          ksrc = kt + (static_cast<int64_t>(x) * P.hkv + h) * C::ROWB + off_c;
+          vsrc = vt + (static_cast<int64_t>(x) * P.hkv + h) * C::ROWB + off_c;
+        }
+        __builtin_amdgcn_global_load_lds(
+            ksrc, (__attribute__((address_space(3))) void *)(tiles[tt] + li * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            vsrc, (__attribute__((address_space(3))) void *)(tiles[tt] + C::HALF + li * 1024), 16, 0, 0);
+      }
+    }
+    // ---- queries and the carried state of split n_full (lanes past the node's q
+    // heads read a real row and are discarded)
+    KvRows<D, 1, QDB> st;
+    st.reset();
+    {
+      const int jr = min(ln, G - 1);
+      const unsigned char *qrow =
+          static_cast<const unsigned char *>(T.q) + (static_cast<int64_t>(node) * P.hq + h * G + jr) * C::ROWB;
+#pragma unroll
+      for (int kk = 0; kk < C::KQ; ++kk) st.q[0][kk] = *reinterpret_cast<const bf16x8 *>(qrow + (32 * kk + 8 * g) * 2);
+      if (T.carry_tiles > 0) {
+        const int64_t crow = static_cast<int64_t>(h) * T.rows_cap + node * G + jr;
+        const float2 ml = *reinterpret_cast<const float2 *>(T.carry_ml + crow * 2);
+        st.m[0] = ml.x;
+        st.l[0] = ml.y;
+#pragma unroll
+        for (int j = 0; j < QDB; ++j)
+          st.acc[0][j] = *reinterpret_cast<const floatx4 *>(T.carry_acc + crow * D + 16 * (qd * QDB + j) + 4 * g);
+      }
+    }
+    wait_vm<0>();  // the gathered tiles are in LDS
+    for (int tt = 0; tt < ntree; ++tt) {
+      const int64_t tb = tb0 + static_cast<int64_t>(kKvTile) * tt;
+      if (tt > 0 && tb % T.split == 0) {
+        // split n_full ends here: it enters the fold as a normalised partial
+        if (ln < G) {
+          const float inv_l = 1.0f / st.l[0];
+#pragma unroll
+          for (int j = 0; j < QDB; ++j) {
+            const uint2 hv = norm_half4(st.acc[0][j], inv_l);
+            float *dst = &x_o[ln][16 * j + 4 * g];
+            dst[0] = half_lo(hv.x);
+            dst[1] = half_hi(hv.x);
+            dst[2] = half_lo(hv.y);
+            dst[3] = half_hi(hv.y);
+          }
+          if (g == 0) {
+            x_ml[ln][0] = st.m[0];
+            x_ml[ln][1] = st.l[0];
+          }
+        }
+        st.reset();
+      }
+      kv_tile<D, 1, QDB, true>(st, tiles[tt], qd * QDB, tb, pos, P.c2);
+    }
+    if (ln < G) {
+#pragma unroll
+      for (int j = 0; j < QDB; ++j) *reinterpret_cast<floatx4 *>(&f_acc[ln][16 * j + 4 * g]) = st.acc[0][j];
+      if (g == 0) {
+        f_ml[ln][0] = st.m[0];
+        f_ml[ln][1] = st.l[0];
+      }
+    }
+  }
+
+  // ---- waves 1..3: the pending rows, then the fold of the split partials
+  if (wave == 1 && qd == 0) {
+    // this node's tree rows go to the cache's pending row L + node
+    for (int c = lane; c < 2 * C::CPR; c += 64) {
+      const int which = c / C::CPR, cc = c % C::CPR;
+      const uint4 x = *reinterpret_cast<const uint4 *>((which ? vt : kt) +
+                                                       (static_cast<int64_t>(node) * P.hkv + h) * C::ROWB + cc * 16);
+      unsigned char *dst = static_cast<unsigned char *>(which ? T.vc : T.kc) +
+                           (static_cast<int64_t>(h) * T.cap + L + node) * C::ROWB + cc * 16;
+      *reinterpret_cast<uint4 *>(dst) = x;
+    }
+  }
+  // Each fold thread takes (row, column pair) items in turn.  The row's splits
+  // before its last (the committed ones, then split n_full if the node's rows
+  // cross into the next split) fold in chunks of kFoldChunk by split index: the
+  // chunk's max first, then its weighted sums in ascending split order; chunks
+  // merge in order.  The chunks before the last fold while wave 0 runs the tree
+  // tiles; the last chunk's loads wait in registers for the split finished there.
+  const int fid = tid - 64;
+  const int items = G * HP;
+  const int n_nl = T.n_full + (crossing ? 1 : 0);       // splits before the row's last
+  const int c_last = n_nl > 0 ? (n_nl - 1) / kFoldChunk * kFoldChunk : 0;
+  const int ns_last = n_nl - c_last;                    // splits in the last chunk
+  const int nm_last = min(ns_last, T.n_full - c_last);  // of which in memory
+  const bool fold_thread = wave > 0 && fid < items;     // one item per thread (items <= 192)
+  Fold2 tot = fold_empty();
+  float2 mlv[kFoldChunk];
+  uint32_t ov[kFoldChunk];
+  int R = 0, col = 0, flane = 0;
+  int64_t ml0 = 0;
+  auto load_chunk = [&](int c0, int nm) {  // loads past the memory splits repeat the last one
+#pragma unroll
+    for (int j = 0; j < kFoldChunk; ++j) {
+      const int sj = c0 + max(0, min(j, nm - 1));
+      mlv[j] = *reinterpret_cast<const float2 *>(T.part_ml + (ml0 + static_cast<int64_t>(sj) * T.rows_cap) * 2);
+      ov[j] = *reinterpret_cast<const uint32_t *>(static_cast<const unsigned char *>(T.part_o) +
+                                                  part_off<D>(T, h, sj, R >> 4, col >> 4, flane) + (col & 3) * 2);
+    }
+  };
+  auto fold_chunk = [&](int ns, int jx, float xm, float xl, float xo0, float xo1) {
+    float mc = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kFoldChunk; ++j)
+      if (j < ns) mc = fmaxf(mc, j == jx ? xm : mlv[j].x);
+    Fold2 ch{mc, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < kFoldChunk; ++j) {
+      if (j < ns) {
+        const bool x = j == jx;
+        const float w = (x ? xl : mlv[j].y) * exp2_fast((x ? xm : mlv[j].x) - mc);
+        ch.l = ch.l + w;
+        ch.x0 = ch.x0 + w * (x ? xo0 : half_lo(ov[j]));
+        ch.x1 = ch.x1 + w * (x ? xo1 : half_hi(ov[j]));
+      }
+    }
+    fold_acc(tot, ch);
+  };
+  if (fold_thread) {
+    const int r = fid / HP, cp = fid % HP;
+    R = node * G + r;
+    col = qd * QD + 2 * cp;
+    flane = ((col & 15) >> 2) * 16 + (R & 15);
+    ml0 = static_cast<int64_t>(h) * T.nsplit_cap * T.rows_cap + R;
+    for (int c0 = 0; c0 < c_last; c0 += kFoldChunk) {
+      load_chunk(c0, kFoldChunk);
+      fold_chunk(kFoldChunk, -1, 0.f, 0.f, 0.f, 0.f);
+    }
+    if (nm_last > 0) load_chunk(c_last, nm_last);
+  }
+  __syncthreads();
+  if (fold_thread) {
+    const int r = fid / HP, cp = fid % HP;
+    if (ns_last > 0) {
+      if (crossing) {
+        fold_chunk(ns_last, T.n_full - c_last, x_ml[r][0], x_ml[r][1], x_o[r][2 * cp], x_o[r][2 * cp + 1]);
+      } else {
+        fold_chunk(ns_last, -1, 0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    fold_acc(tot, Fold2{f_ml[r][0], f_ml[r][1], f_acc[r][2 * cp], f_acc[r][2 * cp + 1]});
+    const float inv = 1.0f / tot.l;
+    const uint32_t w = static_cast<uint32_t>(bf16_bits(tot.x0 * inv)) |
+                       (static_cast<uint32_t>(bf16_bits(tot.x1 * inv)) << 16);
+    *reinterpret_cast<uint32_t *>(static_cast<unsigned char *>(T.o) +
+                                  ((static_cast<int64_t>(node) * P.hq + h * G + r) * D + qd * QD + 2 * cp) * 2) = w;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_split(const KvLaunch &a, int D, int waves, int nb, int n_blocks, hipStream_t s,
+                           KernelEvents ev) {
+#define HDT_KV_SPLIT(DD, W, NB)                                                                         \
+  hipExtLaunchKernelGGL((kv_split_kernel<DD, W, NB>), dim3(n_blocks), dim3(W * 64), 0, s, ev.start, ev.stop, \
+                        0, a)
+  if (D == 256) {
+    if (waves == 8 && nb == 1) HDT_KV_SPLIT(256, 8, 1);
+    else if (waves == 4 && nb == 3) HDT_KV_SPLIT(256, 4, 3);
+    else return hipErrorInvalidValue;
+  } else if (D == 64) {
+    if (waves == 8 && nb == 1) HDT_KV_SPLIT(64, 8, 1);
+    else if (waves == 4 && nb == 3) HDT_KV_SPLIT(64, 4, 3);
+    else return hipErrorInvalidValue;
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef HDT_KV_SPLIT
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_tree(const KvLaunch &a, int D, int n_blocks, hipStream_t s, KernelEvents ev) {
+  if (D == 256) {
+    hipExtLaunchKernelGGL((kv_tree_kernel<256>), dim3(n_blocks), dim3(kKvThreads), 0, s, ev.start, ev.stop, 0, a);
+  } else if (D == 64) {
+    hipExtLaunchKernelGGL((kv_tree_kernel<64>), dim3(n_blocks), dim3(kKvThreads), 0, s, ev.start, ev.stop, 0, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hdt

@@ -14,12 +14,14 @@ namespace hdt {
 
 constexpr int kMaxNodes = 64;
 constexpr int kMaxTrees = 8;
-constexpr int kTile = 64;          // attention keys per tile, anchored at absolute positions
+constexpr int kTile = 64;          // float32 attention: keys per tile, anchored at absolute positions
 constexpr int kAttnWaves = 8;      // waves per attention workgroup (float32 storage)
 constexpr int kAttnThreads = kAttnWaves * 64;
-constexpr int kAttn2Waves = 4;     // bf16 storage: waves per workgroup, one per SIMD
-constexpr int kAttn2Threads = kAttn2Waves * 64;
-constexpr int kAttn2Blocks = 2;    // bf16 storage: 16-row blocks per wave
+constexpr int kKvTile = 32;        // bf16 attention: keys per tile, anchored at absolute positions
+constexpr int kKvWaves = 4;        // bf16 attention: waves per tree-pass workgroup, one per SIMD
+constexpr int kKvThreads = kKvWaves * 64;
+constexpr int kKvStages = 5;       // bf16 attention: LDS tile ring of the split pass
+constexpr int kKvQuarters = 4;     // bf16 attention: output columns split over this many blocks
 constexpr int kGdnThreads = 256;   // 4 waves x 4 value columns x 16 lanes per column
 constexpr int kGdnCols = 16;       // value columns per GDN workgroup
 constexpr int kFoldThreads = 256;  // 4 waves per output row
@@ -79,6 +81,46 @@ struct AttnLaunch {
   float c2;                               // softmax scale times log2(e)
 };
 
+// ---------------------------------------------------------------- attention, bf16 storage
+// Positions are cut into splits of `split` keys (a multiple of kKvTile fixed by the
+// slot's capacity) and splits into kKvTile-key tiles, both anchored at absolute
+// positions.  The split pass (kv_split_kernel) streams every split wholly below L
+// for all (node, q head) rows of a kv head and writes one normalised fp16 partial
+// per (row, split); it also runs the tiles of split n_full = L / split that lie
+// below tb0 = kKvTile * (L / kKvTile) and leaves their float32 running state (the
+// carry).  The tree pass (kv_tree_kernel) takes one (kv head, node, column
+// quarter): it continues from the carry through the tiles from tb0 to the node's
+// own position, whose rows at or past L are the node's ancestors, and folds every
+// split of the row in ascending order.
+struct KvTree {
+  const void *q;                          // [n][hq][D]
+  const void *kt, *vt;                    // tree rows [n][hkv][D]
+  void *kc, *vc;                          // cache of this layer [hkv][cap][D]
+  void *o;                                // [n][hq][D]
+  void *part_o;                           // fp16 [hkv][nsplit_cap][rows_cap/16][D/16][64][4] (MFMA layout)
+  float *part_ml;                         // [hkv][nsplit_cap][rows_cap][2]: max (base 2), sum
+  float *carry_acc;                       // [hkv][rows_cap][D]
+  float *carry_ml;                        // [hkv][rows_cap][2]
+  int64_t L, cap;
+  int32_t n;
+  int32_t split;                          // keys per split
+  int32_t nsplit_cap, rows_cap;
+  int32_t n_full;                         // splits wholly below L
+  int32_t carry_tiles;                    // tiles of split n_full below tb0
+  int32_t row_groups;                     // split-pass items per split (row blocks / blocks per item)
+  int32_t a_begin, a_per_head;            // split pass: first block, items per kv head
+  int32_t b_begin;                        // tree pass: first block
+  int8_t parent[kMaxNodes];
+  int8_t depth[kMaxNodes];
+};
+
+struct KvLaunch {
+  KvTree t[kMaxTrees];
+  int32_t n_trees;
+  int32_t hq, hkv;
+  float c2;                               // softmax scale times log2(e)
+};
+
 // ---------------------------------------------------------------- attention fold
 struct FoldTree {
   const float *part_acc, *part_ml;
@@ -112,17 +154,30 @@ struct CommitLaunch {
 };
 
 // ---------------------------------------------------------------- host entry points
-// Each returns the result of hipGetLastError() after enqueueing.
-hipError_t launch_gdn_tree(const GdnLaunch &a, int dk, int bf16, hipStream_t s);
-hipError_t launch_attn_split(const AttnLaunch &a, int D, int bf16, int n_blocks, hipStream_t s);
-hipError_t launch_attn_fold(const FoldLaunch &a, int D, int bf16, int n_blocks, hipStream_t s);
-hipError_t launch_commit(const CommitLaunch &a, int dk, int bf16, int n_blocks, hipStream_t s);
+// Each returns the result of hipGetLastError() after enqueueing.  With ev0 / ev1
+// set, the dispatch itself records its start and end time into them (the
+// launch goes through hipExtLaunchKernel), so an event pair times the kernel
+// alone, not the queueing around it.
+struct KernelEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+hipError_t launch_gdn_tree(const GdnLaunch &a, int dk, int bf16, hipStream_t s, KernelEvents ev);
+hipError_t launch_attn_split(const AttnLaunch &a, int D, int bf16, int n_blocks, hipStream_t s,
+                             KernelEvents ev);
+hipError_t launch_attn_fold(const FoldLaunch &a, int D, int bf16, int n_blocks, hipStream_t s,
+                            KernelEvents ev);
+// Split pass with `waves` waves of `nb` 16-row blocks each: (8, 1) or (4, 3).
+hipError_t launch_kv_split(const KvLaunch &a, int D, int waves, int nb, int n_blocks, hipStream_t s,
+                           KernelEvents ev);
+hipError_t launch_kv_tree(const KvLaunch &a, int D, int n_blocks, hipStream_t s, KernelEvents ev);
+hipError_t launch_commit(const CommitLaunch &a, int dk, int bf16, int n_blocks, hipStream_t s,
+                         KernelEvents ev);
 
 // Dynamic LDS bytes each kernel asks for (the host checks them against the device).
 size_t gdn_lds_bytes(int dk, int n_max);
 size_t attn_lds_bytes(int D, int bf16, int n_max);
-// Work decomposition of the attention split pass for a storage dtype: rows per
-// shared item and nodes per tail item.
+// Work decomposition of the float32 attention split pass: rows per shared item
+// and nodes per tail item.
 int attn_rows_per_item(int bf16);
 int attn_nodes_per_tail(int bf16);
 size_t commit_lds_bytes(int D, int bf16, int m);

@@ -62,8 +62,8 @@ typedef enum { HDT_F32 = 0, HDT_BF16 = 1 } hdt_dtype;
  *    h reads q/k head h / (gdn_hv / gdn_hk)); gdn_dk = gdn_dv in {64, 128}
  *    (state heads of 128 by 128 in the pages); gdn_dv % 16 == 0.
  *  Attention: attn_hq query heads, attn_hkv kv heads (q head j reads kv head
- *    j / (attn_hq / attn_hkv), at most 16 q heads per kv head), head dim attn_d
- *    in {64, 256}.
+ *    j / (attn_hq / attn_hkv), at most 16 q heads per kv head, and with bf16
+ *    storage at most 6 at attn_d = 256), head dim attn_d in {64, 256}.
  *  io_dtype: storage of q, k, v, gates, outputs and the K/V cache (HDT_BF16,
  *    or HDT_F32 with attn_d = 64).  The GDN state is always float32.
  *  gdn_scale: readout scale s in o = S^T (s q); <= 0 selects 1/sqrt(gdn_dk).

@@ -69,6 +69,7 @@ def make_engine(**kw):
     (dict(attn_d=128), -7),
     (dict(attn_hq=5), -1),
     (dict(attn_hq=34, attn_hkv=2), -7),
+    (dict(attn_hq=14, attn_hkv=2, attn_d=256), -7),
     (dict(io_dtype=hdt.HDT_F32, attn_d=256), -7),
     (dict(io_dtype=7), -1),
     (dict(slots=[dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=10, length=11)]), -1),
@@ -131,14 +132,27 @@ def test_sequencing_rules_without_pending_round():
 
 
 def test_split_size_depends_on_capacity_only():
+    # bf16 storage: the smallest multiple of 32 keys (at least 128) for which a full
+    # cache gives at most 256 (kv head, split) items; float32: a power of two.
     e = make_engine()
-    assert e.split_size(0) == 256 and e.split_size(1) == 256
+    assert e.split_size(0) == 128 and e.split_size(1) == 128
     big = [dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=65536 + 1024, length=65536),
            dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=262144 + 1024, length=0)]
     e2 = make_engine(attn_hkv=4, attn_hq=24, attn_d=256, slots=big)
-    assert e2.split_size(0) == 1024 and e2.split_size(1) == 4096
+    assert e2.split_size(0) == 1056 and e2.split_size(1) == 4128
     e2.reset(0, 5)
-    assert e2.split_size(0) == 1024
+    assert e2.split_size(0) == 1056
+    for cap in (1, 127, 4096, 65536 + 600, 131072, 262144 + 999, 1 << 20):
+        for hkv in (1, 2, 4, 8):
+            slot = [dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=cap, length=0)]
+            s = make_engine(attn_hkv=hkv, attn_hq=hkv * 2, slots=slot).split_size(0)
+            assert s % 32 == 0 and s >= 128
+            assert hkv * -(-cap // s) <= 256 or s == 128
+            assert s == 128 or hkv * -(-cap // (s - 32)) > 256
+    f32 = make_engine(io_dtype=hdt.HDT_F32, slots=big[:1])
+    assert f32.split_size(0) == 512
+    f32b = make_engine(io_dtype=hdt.HDT_F32, attn_hkv=4, attn_hq=8, slots=big)
+    assert f32b.split_size(0) == 1024 and f32b.split_size(1) == 4096
 
 
 def test_one_hip_runtime_in_process():
