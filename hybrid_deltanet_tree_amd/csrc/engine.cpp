@@ -127,6 +127,20 @@ bool plan_tree(int32_t n, const int32_t *parent, int8_t *par, int8_t *dep, int32
   return true;
 }
 
+// States the GDN walk keeps in LDS: node p's, when a later child c of p does not
+// directly follow p (parent[c] != c - 1), so the walk restores S_p from LDS
+// instead of replaying p's root path.  Slots go to the first kGdnSaves such nodes;
+// returns how many were used.
+int plan_saves(int n, const int8_t *par, int8_t *save) {
+  std::memset(save, -1, kMaxNodes);
+  int used = 0;
+  for (int c = 1; c < n; ++c) {
+    const int p = par[c];
+    if (p != c - 1 && save[p] < 0 && used < kGdnSaves) save[p] = static_cast<int8_t>(used++);
+  }
+  return used;
+}
+
 hdt_status check_hip(hdt_engine *e, hipError_t r, const char *what) {
   if (r != hipSuccess) return fail(e, HDT_E_HIP, "%s: %s", what, hipGetErrorString(r));
   return HDT_OK;
@@ -324,6 +338,7 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
         g.wg_begin = wg;
         std::memcpy(g.parent, par[t], kMaxNodes);
         std::memcpy(g.depth, dep[t], kMaxNodes);
+        a.n_saves = std::max(a.n_saves, plan_saves(tr.n_nodes, par[t], g.save));
         wg += m.gdn_hv * (m.gdn_dv / kGdnCols);
       }
       ProfScope p(e, 0);
@@ -567,7 +582,7 @@ hdt_status hdt_forward_tree(hdt_engine *e, int32_t n_trees, const hdt_tree *tree
   {
     int32_t n_max = 0;
     for (int t = 0; t < n_trees; ++t) n_max = std::max(n_max, trees[t].n_nodes);
-    const size_t need_g = e->n_gdn > 0 ? gdn_lds_bytes(m.gdn_dk, n_max) : 0;
+    const size_t need_g = e->n_gdn > 0 ? gdn_lds_bytes(m.gdn_dk, n_max, kGdnSaves) : 0;
     const size_t need_a = e->n_attn > 0 ? attn_lds_bytes(m.attn_d, m.io_dtype == HDT_BF16, n_max) : 0;
     if (need_g > static_cast<size_t>(e->max_lds) || need_a > static_cast<size_t>(e->max_lds))
       return fail(e, HDT_E_UNSUPPORTED, "kernels need %zu / %zu bytes of LDS; the device allows %d",

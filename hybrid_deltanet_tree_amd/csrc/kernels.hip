@@ -44,29 +44,14 @@ __device__ __forceinline__ float rowsum16(float x) {
   return x;
 }
 
-// Three independent rowsum16 reductions, interleaved stage by stage.
-__device__ __forceinline__ void rowsum16x3(float &a, float &b, float &c) {
-  a = a + dpp<0xB1>(a);
-  b = b + dpp<0xB1>(b);
-  c = c + dpp<0xB1>(c);
-  a = a + dpp<0x4E>(a);
-  b = b + dpp<0x4E>(b);
-  c = c + dpp<0x4E>(c);
-  a = a + dpp<0x141>(a);
-  b = b + dpp<0x141>(b);
-  c = c + dpp<0x141>(c);
-  a = a + dpp<0x140>(a);
-  b = b + dpp<0x140>(b);
-  c = c + dpp<0x140>(c);
-}
-
 // ============================================================================ GDN
 
-// LDS layout of the GDN walk (floats, then bytes): k[n][dk], s*q[n][dk],
-// v[n][16], alpha[n], beta[n], u[n][16], o[n][16], depth[n] and parent[n] (int),
-// anc[n][64] (int8).
+// LDS layout of the GDN walk: k[n][dk] and s*q[n][dk] (float); per node
+// {alpha, beta, k . s q, parent} (float4); v[n][16], u[n][16], o[n][16] (float);
+// depth[n] and parent[n] (int); then the kept states [n_saves][16][dk] (float);
+// then anc[n][64] and save[n] (int8).
 __host__ __device__ constexpr size_t gdn_lds_floats(int dk, int n) {
-  return static_cast<size_t>(n) * (2 * dk + 3 * kGdnCols + 4);
+  return static_cast<size_t>(n) * (2 * dk + 4 + 3 * kGdnCols) + ((2 * n + 3) & ~3);
 }
 
 // Sum of x[a] * y[a] over a lane's R elements in a fixed pairwise order.
@@ -111,6 +96,27 @@ __device__ __forceinline__ void unpack16(const uint4 &c, float *out) {
   }
 }
 
+// Two interleaved rowsum16 reductions.
+__device__ __forceinline__ void rowsum16x2(float &a, float &b) {
+  a = a + dpp<0xB1>(a);
+  b = b + dpp<0xB1>(b);
+  a = a + dpp<0x4E>(a);
+  b = b + dpp<0x4E>(b);
+  a = a + dpp<0x141>(a);
+  b = b + dpp<0x141>(b);
+  a = a + dpp<0x140>(a);
+  b = b + dpp<0x140>(b);
+}
+
+// One node's operands, in the registers of a lane: its key rows and s*q rows,
+// {alpha, beta, k . s q, parent} and the value of the lane's column.
+template <int R>
+struct GdnNode {
+  float k[R], q[R];
+  float4 sc;
+  float v;
+};
+
 template <bool BF, int DK>
 __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P) {
   constexpr int R = DK / 16;                 // key rows per lane; 16 lanes hold one value column
@@ -128,13 +134,14 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
   const int nm = P.n_max;
   float *kf = g_lds;
   float *qs = kf + nm * DK;
-  float *vl = qs + nm * DK;
-  float *al = vl + nm * kGdnCols;
-  float *be = al + nm;
-  float *ul = be + nm;
+  float4 *nsc = reinterpret_cast<float4 *>(qs + nm * DK);
+  float *vl = reinterpret_cast<float *>(nsc + nm);
+  float *ul = vl + nm * kGdnCols;
   float *ol = ul + nm * kGdnCols;
   int *dep = reinterpret_cast<int *>(ol + nm * kGdnCols);  // depth[n], then parent[n]
-  int8_t *anc = reinterpret_cast<int8_t *>(dep + 2 * nm);
+  float *kept = reinterpret_cast<float *>(dep + ((2 * nm + 3) & ~3));  // 16-byte aligned
+  int8_t *anc = reinterpret_cast<int8_t *>(kept + P.n_saves * kGdnCols * DK);
+  int8_t *savel = anc + nm * kMaxNodes;
 
   const int cgroups = P.dv / kGdnCols;
   const int local = bid - T.wg_begin;
@@ -146,10 +153,11 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
   const int col = cg * kGdnCols + lc;
 
   // ---- issue every load of the prologue before using any of them (tree first)
-  int par_i = -1, dep_i = 0;
+  int par_i = -1, dep_i = 0, save_i = -1;
   if (tid < n) {
     par_i = T.parent[tid];
     dep_i = T.depth[tid];
+    save_i = T.save[tid];
   }
   float base[R];
   lds_row<R>(T.state + (static_cast<int64_t>(h) * P.dv + col) * DK + g * R, base);
@@ -184,6 +192,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
   if (tid < n) {
     dep[tid] = dep_i;
     dep[nm + tid] = par_i;
+    savel[tid] = static_cast<int8_t>(save_i);
   }
   lds_barrier();
   if (tid < n) {
@@ -220,90 +229,115 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
     for (int e = 0; e < EPC; ++e) vl[i * kGdnCols + cc * EPC + e] = vv[e];
   }
   if (tid < n) {
+    float a, b;
     if constexpr (BF) {
-      al[tid] = __uint_as_float(static_cast<uint32_t>(araw) << 16);
-      be[tid] = __uint_as_float(static_cast<uint32_t>(braw) << 16);
+      a = __uint_as_float(static_cast<uint32_t>(araw) << 16);
+      b = __uint_as_float(static_cast<uint32_t>(braw) << 16);
     } else {
-      al[tid] = araw;
-      be[tid] = braw;
+      a = araw;
+      b = braw;
     }
+    nsc[tid] = make_float4(a, b, 0.0f, __int_as_float((par_i & 0xFF) | ((save_i & 0xFF) << 8)));
     if (cg == 0) static_cast<io_t<BF> *>(T.a_pend)[static_cast<int64_t>(tid) * P.hv + h] = araw;
+  }
+  __syncthreads();
+  // ---- k . s q of every node (it does not depend on the state), one 16-lane row
+  // per node with the walk's own dot product and reduction
+  for (int i0 = 0; i0 < n; i0 += kGdnThreads / 16) {
+    const int i = i0 + (tid >> 4);
+    const int ii = min(i, n - 1);
+    float kk[R], qq[R];
+    lds_row<R>(kf + ii * DK + g * R, kk);
+    lds_row<R>(qs + ii * DK + g * R, qq);
+    const float d = rowsum16(lane_dot<R>(kk, qq));
+    if (i < n && g == 0) nsc[i].z = d;
   }
   __syncthreads();
 
   // ---- walk the nodes in index order (parents first).  Per node, from the
   // parent's state P:  A = alpha P;  r = k^T A;  u = beta (v - r);  S = A + k u^T;
   // o = S^T (s q) taken as A^T (s q) + u (k . s q), so the readout does not wait
-  // for the state write.  Every dot product is a lane_dot then a rowsum16.
+  // for the state write.  Every dot product is a lane_dot then a rowsum16.  The
+  // loop is unrolled twice so the next node's operands load into the other set.
   float cur[R];
 #pragma unroll
   for (int a = 0; a < R; ++a) cur[a] = base[a];
   int cur_node = -1;
-  float kn[R], qn[R];
-  lds_row<R>(kf + g * R, kn);
-  lds_row<R>(qs + g * R, qn);
-  float an = al[0], bn = be[0], vn = vl[lc];
-  int pn = dep[nm + 0];
-  for (int i = 0; i < n; ++i) {
-    float ki[R], qi[R];
-#pragma unroll
-    for (int a = 0; a < R; ++a) {
-      ki[a] = kn[a];
-      qi[a] = qn[a];
-    }
-    const float ai = an, bi = bn, vi = vn;
-    const int p = pn;
-    if (i + 1 < n) {  // next node's operands, in flight during this step
-      lds_row<R>(kf + (i + 1) * DK + g * R, kn);
-      lds_row<R>(qs + (i + 1) * DK + g * R, qn);
-      an = al[i + 1];
-      bn = be[i + 1];
-      vn = vl[(i + 1) * kGdnCols + lc];
-      pn = dep[nm + i + 1];
-    }
-    if (p != cur_node) {
-      // Restore the parent's state: replay its root path's rank-1 steps from
-      // the committed state with the same write as the step below.
-#pragma unroll
-      for (int a = 0; a < R; ++a) cur[a] = base[a];
-      if (p >= 0) {
-        const int dp = dep[p];
-        const int8_t *path = anc + p * kMaxNodes;
-        int j = path[0];
-        float kj[R];
-        lds_row<R>(kf + j * DK + g * R, kj);
-        float aj = al[j], uj = ul[j * kGdnCols + lc];
-        for (int d = 0; d <= dp; ++d) {
-          float kk[R];
-#pragma unroll
-          for (int a = 0; a < R; ++a) kk[a] = kj[a];
-          const float ak = aj, uk = uj;
-          if (d < dp) {
-            j = path[d + 1];
-            lds_row<R>(kf + j * DK + g * R, kj);
-            aj = al[j];
-            uj = ul[j * kGdnCols + lc];
-          }
-#pragma unroll
-          for (int a = 0; a < R; ++a) cur[a] = fmaf(kk[a], uk, ak * cur[a]);
-        }
+  auto load_node = [&](int i, GdnNode<R> &x) {
+    lds_row<R>(kf + i * DK + g * R, x.k);
+    lds_row<R>(qs + i * DK + g * R, x.q);
+    x.sc = nsc[i];
+    x.v = vl[i * kGdnCols + lc];
+  };
+  auto restore = [&](int p) {
+    // the parent's state: kept in LDS, or replayed from the committed state along
+    // its root path with the same rank-1 write as the step below
+    if (p >= 0) {
+      const int sl = __builtin_amdgcn_readfirstlane(static_cast<int>(savel[p]));
+      if (sl >= 0) {
+        lds_row<R>(kept + (sl * kGdnCols + lc) * DK + g * R, cur);
+        return;
       }
     }
+#pragma unroll
+    for (int a = 0; a < R; ++a) cur[a] = base[a];
+    if (p < 0) return;
+    const int dp = dep[p];
+    const int8_t *path = anc + p * kMaxNodes;
+    int j = path[0];
+    float kj[R];
+    lds_row<R>(kf + j * DK + g * R, kj);
+    float aj = nsc[j].x, uj = ul[j * kGdnCols + lc];
+    for (int d = 0; d <= dp; ++d) {
+      float kk[R];
+#pragma unroll
+      for (int a = 0; a < R; ++a) kk[a] = kj[a];
+      const float ak = aj, uk = uj;
+      if (d < dp) {
+        j = path[d + 1];
+        lds_row<R>(kf + j * DK + g * R, kj);
+        aj = nsc[j].x;
+        uj = ul[j * kGdnCols + lc];
+      }
+#pragma unroll
+      for (int a = 0; a < R; ++a) cur[a] = fmaf(kk[a], uk, ak * cur[a]);
+    }
+  };
+  auto step = [&](int i, const GdnNode<R> &x) {
+    const int w = __builtin_amdgcn_readfirstlane(__float_as_int(x.sc.w));
+    const int p = static_cast<int8_t>(w & 0xFF), keep = static_cast<int8_t>((w >> 8) & 0xFF);
+    if (p != cur_node) restore(p);
     float A[R];
 #pragma unroll
-    for (int a = 0; a < R; ++a) A[a] = ai * cur[a];
-    float r = lane_dot<R>(A, ki);
-    float oa = lane_dot<R>(A, qi);
-    float kq = lane_dot<R>(ki, qi);
-    rowsum16x3(r, oa, kq);
-    const float u = bi * (vi - r);
+    for (int a = 0; a < R; ++a) A[a] = x.sc.x * cur[a];
+    float r = lane_dot<R>(A, x.k);
+    float oa = lane_dot<R>(A, x.q);
+    rowsum16x2(r, oa);
+    const float u = x.sc.y * (x.v - r);
 #pragma unroll
-    for (int a = 0; a < R; ++a) cur[a] = fmaf(ki[a], u, A[a]);
-    if (g == 0) {
-      ul[i * kGdnCols + lc] = u;
-      ol[i * kGdnCols + lc] = fmaf(u, kq, oa);
+    for (int a = 0; a < R; ++a) cur[a] = fmaf(x.k[a], u, A[a]);
+    // every lane of the column stores the same bits (no branch)
+    ul[i * kGdnCols + lc] = u;
+    ol[i * kGdnCols + lc] = fmaf(u, x.sc.z, oa);
+    if (keep >= 0) {
+#pragma unroll
+      for (int a = 0; a < R; a += 4)
+        *reinterpret_cast<float4 *>(kept + (keep * kGdnCols + lc) * DK + g * R + a) =
+            make_float4(cur[a], cur[a + 1], cur[a + 2], cur[a + 3]);
     }
     cur_node = i;
+  };
+  // (the scheduling barriers keep the next node's loads ahead of this node's work)
+  GdnNode<R> na, nb;
+  load_node(0, na);
+  for (int i = 0; i < n; i += 2) {
+    if (i + 1 < n) load_node(i + 1, nb);
+    __builtin_amdgcn_sched_barrier(0);
+    step(i, na);
+    if (i + 1 >= n) break;
+    if (i + 2 < n) load_node(i + 2, na);
+    __builtin_amdgcn_sched_barrier(0);
+    step(i + 1, nb);
   }
   __syncthreads();
   for (int e = tid; e < n * kGdnCols; e += kGdnThreads) {
@@ -1007,8 +1041,9 @@ hipError_t set_lds(K kernel, size_t bytes) {
 
 }  // namespace
 
-size_t gdn_lds_bytes(int dk, int n_max) {
-  return gdn_lds_floats(dk, n_max) * sizeof(float) + static_cast<size_t>(n_max) * kMaxNodes;
+size_t gdn_lds_bytes(int dk, int n_max, int n_saves) {
+  return (gdn_lds_floats(dk, n_max) + static_cast<size_t>(n_saves) * kGdnCols * dk) * sizeof(float) +
+         static_cast<size_t>(n_max) * (kMaxNodes + 1);
 }
 
 size_t attn_lds_bytes(int D, int bf16, int n_max) {
@@ -1026,7 +1061,7 @@ size_t commit_lds_bytes(int D, int bf16, int m) {
 
 hipError_t launch_gdn_tree(const GdnLaunch &a, int dk, int bf16, hipStream_t s, KernelEvents ev) {
   const int blocks = a.t[a.n_trees - 1].wg_begin + a.hv * (a.dv / kGdnCols);
-  const size_t lds = gdn_lds_bytes(dk, a.n_max);
+  const size_t lds = gdn_lds_bytes(dk, a.n_max, a.n_saves);
 #define HDT_GDN(BF, DK)                                                                   \
   do {                                                                                    \
     (void)set_lds(gdn_tree_kernel<BF, DK>, lds);                                                \

@@ -400,40 +400,56 @@ __global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
 
 // ============================================================================ tree pass
 
-struct Fold2 {
-  float m, l, x0, x1;
+// Running softmax state of one row over 8 output columns: max (base 2), sum, and
+// the weighted column sums relative to that max.
+struct Fold8 {
+  float m, l;
+  float x[8];
 };
 
-__device__ __forceinline__ Fold2 fold_empty() { return Fold2{-INFINITY, 0.0f, 0.0f, 0.0f}; }
-
-// Add a normalised partial (max ms, sum ls, columns o0, o1).
-__device__ __forceinline__ void fold_norm(Fold2 &f, float ms, float ls, float o0, float o1) {
-  const float mn = fmaxf(f.m, ms);
-  const float a = exp2_fast(f.m - mn), b = exp2_fast(ms - mn);
-  const float w = ls * b;
-  f.l = f.l * a + w;
-  f.x0 = f.x0 * a + o0 * w;
-  f.x1 = f.x1 * a + o1 * w;
-  f.m = mn;
+__device__ __forceinline__ void fold8_empty(Fold8 &f) {
+  f.m = -INFINITY;
+  f.l = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.x[e] = 0.0f;
 }
 
-// Add an unnormalised state (a folded group, or a row's last split).
-__device__ __forceinline__ void fold_acc(Fold2 &f, const Fold2 &y) {
+// f <- f (+) y for states relative to their own maxima.  Symmetric in f and y bit
+// for bit (products and sums of the same two terms), so lanes that swap operands
+// agree.  Neither may be empty.
+__device__ __forceinline__ void fold8_merge(Fold8 &f, const Fold8 &y) {
   const float mn = fmaxf(f.m, y.m);
   const float a = exp2_fast(f.m - mn), b = exp2_fast(y.m - mn);
   f.l = f.l * a + y.l * b;
-  f.x0 = f.x0 * a + y.x0 * b;
-  f.x1 = f.x1 * a + y.x1 * b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.x[e] = f.x[e] * a + y.x[e] * b;
   f.m = mn;
 }
 
-constexpr int kFoldChunk = 64;          // split partials in flight per fold thread
-constexpr int kFoldThreadsKv = kKvThreads - 64;
+// The same state as held by the lane 16 (SWAP16) or 32 lanes away.
+template <bool SWAP16>
+__device__ __forceinline__ Fold8 fold8_partner(const Fold8 &f) {
+  Fold8 y;
+  auto pick = [](float v) {
+    const auto r = SWAP16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false)
+                          : __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    // r[0] and r[1] are this lane's value and the partner's, in lane order
+    const bool upper = SWAP16 ? ((threadIdx.x >> 4) & 1) : ((threadIdx.x >> 5) & 1);
+    return __uint_as_float(upper ? r[0] : r[1]);
+  };
+  y.m = pick(f.m);
+  y.l = pick(f.l);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y.x[e] = pick(f.x[e]);
+  return y;
+}
+
+constexpr int kFoldChunk = 16;  // split partials in flight per fold lane
 
 template <int D>
 __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
   using C = KvCfg<D>;
-  constexpr int QD = C::QD, QDB = C::QDB, HP = QD / 2;
+  constexpr int QD = C::QD, QDB = C::QDB, QO = QD / 8;  // 8-column groups per quarter
   constexpr int MAX_TILES = 3;  // (kKvTile - 1 + kMaxNodes - 1) / kKvTile + 1
   static_assert((kKvTile - 1 + kMaxNodes - 1) / kKvTile + 1 <= MAX_TILES, "tree tiles");
   __shared__ __align__(1024) unsigned char tiles[MAX_TILES][C::TILE];
@@ -450,7 +466,10 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
   const int node = rest % T.n, h = rest / T.n;
   const int G = P.hq / P.hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, ln = lane & 15;
-  const int dep = T.depth[node];
+  // depth by a scalar load of the 32-bit word that holds it (the tree arrays are
+  // bytes; a byte load from the argument block would be a vector load)
+  const int dep = static_cast<int8_t>(
+      (reinterpret_cast<const uint32_t *>(T.depth)[node >> 2] >> (8 * (node & 3))) & 0xFFu);
   const int64_t L = T.L, pos = L + dep;
   const int64_t tb0 = (L / kKvTile) * kKvTile;
   const int ntree = static_cast<int>((pos / kKvTile) * kKvTile - tb0) / kKvTile + 1;
@@ -461,71 +480,75 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
   const unsigned char *vc = static_cast<const unsigned char *>(T.vc) + static_cast<int64_t>(h) * T.cap * C::ROWB;
 
   if (wave == 0) {
-    // ---- ancestors: lane d holds the node's ancestor at depth d (the node itself
-    // past its depth, the filler of masked slots)
-    const int par_v = lane < T.n ? T.parent[lane] : -1;
+    // ---- ancestors first (scalar walk over the parent array held in a VGPR):
+    // lane d holds the node's ancestor at depth d
+    const int pl = min(lane, T.n - 1);
+    const uint32_t par_w = reinterpret_cast<const uint32_t *>(T.parent)[pl >> 2];
+    const int par_v = static_cast<int8_t>((par_w >> (8 * (pl & 3))) & 0xFFu);
     int anc_v = node;
     {
       int x = node;
       for (int d = dep; d >= 0; --d) {
-        if (lane == d) anc_v = x;
-        if (d > 0) x = __builtin_amdgcn_readlane(par_v, x);
+        anc_v = lane == d ? x : anc_v;
+        x = __builtin_amdgcn_readlane(par_v, max(x, 0));
       }
     }
-    // ---- gather the node's tiles into LDS: committed rows below L, then the
-    // ancestors' tree rows, then the filler.  A wave-wide load covers kKvTile-row
-    // slices of RPL rows; the row's source is uniform over its CPR lanes.
+    // ---- the queries and the carried state of split n_full, in flight with the
+    // gather below (lanes past the node's q heads read a real row and are
+    // discarded; without a carry the loads read the buffer and are dropped)
+    KvRows<D, 1, QDB> st;
+    const int jr = min(ln, G - 1);
+    {
+      const unsigned char *qrow =
+          static_cast<const unsigned char *>(T.q) + (static_cast<int64_t>(node) * P.hq + h * G + jr) * C::ROWB;
+#pragma unroll
+      for (int kk = 0; kk < C::KQ; ++kk) st.q[0][kk] = *reinterpret_cast<const bf16x8 *>(qrow + (32 * kk + 8 * g) * 2);
+    }
+    const int64_t crow = static_cast<int64_t>(h) * T.rows_cap + node * G + jr;
+    const float2 cml = *reinterpret_cast<const float2 *>(T.carry_ml + crow * 2);
+    floatx4 cacc[QDB];
+#pragma unroll
+    for (int j = 0; j < QDB; ++j)
+      cacc[j] = *reinterpret_cast<const floatx4 *>(T.carry_acc + crow * D + 16 * (qd * QDB + j) + 4 * g);
+    // ---- gather the node's tiles into LDS: committed rows below L, the
+    // ancestors' tree rows, then the node's own row as the filler of masked slots.
+    // Rows are counted from tb0 in 32-bit; lane d of trow_v holds the byte offset of
+    // the tree row at depth d.  A wave-wide load covers RPL rows, whose depths are
+    // uniform, so their tree rows come from readlane.
+    const int lres = static_cast<int>(L - tb0);  // committed rows in the first tile
+    const int trow_v = ((lane <= dep ? anc_v : node) * P.hkv + h) * C::ROWB;
+    const unsigned char *kres0 = kc + tb0 * C::ROWB;
+    const unsigned char *vres0 = vc + tb0 * C::ROWB;
+    const int rr = lane / C::CPR, cs = lane % C::CPR;
     for (int tt = 0; tt < ntree; ++tt) {
-      const int64_t tb = tb0 + static_cast<int64_t>(kKvTile) * tt;
 #pragma unroll
       for (int li = 0; li < C::LOADS / 2; ++li) {
-        const int row = li * C::RPL + lane / C::CPR;
-        const int cs = lane % C::CPR;
-        const int64_t p = tb + row;
-        // the tree row of position p >= L: ancestor at depth p - L, or the node
-        int x = node;
+        const int row = li * C::RPL + rr;  // row within the tile
+        const int rbase = kKvTile * tt + li * C::RPL;
+        int toff = 0;
 #pragma unroll
-        for (int rr = 0; rr < C::RPL; ++rr) {
-          const int64_t pr = tb + li * C::RPL + rr;  // uniform
-          if (pr >= L && pr <= pos) {
-            const int a = __builtin_amdgcn_readlane(anc_v, static_cast<int>(pr - L));
-            if (lane / C::CPR == rr) x = a;
-          }
+        for (int q = 0; q < C::RPL; ++q) {
+          const int dq = min(max(rbase + q - lres, 0), 63);  // uniform
+          const int tq = __builtin_amdgcn_readlane(trow_v, dq);
+          toff = rr == q ? tq : toff;
         }
-        const int64_t off_c = static_cast<int64_t>((cs ^ swz<D>(row)) << 4);
-        const unsigned char *ksrc, *vsrc;
-        if (p < L) {
-          ksrc = kc + p * C::ROWB + off_c;
-          vsrc = vc + p * C::ROWB + off_c;
-        } else {
-          ksrc = kt + (static_cast<int64_t>(x) * P.hkv + h) * C::ROWB + off_c;
-          vsrc = vt + (static_cast<int64_t>(x) * P.hkv + h) * C::ROWB + off_c;
-        }
+        const int rel = rbase + rr;
+        const int off_c = (cs ^ swz<D>(row)) << 4;
+        const bool res = rel < lres;
+        const unsigned char *ksrc = (res ? kres0 + rel * C::ROWB : kt + toff) + off_c;
+        const unsigned char *vsrc = (res ? vres0 + rel * C::ROWB : vt + toff) + off_c;
         __builtin_amdgcn_global_load_lds(
             ksrc, (__attribute__((address_space(3))) void *)(tiles[tt] + li * 1024), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(
             vsrc, (__attribute__((address_space(3))) void *)(tiles[tt] + C::HALF + li * 1024), 16, 0, 0);
       }
     }
-    // ---- queries and the carried state of split n_full (lanes past the node's q
-    // heads read a real row and are discarded)
-    KvRows<D, 1, QDB> st;
     st.reset();
-    {
-      const int jr = min(ln, G - 1);
-      const unsigned char *qrow =
-          static_cast<const unsigned char *>(T.q) + (static_cast<int64_t>(node) * P.hq + h * G + jr) * C::ROWB;
+    if (T.carry_tiles > 0) {
+      st.m[0] = cml.x;
+      st.l[0] = cml.y;
 #pragma unroll
-      for (int kk = 0; kk < C::KQ; ++kk) st.q[0][kk] = *reinterpret_cast<const bf16x8 *>(qrow + (32 * kk + 8 * g) * 2);
-      if (T.carry_tiles > 0) {
-        const int64_t crow = static_cast<int64_t>(h) * T.rows_cap + node * G + jr;
-        const float2 ml = *reinterpret_cast<const float2 *>(T.carry_ml + crow * 2);
-        st.m[0] = ml.x;
-        st.l[0] = ml.y;
-#pragma unroll
-        for (int j = 0; j < QDB; ++j)
-          st.acc[0][j] = *reinterpret_cast<const floatx4 *>(T.carry_acc + crow * D + 16 * (qd * QDB + j) + 4 * g);
-      }
+      for (int j = 0; j < QDB; ++j) st.acc[0][j] = cacc[j];
     }
     wait_vm<0>();  // the gathered tiles are in LDS
     for (int tt = 0; tt < ntree; ++tt) {
@@ -574,79 +597,138 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
       *reinterpret_cast<uint4 *>(dst) = x;
     }
   }
-  // Each fold thread takes (row, column pair) items in turn.  The row's splits
-  // before its last (the committed ones, then split n_full if the node's rows
-  // cross into the next split) fold in chunks of kFoldChunk by split index: the
-  // chunk's max first, then its weighted sums in ascending split order; chunks
-  // merge in order.  The chunks before the last fold while wave 0 runs the tree
-  // tiles; the last chunk's loads wait in registers for the split finished there.
-  const int fid = tid - 64;
-  const int items = G * HP;
-  const int n_nl = T.n_full + (crossing ? 1 : 0);       // splits before the row's last
-  const int c_last = n_nl > 0 ? (n_nl - 1) / kFoldChunk * kFoldChunk : 0;
-  const int ns_last = n_nl - c_last;                    // splits in the last chunk
-  const int nm_last = min(ns_last, T.n_full - c_last);  // of which in memory
-  const bool fold_thread = wave > 0 && fid < items;     // one item per thread (items <= 192)
-  Fold2 tot = fold_empty();
+  // The row's splits before its last (the committed ones, then split n_full if the
+  // node's rows cross into the next split: n_nl in all) fold in four ranges of
+  // consecutive splits, one per 16-lane row of a fold wave; lane (sq, it) of fold
+  // wave w takes item (w - 1) * 16 + it = (q head, 8-column group) and range sq.
+  // A range folds in chunks of kFoldChunk (the chunk's max, then weighted sums in
+  // ascending split order; chunks merge in order).  The ranges then merge as
+  // (0 (+) 1) (+) (2 (+) 3), then the last split's float32 state.
+  const int n_nl = T.n_full + (crossing ? 1 : 0);
+  const int per = (n_nl + 3) / 4;
+  const int sq = lane >> 4, it = (wave - 1) * 16 + (lane & 15);
+  const int items = G * QO;
+  const bool fold_lane = wave > 0 && it < items;
+  const int r = min(it / QO, G - 1), co = it % QO;
+  const int R = node * G + r;
+  const int col = qd * QD + 8 * co;
+  const int s_lo = min(sq * per, n_nl), s_hi = min(s_lo + per, n_nl);
+  Fold8 acc8;
+  fold8_empty(acc8);
   float2 mlv[kFoldChunk];
-  uint32_t ov[kFoldChunk];
-  int R = 0, col = 0, flane = 0;
-  int64_t ml0 = 0;
+  uint2 ov0[kFoldChunk], ov1[kFoldChunk];
   auto load_chunk = [&](int c0, int nm) {  // loads past the memory splits repeat the last one
 #pragma unroll
     for (int j = 0; j < kFoldChunk; ++j) {
       const int sj = c0 + max(0, min(j, nm - 1));
-      mlv[j] = *reinterpret_cast<const float2 *>(T.part_ml + (ml0 + static_cast<int64_t>(sj) * T.rows_cap) * 2);
-      ov[j] = *reinterpret_cast<const uint32_t *>(static_cast<const unsigned char *>(T.part_o) +
-                                                  part_off<D>(T, h, sj, R >> 4, col >> 4, flane) + (col & 3) * 2);
+      const int64_t prow = (static_cast<int64_t>(h) * T.nsplit_cap + sj) * T.rows_cap + R;
+      mlv[j] = *reinterpret_cast<const float2 *>(T.part_ml + prow * 2);
+      const unsigned char *po = static_cast<const unsigned char *>(T.part_o);
+      ov0[j] = *reinterpret_cast<const uint2 *>(po + part_off<D>(T, h, sj, R >> 4, col >> 4, ((col & 15) >> 2) * 16 + (R & 15)));
+      ov1[j] = *reinterpret_cast<const uint2 *>(po + part_off<D>(T, h, sj, R >> 4, col >> 4, (((col & 15) >> 2) + 1) * 16 + (R & 15)));
     }
   };
-  auto fold_chunk = [&](int ns, int jx, float xm, float xl, float xo0, float xo1) {
+  // fold splits [c0, c0 + ns) of the loaded chunk; index jx (if >= 0) is the
+  // crossing partial, taken from LDS
+  auto fold_chunk = [&](int ns, int jx) {
     float mc = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kFoldChunk; ++j)
-      if (j < ns) mc = fmaxf(mc, j == jx ? xm : mlv[j].x);
-    Fold2 ch{mc, 0.0f, 0.0f, 0.0f};
+      if (j < ns) mc = fmaxf(mc, j == jx ? x_ml[r][0] : mlv[j].x);
+    Fold8 ch;
+    fold8_empty(ch);
+    ch.m = mc;
 #pragma unroll
     for (int j = 0; j < kFoldChunk; ++j) {
       if (j < ns) {
         const bool x = j == jx;
-        const float w = (x ? xl : mlv[j].y) * exp2_fast((x ? xm : mlv[j].x) - mc);
+        const float w = (x ? x_ml[r][1] : mlv[j].y) * exp2_fast((x ? x_ml[r][0] : mlv[j].x) - mc);
+        float o[8];
+        if (x) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = x_o[r][8 * co + e];
+        } else {
+          o[0] = half_lo(ov0[j].x);
+          o[1] = half_hi(ov0[j].x);
+          o[2] = half_lo(ov0[j].y);
+          o[3] = half_hi(ov0[j].y);
+          o[4] = half_lo(ov1[j].x);
+          o[5] = half_hi(ov1[j].x);
+          o[6] = half_lo(ov1[j].y);
+          o[7] = half_hi(ov1[j].y);
+        }
         ch.l = ch.l + w;
-        ch.x0 = ch.x0 + w * (x ? xo0 : half_lo(ov[j]));
-        ch.x1 = ch.x1 + w * (x ? xo1 : half_hi(ov[j]));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ch.x[e] = ch.x[e] + w * o[e];
       }
     }
-    fold_acc(tot, ch);
-  };
-  if (fold_thread) {
-    const int r = fid / HP, cp = fid % HP;
-    R = node * G + r;
-    col = qd * QD + 2 * cp;
-    flane = ((col & 15) >> 2) * 16 + (R & 15);
-    ml0 = static_cast<int64_t>(h) * T.nsplit_cap * T.rows_cap + R;
-    for (int c0 = 0; c0 < c_last; c0 += kFoldChunk) {
-      load_chunk(c0, kFoldChunk);
-      fold_chunk(kFoldChunk, -1, 0.f, 0.f, 0.f, 0.f);
+    if (acc8.m == -INFINITY && acc8.l == 0.0f) {
+      acc8 = ch;
+    } else {
+      fold8_merge(acc8, ch);
     }
-    if (nm_last > 0) load_chunk(c_last, nm_last);
+  };
+  // chunks of this range wholly in memory fold now; a chunk that holds the
+  // crossing partial waits for wave 0
+  int c_defer = -1, ns_defer = 0;
+  if (fold_lane) {
+    for (int c0 = s_lo; c0 < s_hi; c0 += kFoldChunk) {
+      const int ns = min(kFoldChunk, s_hi - c0);
+      const int nm = min(ns, T.n_full - c0);
+      load_chunk(c0, nm);
+      if (nm < ns) {  // holds split n_full, finished by wave 0
+        c_defer = c0;
+        ns_defer = ns;
+        break;
+      }
+      fold_chunk(ns, -1);
+    }
   }
   __syncthreads();
-  if (fold_thread) {
-    const int r = fid / HP, cp = fid % HP;
-    if (ns_last > 0) {
-      if (crossing) {
-        fold_chunk(ns_last, T.n_full - c_last, x_ml[r][0], x_ml[r][1], x_o[r][2 * cp], x_o[r][2 * cp + 1]);
-      } else {
-        fold_chunk(ns_last, -1, 0.f, 0.f, 0.f, 0.f);
+  if (wave > 0) {
+    if (fold_lane && c_defer >= 0) fold_chunk(ns_defer, T.n_full - c_defer);
+    // merge the four ranges: (0 (+) 1) (+) (2 (+) 3); empty ranges (more lanes
+    // than splits) contribute nothing
+    const bool has = s_lo < s_hi;
+    {
+      Fold8 y = fold8_partner<true>(acc8);
+      const bool yhas = __shfl_xor(static_cast<int>(has), 16) != 0;
+      if (has && yhas) {
+        if ((lane >> 4) & 1) { Fold8 lo = y; fold8_merge(lo, acc8); acc8 = lo; } else { fold8_merge(acc8, y); }
+      } else if (yhas) {
+        acc8 = y;
       }
     }
-    fold_acc(tot, Fold2{f_ml[r][0], f_ml[r][1], f_acc[r][2 * cp], f_acc[r][2 * cp + 1]});
-    const float inv = 1.0f / tot.l;
-    const uint32_t w = static_cast<uint32_t>(bf16_bits(tot.x0 * inv)) |
-                       (static_cast<uint32_t>(bf16_bits(tot.x1 * inv)) << 16);
-    *reinterpret_cast<uint32_t *>(static_cast<unsigned char *>(T.o) +
-                                  ((static_cast<int64_t>(node) * P.hq + h * G + r) * D + qd * QD + 2 * cp) * 2) = w;
+    const bool has2 = has || (__shfl_xor(static_cast<int>(has), 16) != 0);
+    {
+      Fold8 y = fold8_partner<false>(acc8);
+      const bool yhas = __shfl_xor(static_cast<int>(has2), 32) != 0;
+      if (has2 && yhas) {
+        if ((lane >> 5) & 1) { Fold8 lo = y; fold8_merge(lo, acc8); acc8 = lo; } else { fold8_merge(acc8, y); }
+      } else if (yhas) {
+        acc8 = y;
+      }
+    }
+    if (fold_lane && sq == 0) {
+      Fold8 last;
+      last.m = f_ml[r][0];
+      last.l = f_ml[r][1];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) last.x[e] = f_acc[r][8 * co + e];
+      if (n_nl > 0) {
+        fold8_merge(acc8, last);
+      } else {
+        acc8 = last;
+      }
+      const float inv = 1.0f / acc8.l;
+      uint4 w;
+      w.x = static_cast<uint32_t>(bf16_bits(acc8.x[0] * inv)) | (static_cast<uint32_t>(bf16_bits(acc8.x[1] * inv)) << 16);
+      w.y = static_cast<uint32_t>(bf16_bits(acc8.x[2] * inv)) | (static_cast<uint32_t>(bf16_bits(acc8.x[3] * inv)) << 16);
+      w.z = static_cast<uint32_t>(bf16_bits(acc8.x[4] * inv)) | (static_cast<uint32_t>(bf16_bits(acc8.x[5] * inv)) << 16);
+      w.w = static_cast<uint32_t>(bf16_bits(acc8.x[6] * inv)) | (static_cast<uint32_t>(bf16_bits(acc8.x[7] * inv)) << 16);
+      *reinterpret_cast<uint4 *>(static_cast<unsigned char *>(T.o) +
+                                 ((static_cast<int64_t>(node) * P.hq + h * G + r) * D + col) * 2) = w;
+    }
   }
 }
 

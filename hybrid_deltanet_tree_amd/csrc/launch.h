@@ -24,6 +24,7 @@ constexpr int kKvStages = 5;       // bf16 attention: LDS tile ring of the split
 constexpr int kKvQuarters = 4;     // bf16 attention: output columns split over this many blocks
 constexpr int kGdnThreads = 256;   // 4 waves x 4 value columns x 16 lanes per column
 constexpr int kGdnCols = 16;       // value columns per GDN workgroup
+constexpr int kGdnSaves = 8;       // GDN: states kept in LDS for later siblings (branch points)
 constexpr int kFoldThreads = 256;  // 4 waves per output row
 
 // ---------------------------------------------------------------- GDN tree walk
@@ -38,6 +39,7 @@ struct GdnTree {
   int32_t wg_begin;                      // first workgroup of this tree
   int8_t parent[kMaxNodes];
   int8_t depth[kMaxNodes];
+  int8_t save[kMaxNodes];                // LDS slot that keeps node i's state, or -1
 };
 
 struct GdnLaunch {
@@ -45,6 +47,7 @@ struct GdnLaunch {
   int32_t n_trees;
   int32_t hk, hv, dv;
   int32_t n_max;                         // largest n over the trees (sizes LDS)
+  int32_t n_saves;                       // largest number of kept states over the trees
   float scale;
 };
 
@@ -110,8 +113,8 @@ struct KvTree {
   int32_t row_groups;                     // split-pass items per split (row blocks / blocks per item)
   int32_t a_begin, a_per_head;            // split pass: first block, items per kv head
   int32_t b_begin;                        // tree pass: first block
-  int8_t parent[kMaxNodes];
-  int8_t depth[kMaxNodes];
+  alignas(4) int8_t parent[kMaxNodes];    // read as 32-bit words
+  alignas(4) int8_t depth[kMaxNodes];
 };
 
 struct KvLaunch {
@@ -174,7 +177,7 @@ hipError_t launch_commit(const CommitLaunch &a, int dk, int bf16, int n_blocks, 
                          KernelEvents ev);
 
 // Dynamic LDS bytes each kernel asks for (the host checks them against the device).
-size_t gdn_lds_bytes(int dk, int n_max);
+size_t gdn_lds_bytes(int dk, int n_max, int n_saves);
 size_t attn_lds_bytes(int D, int bf16, int n_max);
 // Work decomposition of the float32 attention split pass: rows per shared item
 // and nodes per tail item.
