@@ -1,7 +1,7 @@
 """Benchmark of the tree-verify hot path on one MI355X.
 
 A step is one pass of the whole path over one round: forward_tree through every
-layer of the stack (Gated DeltaNet tree walk, attention split pass and fold),
+layer of the stack (Gated DeltaNet tree walk, attention split pass and tree pass),
 then commit_tree of a seeded accepted path.  The default workload is the 64-layer
 3:1 stack (48 GDN + 16 attention layers) at 65,536 resident tokens with a
 16-node draft tree; inputs are seeded synthetic data resident in HBM before the
@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "64-layer tree-verify ms at 65k ctx, 16-node tree; achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
-SPLIT_KERNEL = "attn2_split_kernel"
+SPLIT_KERNEL = "kv_split_kernel"
 COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_split_stack65k_traffic.json")
 
@@ -95,9 +95,11 @@ def algorithmic_bytes(w, L, n):
             + 2 * 2 * n * w.attn_hkv * w.attn_d * 2 + n * w.attn_hq * w.attn_d * 2)
     gdn = (w.gdn_hv * w.gdn_dk * w.gdn_dv * 4 + 2 * n * w.gdn_hk * w.gdn_dk * 2
            + n * w.gdn_hv * w.gdn_dv * 2 + 2 * n * w.gdn_hv * 2 + n * w.gdn_hv * w.gdn_dv * 2)
-    # the split kernel's share of an attention layer: everything but the output rows,
-    # which the fold kernel writes
-    split = attn - n * w.attn_hq * w.attn_d * 2
+    # the split pass's share of an attention layer: the resident K/V rows below the
+    # last 32-key tile boundary under L, and the queries (the tree pass reads the rest
+    # and writes the tree rows and the outputs)
+    tb0 = (int(L) // 32) * 32
+    split = 2 * w.attn_hkv * tb0 * w.attn_d * 2 + n * w.attn_hq * w.attn_d * 2
     return attn, gdn, split
 
 
@@ -228,7 +230,7 @@ def main():
     verify_gbps = verify_bytes / (med * 1e-3) / 1e9
     kernels = {name: {"avg_us": round(1e3 * prof[k][0] / max(1, prof[k][1]), 2),
                       "launches_per_step": prof[k][1] // args.steps}
-               for k, name in ((0, "gdn_tree"), (1, "attn_split"), (2, "attn_fold"), (3, "commit"))}
+               for k, name in ((0, "gdn_tree"), (1, "attn_split"), (2, "attn_tree"), (3, "commit"))}
 
     traffic = None   # measured bytes are stale once the kernels change
     if args.workload == "stack_65k" and os.path.exists(TRAFFIC_FILE):
