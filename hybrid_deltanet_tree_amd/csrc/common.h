@@ -80,6 +80,49 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
                                            static_cast<int>(bytes), 0x00020000);
 }
 
+// Stores at device (agent) scope: written through this XCD's L2, so results that a
+// later kernel reads are not left dirty in L2 for the end-of-kernel write-back.
+__device__ __forceinline__ void st_agent(void *p, uint64_t v) {
+  __hip_atomic_store(static_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(void *p, uint2 v) {
+  st_agent(p, static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32));
+}
+__device__ __forceinline__ void st_agent(void *p, float2 v) {
+  st_agent(p, make_uint2(__float_as_uint(v.x), __float_as_uint(v.y)));
+}
+__device__ __forceinline__ void st_agent(void *p, floatx4 v) {
+  st_agent(p, make_uint2(__float_as_uint(v[0]), __float_as_uint(v[1])));
+  st_agent(static_cast<char *>(p) + 8, make_uint2(__float_as_uint(v[2]), __float_as_uint(v[3])));
+}
+
+// Brings the 64-byte lines of a uniform (kernel-argument) region into the scalar
+// cache with loads issued together and one wait, so that later reads of its fields
+// hit that cache instead of each paying a memory round trip in turn.  `bytes` is at
+// most 384; `tail` is one more uniform address (the launch's shared fields).
+__device__ __forceinline__ void scalar_touch(const void *base, int bytes, const void *tail) {
+  const unsigned char *b = static_cast<const unsigned char *>(base);
+  const int last = bytes - 4;
+  uint32_t x[6];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) x[i] = *reinterpret_cast<const uint32_t *>(b + min(64 * i, last));
+  const uint32_t y = *static_cast<const uint32_t *>(tail);
+  asm volatile("" ::"s"(x[0]), "s"(x[1]), "s"(x[2]), "s"(x[3]), "s"(x[4]), "s"(x[5]), "s"(y));
+}
+
+// LDS byte address of a pointer into shared memory, and back.
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8 *)(p)));
+}
+__device__ __forceinline__ const lds_u8 *lds_ptr(uint32_t a) {
+  return reinterpret_cast<const lds_u8 *>(static_cast<uintptr_t>(a));
+}
+__device__ __forceinline__ shortx4 ds_read_tr_at(uint32_t a) {
+  typedef __attribute__((address_space(3))) shortx4 *lds_v4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(lds_ptr(a)));
+}
+
 // Transposed LDS read (ds_read_b64_tr_b16).  In each group of 16 lanes, lane p
 // supplies the address of 4 consecutive bf16 values; lane j receives element j % 4
 // of the values addressed by lanes 4e + j / 4, for e = 0..3.

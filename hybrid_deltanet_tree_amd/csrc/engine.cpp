@@ -244,12 +244,16 @@ hdt_status launch_kv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *trees
   a.hq = m.attn_hq;
   a.hkv = m.attn_hkv;
   a.c2 = m.attn_scale * 1.4426950408889634f;
-  // Split-pass shape: 8 waves of one 16-row block (up to 128 rows per item, two
-  // waves per SIMD), or 4 waves of three blocks when a tree has 129..192 rows.
+  // Split-pass shape: up to 96 rows (6 blocks of 16), 6 waves that compute one
+  // block each beside 2 waves that only issue the tile loads; up to 128 rows, 8
+  // waves that do both; 129..192 rows, 4 waves of three blocks; more, row groups
+  // of 128.
   int max_blocks = 1;
   for (int t = 0; t < n_trees; ++t) max_blocks = std::max(max_blocks, (trees[t].n_nodes * G + 15) / 16);
   const int waves = (max_blocks > 8 && max_blocks <= 12) ? 4 : 8;
   const int nb = waves == 4 ? 3 : 1;
+  const int pw = max_blocks <= 6 ? 2 : 0;
+  const int cw = waves - pw;
   int32_t items_a = 0, items_b = 0;
   for (int t = 0; t < n_trees; ++t) {
     const hdt_tree &tr = trees[t];
@@ -277,18 +281,16 @@ hdt_status launch_kv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *trees
     const int64_t tb0 = s.d.length / kKvTile * kKvTile;
     x.carry_tiles = static_cast<int32_t>((tb0 - static_cast<int64_t>(x.n_full) * s.split) / kKvTile);
     const int blocks = (tr.n_nodes * G + 15) / 16;
-    x.row_groups = (blocks + waves * nb - 1) / (waves * nb);
+    x.row_groups = (blocks + cw * nb - 1) / (cw * nb);
     x.a_per_head = (x.n_full + (x.carry_tiles > 0 ? 1 : 0)) * x.row_groups;
-    x.a_begin = items_a;
-    items_a += m.attn_hkv * x.a_per_head;
-    x.b_begin = items_b;
-    items_b += m.attn_hkv * tr.n_nodes * kKvQuarters;
+    items_a = std::max(items_a, m.attn_hkv * x.a_per_head);
+    items_b = std::max(items_b, m.attn_hkv * tr.n_nodes * kKvQuarters);
     std::memcpy(x.parent, par[t], kMaxNodes);
     std::memcpy(x.depth, dep[t], kMaxNodes);
   }
   if (items_a > 0) {
     ProfScope p(e, 1);
-    hdt_status st = check_hip(e, launch_kv_split(a, m.attn_d, waves, nb, items_a, stream, p.events()),
+    hdt_status st = check_hip(e, launch_kv_split(a, m.attn_d, waves, nb, pw, items_a, stream, p.events()),
                               "attention split launch");
     if (st != HDT_OK) return st;
   }
@@ -315,7 +317,6 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
       a.dv = m.gdn_dv;
       a.n_max = n_max;
       a.scale = m.gdn_scale;
-      int32_t wg = 0;
       for (int t = 0; t < n_trees; ++t) {
         const hdt_tree &tr = trees[t];
         SlotState &s = e->slots[tr.slot];
@@ -335,11 +336,9 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
                    static_cast<size_t>(ki) * nm * m.gdn_hk * m.gdn_dk * e->esz;
         g.a_pend = static_cast<char *>(s.a_pend) + static_cast<size_t>(ki) * nm * m.gdn_hv * e->esz;
         g.n = tr.n_nodes;
-        g.wg_begin = wg;
         std::memcpy(g.parent, par[t], kMaxNodes);
         std::memcpy(g.depth, dep[t], kMaxNodes);
         a.n_saves = std::max(a.n_saves, plan_saves(tr.n_nodes, par[t], g.save));
-        wg += m.gdn_hv * (m.gdn_dv / kGdnCols);
       }
       ProfScope p(e, 0);
       hdt_status st =

@@ -54,17 +54,17 @@ __host__ __device__ constexpr size_t gdn_lds_floats(int dk, int n) {
   return static_cast<size_t>(n) * (2 * dk + 4 + 3 * kGdnCols) + ((2 * n + 3) & ~3);
 }
 
-// Sum of x[a] * y[a] over a lane's R elements in a fixed pairwise order.
+// Sum of x[a] * y[a] over a lane's R elements in a fixed order: even and odd
+// elements in two fused chains, then their sum.
 template <int R>
 __device__ __forceinline__ float lane_dot(const float *x, const float *y) {
-  float s[R / 2];
+  float s0 = x[0] * y[0], s1 = x[1] * y[1];
 #pragma unroll
-  for (int j = 0; j < R / 2; ++j) s[j] = fmaf(x[2 * j], y[2 * j], x[2 * j + 1] * y[2 * j + 1]);
-#pragma unroll
-  for (int w = R / 4; w >= 1; w /= 2)
-#pragma unroll
-    for (int j = 0; j < w; ++j) s[j] = s[2 * j] + s[2 * j + 1];
-  return s[0];
+  for (int a = 2; a < R; a += 2) {
+    s0 = fmaf(x[a], y[a], s0);
+    s1 = fmaf(x[a + 1], y[a + 1], s1);
+  }
+  return s0 + s1;
 }
 
 template <int R>
@@ -126,10 +126,9 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
   constexpr int MAXC = (kMaxNodes * CPR + kGdnThreads - 1) / kGdnThreads;
   constexpr int VCH = kGdnCols / EPC;        // chunks of one node's 16 value columns
   extern __shared__ __align__(16) float g_lds[];
-  const int bid = blockIdx.x;
-  int t = 0;
-  while (t + 1 < P.n_trees && bid >= P.t[t + 1].wg_begin) ++t;
-  const GdnTree &T = P.t[t];
+  // grid: x = (v head, column group), y = tree
+  const GdnTree &T = P.t[blockIdx.y];
+  scalar_touch(&T, sizeof(GdnTree), &P.n_trees);
   const int n = T.n;
   const int nm = P.n_max;
   float *kf = g_lds;
@@ -144,7 +143,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
   int8_t *savel = anc + nm * kMaxNodes;
 
   const int cgroups = P.dv / kGdnCols;
-  const int local = bid - T.wg_begin;
+  const int local = blockIdx.x;
   const int h = local / cgroups, cg = local % cgroups;
   const int ratio = P.hv / P.hk, qh = h / ratio;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -303,10 +302,15 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
       for (int a = 0; a < R; ++a) cur[a] = fmaf(kk[a], uk, ak * cur[a]);
     }
   };
+  // the parent's state into `cur` when it is not the node just finished
+  auto prepare = [&](const GdnNode<R> &x) {
+    const int w = __builtin_amdgcn_readfirstlane(__float_as_int(x.sc.w));
+    const int p = static_cast<int8_t>(w & 0xFF);
+    if (p != cur_node) restore(p);
+  };
   auto step = [&](int i, const GdnNode<R> &x) {
     const int w = __builtin_amdgcn_readfirstlane(__float_as_int(x.sc.w));
-    const int p = static_cast<int8_t>(w & 0xFF), keep = static_cast<int8_t>((w >> 8) & 0xFF);
-    if (p != cur_node) restore(p);
+    const int keep = static_cast<int8_t>((w >> 8) & 0xFF);
     float A[R];
 #pragma unroll
     for (int a = 0; a < R; ++a) A[a] = x.sc.x * cur[a];
@@ -327,15 +331,28 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
     }
     cur_node = i;
   };
-  // (the scheduling barriers keep the next node's loads ahead of this node's work)
+  // Per node: wait for its operands (loaded during the previous node), restore
+  // the parent's state if needed, issue the next node's loads into the other
+  // register set, then compute with no LDS read outstanding that the node needs.
+  // The next node's index is clamped so the loads are unconditional.  LDS
+  // operations of a wave complete in order, so the operands are in once at most
+  // the previous node's two u / o stores are outstanding (its state copy, when
+  // kept, only makes the wait longer).
   GdnNode<R> na, nb;
   load_node(0, na);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   for (int i = 0; i < n; i += 2) {
-    if (i + 1 < n) load_node(i + 1, nb);
+    __builtin_amdgcn_s_waitcnt(0xC27F);  // lgkmcnt(2)
+    prepare(na);
+    __builtin_amdgcn_sched_barrier(0);
+    load_node(min(i + 1, n - 1), nb);
     __builtin_amdgcn_sched_barrier(0);
     step(i, na);
     if (i + 1 >= n) break;
-    if (i + 2 < n) load_node(i + 2, na);
+    __builtin_amdgcn_s_waitcnt(0xC27F);
+    prepare(nb);
+    __builtin_amdgcn_sched_barrier(0);
+    load_node(min(i + 2, n - 1), na);
     __builtin_amdgcn_sched_barrier(0);
     step(i + 1, nb);
   }
@@ -1060,12 +1077,12 @@ size_t commit_lds_bytes(int D, int bf16, int m) {
 }
 
 hipError_t launch_gdn_tree(const GdnLaunch &a, int dk, int bf16, hipStream_t s, KernelEvents ev) {
-  const int blocks = a.t[a.n_trees - 1].wg_begin + a.hv * (a.dv / kGdnCols);
+  const dim3 blocks(a.hv * (a.dv / kGdnCols), a.n_trees);
   const size_t lds = gdn_lds_bytes(dk, a.n_max, a.n_saves);
 #define HDT_GDN(BF, DK)                                                                   \
   do {                                                                                    \
     (void)set_lds(gdn_tree_kernel<BF, DK>, lds);                                                \
-    hipExtLaunchKernelGGL((gdn_tree_kernel<BF, DK>), dim3(blocks), dim3(kGdnThreads), lds, s,     \
+    hipExtLaunchKernelGGL((gdn_tree_kernel<BF, DK>), blocks, dim3(kGdnThreads), lds, s,     \
                           ev.start, ev.stop, 0, a);                                               \
   } while (0)
   if (bf16) {

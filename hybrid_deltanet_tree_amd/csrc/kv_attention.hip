@@ -98,47 +98,84 @@ struct KvRows {
   }
 };
 
+// Tile-invariant LDS byte offsets of this lane's operand reads within a tile: the
+// score operand of key block 0 at k-step kk, and the low transposed value read of
+// column block db0 + j.  Key block 1 and the high value read sit 16 rows further
+// (the swizzle repeats every 16 rows), an immediate offset.
+template <int D, int NDB>
+struct KvLane {
+  uint32_t ko[KvCfg<D>::KQ];
+  uint32_t vo[NDB];
+  __device__ __forceinline__ void init(int db0) {
+    using C = KvCfg<D>;
+    const int lane = threadIdx.x & 63, g = lane >> 4, ln = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < C::KQ; ++kk) ko[kk] = static_cast<uint32_t>(chunk_off<D>(ln, 4 * kk + g));
+    const int r0 = 4 * g + (ln >> 2);
+    const int half8 = 8 * (ln & 1);
+#pragma unroll
+    for (int j = 0; j < NDB; ++j) {
+      const int c = 2 * (db0 + j) + ((ln & 3) >> 1);
+      vo[j] = static_cast<uint32_t>(C::HALF + chunk_off<D>(r0, c) + half8);
+    }
+  }
+};
+
 // One tile (kKvTile keys from absolute position tb; K then V in `tile`, swizzled)
-// for the NB row blocks of this wave, output columns [16 db0, 16 (db0 + NDB)).
+// for the NB row blocks of this wave, output columns [16 db0, 16 (db0 + NDB)) with
+// the offsets of `ofs` (made for db0).
 // MASK: keys past `pos` get probability 0.  Every block is computed (a block with
 // no rows of its own holds copies of real queries and is discarded by the caller),
 // so the instruction stream has no branches; all LDS reads of an operand are
 // issued before the MFMAs that use them, and the value reads before the softmax.
 template <int D, int NB, int NDB, bool MASK>
-__device__ __forceinline__ void kv_tile(KvRows<D, NB, NDB> &st, const unsigned char *tile, int db0,
+__device__ __forceinline__ void kv_tile(KvRows<D, NB, NDB> &st, uint32_t tile, const KvLane<D, NDB> &ofs,
                                         int64_t tb, int64_t pos, float c2) {
   using C = KvCfg<D>;
-  const int lane = threadIdx.x & 63, g = lane >> 4, ln = lane & 15;
-  const unsigned char *lk = tile;
-  const unsigned char *lv = tile + C::HALF;
+  constexpr int KB1 = 16 * C::ROWB;  // key block 1 / value rows 16..31
+  constexpr int KQ = C::KQ;
+  // the first MFMA waits for its reads while the rest stay in flight (the LDS
+  // counter holds at most 15 outstanding reads)
+  constexpr int KPRE = KQ > 7 ? 7 : KQ;
+  const int lane = threadIdx.x & 63, g = lane >> 4;
+  typedef __attribute__((address_space(3))) const bf16x8 *lds_b8;
   // ---- scores S^T = K Q^T: lane (g, n) gets keys 16 kb + 4 g + i of row n
-  bf16x8 ka[2][C::KQ];
+  bf16x8 ka[2][KQ];
+  // nothing of this wave's is outstanding on the LDS here; saying so lets the
+  // waits below count only this tile's reads
+  __builtin_amdgcn_s_waitcnt(0xC07F);
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int kk = 0; kk < C::KQ; ++kk)
-      ka[kb][kk] = *reinterpret_cast<const bf16x8 *>(lk + chunk_off<D>(16 * kb + ln, 4 * kk + g));
+  for (int kk = 0; kk < KPRE; ++kk) {
+    const uint32_t a = tile + ofs.ko[kk];
+    ka[0][kk] = *(lds_b8)(lds_ptr(a));
+    ka[1][kk] = *(lds_b8)(lds_ptr(a + KB1));
+  }
+  __builtin_amdgcn_sched_barrier(0);
   floatx4 s[NB][2];
 #pragma unroll
   for (int b = 0; b < NB; ++b) s[b][0] = s[b][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kk = 0; kk < C::KQ; ++kk)
+  for (int kk = 0; kk < KQ; ++kk) {
+    if (kk + KPRE < KQ) {
+      const uint32_t a = tile + ofs.ko[kk + KPRE];
+      ka[0][kk + KPRE] = *(lds_b8)(lds_ptr(a));
+      ka[1][kk + KPRE] = *(lds_b8)(lds_ptr(a + KB1));
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int b = 0; b < NB; ++b)
         s[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][kk], st.q[b][kk], s[b][kb], 0, 0, 0);
+  }
   // ---- value operands for O^T += V^T P^T.  The transposed read gives lane (g, m)
   // the values of keys 4 g + e (lo) and 16 + 4 g + e (hi), e = 0..3, at column
   // 16 db + m: the same key order as the probabilities below.
-  const int r0 = 4 * g + (ln >> 2);
-  const int half8 = 8 * (ln & 1);
   bf16x8 va[NDB];
 #pragma unroll
   for (int j = 0; j < NDB; ++j) {
-    const int c = 2 * (db0 + j) + ((ln & 3) >> 1);
-    const shortx4 lo = ds_read_tr(lv + chunk_off<D>(r0, c) + half8);
-    const shortx4 hi = ds_read_tr(lv + chunk_off<D>(r0 + 16, c) + half8);
+    const uint32_t a = tile + ofs.vo[j];
+    const shortx4 lo = ds_read_tr_at(a);
+    const shortx4 hi = ds_read_tr_at(a + KB1);
     va[j] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
                                            lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
   }
@@ -213,19 +250,21 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
 }
 
-// This wave's share (IPW wave-wide loads) of the direct-to-LDS loads of a tile of
-// one kv head.  Lane l of a wave-wide load lands at LDS (M0 + 16 l); the lane picks
-// the global chunk that the swizzle puts there.  The loads are issued from inline
-// assembly so that the compiler does not fence later LDS reads on them; the caller
-// waits with wait_vm before the barrier that publishes the tile.
-template <int D, int W>
+// A producer wave's share (IPW wave-wide loads) of the direct-to-LDS loads of a tile
+// of one kv head, with NP producer waves.  Lane l of a wave-wide load lands at LDS
+// (M0 + 16 l); the lane picks the global chunk that the swizzle puts there.  The
+// loads are issued from inline assembly so that the compiler does not fence later
+// LDS reads on them; the caller waits with wait_vm before the barrier that
+// publishes the tile.
+template <int D, int NP>
 struct KvDma {
-  static constexpr int IPW = KvCfg<D>::LOADS / W;
+  static constexpr int IPW = KvCfg<D>::LOADS / NP;
+  static_assert(KvCfg<D>::LOADS % NP == 0, "loads per producer wave");
   uint32_t off[IPW];  // byte offset of this lane's chunk within the tile's rows
   int ins0;           // first wave-wide load of this wave (uniform)
-  __device__ __forceinline__ void init() {
+  __device__ __forceinline__ void init(int pw) {
     using C = KvCfg<D>;
-    ins0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * IPW;
+    ins0 = __builtin_amdgcn_readfirstlane(pw) * IPW;
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int x = 0; x < IPW; ++x) {
@@ -248,7 +287,7 @@ struct KvDma {
       const bool v = ins >= C::LOADS / 2;  // uniform over the wave
       asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
                    :
-                   : "v"(base + off[x]), "s"(lds + ins * 1024), "s"(v ? vres : kres)
+                   : "v"(base + off[x]), "s"(__builtin_amdgcn_readfirstlane(lds + ins * 1024)), "s"(v ? vres : kres)
                    : "memory", "m0");
     }
   }
@@ -265,46 +304,24 @@ __device__ __forceinline__ int64_t part_off(const KvTree &T, int h, int s, int b
   return ((((static_cast<int64_t>(h) * T.nsplit_cap + s) * nblk_cap + blk) * KvCfg<D>::DB + db) * 64 + lane) * 8;
 }
 
-// Direct-to-LDS load of query rows [row0, row0 + 16 * nq) of kv head h (row r is q
-// head h * G + r % G of node r / G; rows past the tree's are clamped to its last row)
-// into `dst`, swizzled like a K tile.  Issued by every wave, RPL rows per load.
-template <int D, int W>
-__device__ __forceinline__ void q_dma(unsigned char *dst, __amdgpu_buffer_rsrc_t qres, int row0, int nq, int M,
-                                      int G, int hq, int h) {
-  using C = KvCfg<D>;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int loads = 16 * nq / C::RPL;
-  for (int ins = wave; ins < loads; ins += W) {
-    const int row = ins * C::RPL + lane / C::CPR;
-    const int cs = lane % C::CPR;
-    const int r = min(row0 + row, M - 1);
-    const uint32_t off = static_cast<uint32_t>((static_cast<int64_t>(r / G) * hq + h * G + r % G) * C::ROWB +
-                                               ((cs ^ swz<D>(row)) << 4));
-    const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-        (__attribute__((address_space(3))) unsigned char *)(dst + ins * 1024)));
-    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-                 :
-                 : "v"(off), "s"(m0), "s"(qres)
-                 : "memory", "m0");
-  }
-}
-
-template <int D, int W, int NB>
+// W waves of which the first CW = W - PW compute (NB row blocks each) and the last
+// PW only issue the tile loads (PW = 0: every wave issues its share of them).  The
+// producer waves keep the load queue full without holding up the MFMA and softmax
+// work of the others.
+template <int D, int W, int NB, int PW>
 __global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
   using C = KvCfg<D>;
   constexpr int S = kKvStages;
-  constexpr int IPW = KvDma<D, W>::IPW;
-  // queries of the item (W * NB blocks of 16 rows) sit in the last QS stages until
-  // they are in registers
-  constexpr int QS = (W * NB * 16 * C::ROWB + C::TILE - 1) / C::TILE;
-  static_assert(QS < S, "the queries must leave a stage for the first tile");
+  constexpr int CW = W - PW;              // computing waves
+  constexpr int NP = PW > 0 ? PW : W;     // producer waves
+  constexpr int IPW = KvDma<D, NP>::IPW;
+  static_assert((S - 2) * IPW <= 63, "loads in flight per wave");
   __shared__ __align__(1024) unsigned char ring[S][C::TILE];
-  const int bid = blockIdx.x;
-  int t = 0;
-  while (t + 1 < P.n_trees && bid >= P.t[t + 1].a_begin) ++t;
-  const KvTree &T = P.t[t];
-  const int local = bid - T.a_begin;
+  // grid: x = item of the tree, y = tree
+  const KvTree &T = P.t[blockIdx.y];
+  scalar_touch(&T, sizeof(KvTree), &P.n_trees);
+  const int local = blockIdx.x;
+  if (local >= P.hkv * T.a_per_head) return;
   const int h = local / T.a_per_head, r = local % T.a_per_head;
   const int rg = r % T.row_groups, s = r / T.row_groups;
   const bool carry = s == T.n_full;  // the tiles of split n_full below tb0
@@ -314,46 +331,44 @@ __global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
   const int split_tiles = T.split / kKvTile;
   const int ntiles = carry ? T.carry_tiles : split_tiles;
   const int64_t tile0 = static_cast<int64_t>(s) * split_tiles;
-  // Row blocks of the item: [rblk0, rblk0 + nblk); wave w takes blocks rblk0 + NB w + k.
-  // Waves past the rows only load.
-  const int rblk0 = rg * W * NB;
-  const int nblk = min(W * NB, (M + 15) / 16 - rblk0);
-  const bool computes = wave * NB < nblk;
+  // Row blocks of the item: [rblk0, rblk0 + nblk); wave w < CW takes blocks
+  // rblk0 + NB w + k.  Waves past the rows do not compute.
+  const int rblk0 = rg * CW * NB;
+  const int nblk = min(CW * NB, (M + 15) / 16 - rblk0);
+  const bool computes = wave < CW && wave * NB < nblk;
+  const bool producer = PW == 0 || wave >= CW;  // uniform over the wave
+  const int pw = PW == 0 ? wave : wave - CW;
 
   const unsigned char *kc = static_cast<const unsigned char *>(T.kc) + static_cast<int64_t>(h) * T.cap * C::ROWB;
   const unsigned char *vc = static_cast<const unsigned char *>(T.vc) + static_cast<int64_t>(h) * T.cap * C::ROWB;
   const __amdgpu_buffer_rsrc_t kres = make_rsrc(kc, T.L * C::ROWB);
   const __amdgpu_buffer_rsrc_t vres = make_rsrc(vc, T.L * C::ROWB);
-  const __amdgpu_buffer_rsrc_t qres = make_rsrc(T.q, static_cast<int64_t>(T.n) * P.hq * C::ROWB);
 
-  // ---- prologue: queries and the first S - QS tiles in flight together
-  // every computing wave gets NB blocks of real query rows (past the tree's rows,
-  // copies of its last row)
-  KvDma<D, W> dma;
-  dma.init();
-  q_dma<D, W>(ring[S - QS], qres, 16 * rblk0, (nblk + NB - 1) / NB * NB, M, G, P.hq, h);
-  const int first = min(S - QS, ntiles);
-  for (int x = 0; x < first; ++x) dma.issue(ring[x], kres, vres, (tile0 + x) * kKvTile);
-  // this wave's query loads are the oldest; tiles 1 .. first - 1 may stay in flight
-  switch (first - 1) {
-    case 3: wait_vm<3 * IPW>(); break;
-    case 2: wait_vm<2 * IPW>(); break;
-    case 1: wait_vm<IPW>(); break;
-    default: wait_vm<0>(); break;
-  }
-  bare_barrier();  // queries and tile 0 are in LDS
+  // ---- prologue: the producers load tile 0 while the computing waves load their
+  // query rows straight into registers (rows past the tree's repeat its last row);
+  // the other tiles go out once tile 0 is in, so that every workgroup's first tile
+  // is not queued behind the rest of the burst.
+  KvDma<D, NP> dma;
+  dma.init(pw);
+  if (producer) dma.issue(ring[0], kres, vres, tile0 * kKvTile);
   KvRows<D, NB, C::DB> st;
+  KvLane<D, C::DB> ofs;
+  ofs.init(0);
+  if (computes) {
+    const unsigned char *qb = static_cast<const unsigned char *>(T.q);
 #pragma unroll
-  for (int k = 0; k < NB; ++k) {
-    const int row = 16 * (NB * wave + k) + ln;
+    for (int k = 0; k < NB; ++k) {
+      const int r = min(16 * (rblk0 + NB * wave + k) + ln, M - 1);
+      const unsigned char *qr = qb + (static_cast<int64_t>(r / G) * P.hq + h * G + r % G) * C::ROWB;
 #pragma unroll
-    for (int kk = 0; kk < C::KQ; ++kk)
-      st.q[k][kk] = *reinterpret_cast<const bf16x8 *>(ring[S - QS] + chunk_off<D>(row, 4 * kk + g));
+      for (int kk = 0; kk < C::KQ; ++kk) st.q[k][kk] = *reinterpret_cast<const bf16x8 *>(qr + (4 * kk + g) * 16);
+    }
   }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // query reads done (lgkmcnt 0)
-  bare_barrier();                      // the query stages are free
-  for (int x = first; x < S - 1 && x < ntiles; ++x) dma.issue(ring[x], kres, vres, (tile0 + x) * kKvTile);
+  wait_vm<0>();
+  bare_barrier();  // tile 0 is in LDS
   st.reset();
+  const uint32_t ring0 = lds_addr(ring[0]);
+  int stage = 0;  // tt % S
   for (int tt = 0; tt < ntiles; ++tt) {
     if (tt > 0) {
       // tiles tt .. tt + ahead are in flight; wait for tile tt
@@ -369,8 +384,15 @@ __global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
       }
       bare_barrier();  // tile tt landed for every wave; tile tt - 1 is no longer read
     }
-    if (tt + S - 1 < ntiles) dma.issue(ring[(tt + S - 1) % S], kres, vres, (tile0 + tt + S - 1) * kKvTile);
-    if (computes) kv_tile<D, NB, C::DB, false>(st, ring[tt % S], 0, 0, 0, P.c2);
+    if (producer) {
+      if (tt == 0) {
+        for (int x = 1; x < S && x < ntiles; ++x) dma.issue(ring[x], kres, vres, (tile0 + x) * kKvTile);
+      } else if (tt + S - 1 < ntiles) {
+        dma.issue(ring[stage == 0 ? S - 1 : stage - 1], kres, vres, (tile0 + tt + S - 1) * kKvTile);
+      }
+    }
+    if (computes) kv_tile<D, NB, C::DB, false>(st, ring0 + stage * C::TILE, ofs, 0, 0, P.c2);
+    stage = stage == S - 1 ? 0 : stage + 1;
   }
   if (!computes) return;
 #pragma unroll
@@ -383,17 +405,17 @@ __global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
       const float inv_l = 1.0f / st.l[k];
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
-        *reinterpret_cast<uint2 *>(po + part_off<D>(T, h, s, blk, db, lane)) = norm_half4(st.acc[k][db], inv_l);
+        st_agent(po + part_off<D>(T, h, s, blk, db, lane), norm_half4(st.acc[k][db], inv_l));
       if (g == 0 && row < M) {
         const int64_t prow = (static_cast<int64_t>(h) * T.nsplit_cap + s) * T.rows_cap + row;
-        *reinterpret_cast<float2 *>(T.part_ml + prow * 2) = make_float2(st.m[k], st.l[k]);
+        st_agent(T.part_ml + prow * 2, make_float2(st.m[k], st.l[k]));
       }
     } else if (row < M) {
       const int64_t crow = static_cast<int64_t>(h) * T.rows_cap + row;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
-        *reinterpret_cast<floatx4 *>(T.carry_acc + crow * D + 16 * db + 4 * g) = st.acc[k][db];
-      if (g == 0) *reinterpret_cast<float2 *>(T.carry_ml + crow * 2) = make_float2(st.m[k], st.l[k]);
+        st_agent(T.carry_acc + crow * D + 16 * db + 4 * g, st.acc[k][db]);
+      if (g == 0) st_agent(T.carry_ml + crow * 2, make_float2(st.m[k], st.l[k]));
     }
   }
 }
@@ -457,11 +479,11 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
   __shared__ float x_ml[16][2];
   __shared__ __align__(16) float f_acc[16][QD];  // the row's last split, float32 state
   __shared__ float f_ml[16][2];
-  const int bid = blockIdx.x;
-  int t = 0;
-  while (t + 1 < P.n_trees && bid >= P.t[t + 1].b_begin) ++t;
-  const KvTree &T = P.t[t];
-  const int local = bid - T.b_begin;
+  // grid: x = (kv head, node, column quarter) of the tree, y = tree
+  const KvTree &T = P.t[blockIdx.y];
+  scalar_touch(&T, sizeof(KvTree), &P.n_trees);
+  const int local = blockIdx.x;
+  if (local >= P.hkv * T.n * kKvQuarters) return;
   const int qd = local % kKvQuarters, rest = local / kKvQuarters;
   const int node = rest % T.n, h = rest / T.n;
   const int G = P.hq / P.hkv;
@@ -497,6 +519,8 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
     // gather below (lanes past the node's q heads read a real row and are
     // discarded; without a carry the loads read the buffer and are dropped)
     KvRows<D, 1, QDB> st;
+    KvLane<D, QDB> ofs;
+    ofs.init(qd * QDB);
     const int jr = min(ln, G - 1);
     {
       const unsigned char *qrow =
@@ -573,7 +597,7 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
         }
         st.reset();
       }
-      kv_tile<D, 1, QDB, true>(st, tiles[tt], qd * QDB, tb, pos, P.c2);
+      kv_tile<D, 1, QDB, true>(st, lds_addr(tiles[tt]), ofs, tb, pos, P.c2);
     }
     if (ln < G) {
 #pragma unroll
@@ -734,18 +758,20 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
 
 }  // namespace
 
-hipError_t launch_kv_split(const KvLaunch &a, int D, int waves, int nb, int n_blocks, hipStream_t s,
+hipError_t launch_kv_split(const KvLaunch &a, int D, int waves, int nb, int pw, int max_items, hipStream_t s,
                            KernelEvents ev) {
-#define HDT_KV_SPLIT(DD, W, NB)                                                                         \
-  hipExtLaunchKernelGGL((kv_split_kernel<DD, W, NB>), dim3(n_blocks), dim3(W * 64), 0, s, ev.start, ev.stop, \
-                        0, a)
+  const dim3 grid(max_items, a.n_trees);
+#define HDT_KV_SPLIT(DD, W, NB, PW)                                                                         \
+  hipExtLaunchKernelGGL((kv_split_kernel<DD, W, NB, PW>), grid, dim3(W * 64), 0, s, ev.start, ev.stop, 0, a)
   if (D == 256) {
-    if (waves == 8 && nb == 1) HDT_KV_SPLIT(256, 8, 1);
-    else if (waves == 4 && nb == 3) HDT_KV_SPLIT(256, 4, 3);
+    if (waves == 8 && nb == 1 && pw == 2) HDT_KV_SPLIT(256, 8, 1, 2);
+    else if (waves == 8 && nb == 1 && pw == 0) HDT_KV_SPLIT(256, 8, 1, 0);
+    else if (waves == 4 && nb == 3 && pw == 0) HDT_KV_SPLIT(256, 4, 3, 0);
     else return hipErrorInvalidValue;
   } else if (D == 64) {
-    if (waves == 8 && nb == 1) HDT_KV_SPLIT(64, 8, 1);
-    else if (waves == 4 && nb == 3) HDT_KV_SPLIT(64, 4, 3);
+    if (waves == 8 && nb == 1 && pw == 2) HDT_KV_SPLIT(64, 8, 1, 2);
+    else if (waves == 8 && nb == 1 && pw == 0) HDT_KV_SPLIT(64, 8, 1, 0);
+    else if (waves == 4 && nb == 3 && pw == 0) HDT_KV_SPLIT(64, 4, 3, 0);
     else return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;
@@ -754,11 +780,12 @@ hipError_t launch_kv_split(const KvLaunch &a, int D, int waves, int nb, int n_bl
   return hipGetLastError();
 }
 
-hipError_t launch_kv_tree(const KvLaunch &a, int D, int n_blocks, hipStream_t s, KernelEvents ev) {
+hipError_t launch_kv_tree(const KvLaunch &a, int D, int max_items, hipStream_t s, KernelEvents ev) {
+  const dim3 grid(max_items, a.n_trees);
   if (D == 256) {
-    hipExtLaunchKernelGGL((kv_tree_kernel<256>), dim3(n_blocks), dim3(kKvThreads), 0, s, ev.start, ev.stop, 0, a);
+    hipExtLaunchKernelGGL((kv_tree_kernel<256>), grid, dim3(kKvThreads), 0, s, ev.start, ev.stop, 0, a);
   } else if (D == 64) {
-    hipExtLaunchKernelGGL((kv_tree_kernel<64>), dim3(n_blocks), dim3(kKvThreads), 0, s, ev.start, ev.stop, 0, a);
+    hipExtLaunchKernelGGL((kv_tree_kernel<64>), grid, dim3(kKvThreads), 0, s, ev.start, ev.stop, 0, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -36,7 +36,6 @@ struct GdnTree {
   void *k_pend;                          // [max_nodes][hk][dk]: copy of k (io dtype)
   void *a_pend;                          // [max_nodes][hv]:     copy of alpha (io dtype)
   int32_t n;
-  int32_t wg_begin;                      // first workgroup of this tree
   int8_t parent[kMaxNodes];
   int8_t depth[kMaxNodes];
   int8_t save[kMaxNodes];                // LDS slot that keeps node i's state, or -1
@@ -111,8 +110,7 @@ struct KvTree {
   int32_t n_full;                         // splits wholly below L
   int32_t carry_tiles;                    // tiles of split n_full below tb0
   int32_t row_groups;                     // split-pass items per split (row blocks / blocks per item)
-  int32_t a_begin, a_per_head;            // split pass: first block, items per kv head
-  int32_t b_begin;                        // tree pass: first block
+  int32_t a_per_head;                     // split pass: items per kv head
   alignas(4) int8_t parent[kMaxNodes];    // read as 32-bit words
   alignas(4) int8_t depth[kMaxNodes];
 };
@@ -170,9 +168,9 @@ hipError_t launch_attn_split(const AttnLaunch &a, int D, int bf16, int n_blocks,
 hipError_t launch_attn_fold(const FoldLaunch &a, int D, int bf16, int n_blocks, hipStream_t s,
                             KernelEvents ev);
 // Split pass with `waves` waves of `nb` 16-row blocks each: (8, 1) or (4, 3).
-hipError_t launch_kv_split(const KvLaunch &a, int D, int waves, int nb, int n_blocks, hipStream_t s,
+hipError_t launch_kv_split(const KvLaunch &a, int D, int waves, int nb, int pw, int max_items, hipStream_t s,
                            KernelEvents ev);
-hipError_t launch_kv_tree(const KvLaunch &a, int D, int n_blocks, hipStream_t s, KernelEvents ev);
+hipError_t launch_kv_tree(const KvLaunch &a, int D, int max_items, hipStream_t s, KernelEvents ev);
 hipError_t launch_commit(const CommitLaunch &a, int dk, int bf16, int n_blocks, hipStream_t s,
                          KernelEvents ev);
 
