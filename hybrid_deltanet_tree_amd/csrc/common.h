@@ -80,22 +80,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
                                            static_cast<int>(bytes), 0x00020000);
 }
 
-// Stores at device (agent) scope: written through this XCD's L2, so results that a
-// later kernel reads are not left dirty in L2 for the end-of-kernel write-back.
-__device__ __forceinline__ void st_agent(void *p, uint64_t v) {
-  __hip_atomic_store(static_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent(void *p, uint2 v) {
-  st_agent(p, static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32));
-}
-__device__ __forceinline__ void st_agent(void *p, float2 v) {
-  st_agent(p, make_uint2(__float_as_uint(v.x), __float_as_uint(v.y)));
-}
-__device__ __forceinline__ void st_agent(void *p, floatx4 v) {
-  st_agent(p, make_uint2(__float_as_uint(v[0]), __float_as_uint(v[1])));
-  st_agent(static_cast<char *>(p) + 8, make_uint2(__float_as_uint(v[2]), __float_as_uint(v[3])));
-}
-
 // Brings the 64-byte lines of a uniform (kernel-argument) region into the scalar
 // cache with loads issued together and one wait, so that later reads of its fields
 // hit that cache instead of each paying a memory round trip in turn.  `bytes` is at

@@ -168,8 +168,7 @@ hdt_status ensure_alloc(hdt_engine *e) {
       const size_t base = static_cast<size_t>(m.attn_hkv) * s.nsplit_cap * rows;
       const size_t carry = static_cast<size_t>(m.attn_hkv) * rows;
       if (m.io_dtype == HDT_BF16) {
-        const size_t blocks = static_cast<size_t>(m.attn_hkv) * s.nsplit_cap * ((rows + 15) / 16);
-        if (hipMalloc(&s.part_o, blocks * 16 * m.attn_d * 2) != hipSuccess ||
+        if (hipMalloc(&s.part_o, base * m.attn_d * 2) != hipSuccess ||
             hipMalloc(&s.part_ml, base * 2 * sizeof(float)) != hipSuccess ||
             hipMalloc(&s.carry_acc, carry * m.attn_d * sizeof(float)) != hipSuccess ||
             hipMalloc(&s.carry_ml, carry * 2 * sizeof(float)) != hipSuccess)

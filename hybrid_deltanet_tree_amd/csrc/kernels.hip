@@ -96,8 +96,25 @@ __device__ __forceinline__ void unpack16(const uint4 &c, float *out) {
   }
 }
 
-// Two interleaved rowsum16 reductions.
-__device__ __forceinline__ void rowsum16x2(float &a, float &b) {
+// Sum over the LPC lanes that hold one value column (16: a DPP row; 32: two
+// adjacent rows, joined by a row swap).  Every lane of the column gets the same
+// bits: each stage adds the same two partials in either order.
+template <int LPC>
+__device__ __forceinline__ float colsum(float x) {
+  static_assert(LPC == 16 || LPC == 32, "lanes per column");
+  x = rowsum16(x);
+  if constexpr (LPC == 32) {
+    // with both operands x, the two results hold this row's and the partner row's
+    // value (in an order that depends on the row): their sum is the same in both
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return x;
+}
+
+// Two interleaved colsum reductions.
+template <int LPC>
+__device__ __forceinline__ void colsum2(float &a, float &b) {
   a = a + dpp<0xB1>(a);
   b = b + dpp<0xB1>(b);
   a = a + dpp<0x4E>(a);
@@ -106,6 +123,12 @@ __device__ __forceinline__ void rowsum16x2(float &a, float &b) {
   b = b + dpp<0x141>(b);
   a = a + dpp<0x140>(a);
   b = b + dpp<0x140>(b);
+  if constexpr (LPC == 32) {
+    const auto ra = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+    const auto rb = __builtin_amdgcn_permlane16_swap(__float_as_uint(b), __float_as_uint(b), false, false);
+    a = __uint_as_float(ra[0]) + __uint_as_float(ra[1]);
+    b = __uint_as_float(rb[0]) + __uint_as_float(rb[1]);
+  }
 }
 
 // One node's operands, in the registers of a lane: its key rows and s*q rows,
@@ -118,12 +141,16 @@ struct GdnNode {
 };
 
 template <bool BF, int DK>
-__global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P) {
-  constexpr int R = DK / 16;                 // key rows per lane; 16 lanes hold one value column
+__global__ __launch_bounds__(gdn_threads(DK)) void gdn_tree_kernel(const GdnLaunch P) {
+  constexpr int LPC = kGdnLanes;             // lanes per value column
+  constexpr int R = DK / LPC;                // key rows per lane
+  constexpr int CPW = 64 / LPC;              // value columns per wave
+  constexpr int NT = gdn_threads(DK);        // kGdnCols / CPW waves
+  static_assert(NT == kGdnCols / CPW * 64, "workgroup shape");
   constexpr int ESZ = BF ? 2 : 4;
   constexpr int EPC = 16 / ESZ;              // elements per 16-byte chunk
   constexpr int CPR = DK / EPC;              // chunks per q/k row
-  constexpr int MAXC = (kMaxNodes * CPR + kGdnThreads - 1) / kGdnThreads;
+  constexpr int MAXC = (kMaxNodes * CPR + NT - 1) / NT;
   constexpr int VCH = kGdnCols / EPC;        // chunks of one node's 16 value columns
   extern __shared__ __align__(16) float g_lds[];
   // grid: x = (v head, column group), y = tree
@@ -147,8 +174,8 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
   const int h = local / cgroups, cg = local % cgroups;
   const int ratio = P.hv / P.hk, qh = h / ratio;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int lc = wave * 4 + (lane >> 4);  // value column within the workgroup
-  const int g = lane & 15;                // key rows [g*R, g*R+R)
+  const int lc = wave * CPW + lane / LPC;  // value column within the workgroup
+  const int g = lane % LPC;                // key rows [g*R, g*R+R)
   const int col = cg * kGdnCols + lc;
 
   // ---- issue every load of the prologue before using any of them (tree first)
@@ -166,7 +193,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
   const int nch = n * CPR;
 #pragma unroll
   for (int x = 0; x < MAXC; ++x) {
-    const int c = tid + x * kGdnThreads;
+    const int c = tid + x * NT;
     if (c < nch) {
       const int i = c / CPR, cc = c % CPR;
       const int64_t off = (static_cast<int64_t>(i) * P.hk + qh) * DK * ESZ + cc * 16;
@@ -204,7 +231,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
   const bool keep_k = (cg == 0) && (h % ratio == 0);
 #pragma unroll
   for (int x = 0; x < MAXC; ++x) {
-    const int c = tid + x * kGdnThreads;
+    const int c = tid + x * NT;
     if (c < nch) {
       const int i = c / CPR, cc = c % CPR;
       float kv[EPC], qv[EPC];
@@ -242,13 +269,13 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
   __syncthreads();
   // ---- k . s q of every node (it does not depend on the state), one 16-lane row
   // per node with the walk's own dot product and reduction
-  for (int i0 = 0; i0 < n; i0 += kGdnThreads / 16) {
-    const int i = i0 + (tid >> 4);
+  for (int i0 = 0; i0 < n; i0 += NT / LPC) {
+    const int i = i0 + tid / LPC;
     const int ii = min(i, n - 1);
     float kk[R], qq[R];
     lds_row<R>(kf + ii * DK + g * R, kk);
     lds_row<R>(qs + ii * DK + g * R, qq);
-    const float d = rowsum16(lane_dot<R>(kk, qq));
+    const float d = colsum<LPC>(lane_dot<R>(kk, qq));
     if (i < n && g == 0) nsc[i].z = d;
   }
   __syncthreads();
@@ -256,7 +283,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
   // ---- walk the nodes in index order (parents first).  Per node, from the
   // parent's state P:  A = alpha P;  r = k^T A;  u = beta (v - r);  S = A + k u^T;
   // o = S^T (s q) taken as A^T (s q) + u (k . s q), so the readout does not wait
-  // for the state write.  Every dot product is a lane_dot then a rowsum16.  The
+  // for the state write.  Every dot product is a lane_dot then a colsum.  The
   // loop is unrolled twice so the next node's operands load into the other set.
   float cur[R];
 #pragma unroll
@@ -316,7 +343,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
     for (int a = 0; a < R; ++a) A[a] = x.sc.x * cur[a];
     float r = lane_dot<R>(A, x.k);
     float oa = lane_dot<R>(A, x.q);
-    rowsum16x2(r, oa);
+    colsum2<LPC>(r, oa);
     const float u = x.sc.y * (x.v - r);
 #pragma unroll
     for (int a = 0; a < R; ++a) cur[a] = fmaf(x.k[a], u, A[a]);
@@ -357,7 +384,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_tree_kernel(const GdnLaunch P
     step(i + 1, nb);
   }
   __syncthreads();
-  for (int e = tid; e < n * kGdnCols; e += kGdnThreads) {
+  for (int e = tid; e < n * kGdnCols; e += NT) {
     const int i = e / kGdnCols, c = e % kGdnCols;
     const int64_t idx = (static_cast<int64_t>(i) * P.hv + h) * P.dv + cg * kGdnCols + c;
     st_io<BF>(T.o, idx, ol[e]);
@@ -1082,7 +1109,7 @@ hipError_t launch_gdn_tree(const GdnLaunch &a, int dk, int bf16, hipStream_t s, 
 #define HDT_GDN(BF, DK)                                                                   \
   do {                                                                                    \
     (void)set_lds(gdn_tree_kernel<BF, DK>, lds);                                                \
-    hipExtLaunchKernelGGL((gdn_tree_kernel<BF, DK>), blocks, dim3(kGdnThreads), lds, s,     \
+    hipExtLaunchKernelGGL((gdn_tree_kernel<BF, DK>), blocks, dim3(gdn_threads(DK)), lds, s,  \
                           ev.start, ev.stop, 0, a);                                               \
   } while (0)
   if (bf16) {

@@ -295,13 +295,11 @@ struct KvDma {
 
 // ============================================================================ split pass
 
-// Offset of the 8-byte group (4 columns) that lane `lane` of row block `blk` holds for
-// 16-column block db, in the partials of (kv head h, split s): partials are stored in
-// the MFMA output layout, 512 contiguous bytes per (row block, column block).
+// Byte offset of (row, column) in the fp16 partials of (kv head h, split s): rows
+// of D values, so that the fold reads 16 contiguous bytes per 8 columns.
 template <int D>
-__device__ __forceinline__ int64_t part_off(const KvTree &T, int h, int s, int blk, int db, int lane) {
-  const int64_t nblk_cap = (T.rows_cap + 15) / 16;
-  return ((((static_cast<int64_t>(h) * T.nsplit_cap + s) * nblk_cap + blk) * KvCfg<D>::DB + db) * 64 + lane) * 8;
+__device__ __forceinline__ int64_t part_off(const KvTree &T, int h, int s, int row, int col) {
+  return (((static_cast<int64_t>(h) * T.nsplit_cap + s) * T.rows_cap + row) * D + col) * 2;
 }
 
 // W waves of which the first CW = W - PW compute (NB row blocks each) and the last
@@ -394,28 +392,42 @@ __global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
     if (computes) kv_tile<D, NB, C::DB, false>(st, ring0 + stage * C::TILE, ofs, 0, 0, P.c2);
     stage = stage == S - 1 ? 0 : stage + 1;
   }
+  // ---- epilogue.  The partials go out as whole rows: each wave writes its block's
+  // normalised fp16 values into its own padded region of the (now idle) ring, then
+  // stores them back 16 contiguous bytes per lane, two rows per wave-wide store.
+  constexpr int SROW = C::ROWB + 16;  // padded row: the 16 rows of a column group hit distinct banks
+  static_assert(CW * 16 * SROW <= S * C::TILE, "staging area");
+  bare_barrier();  // every wave is past its last tile
   if (!computes) return;
+  unsigned char *stage_w = &ring[0][0] + wave * 16 * SROW;
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
     const int blk = rblk0 + NB * wave + k;
     const int row = 16 * blk + ln;
     if (!carry) {
-      // normalised fp16 partial in the MFMA output layout: 512 B per column block
-      unsigned char *po = static_cast<unsigned char *>(T.part_o);
       const float inv_l = 1.0f / st.l[k];
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
-        st_agent(po + part_off<D>(T, h, s, blk, db, lane), norm_half4(st.acc[k][db], inv_l));
+        *reinterpret_cast<uint2 *>(stage_w + ln * SROW + (16 * db + 4 * g) * 2) = norm_half4(st.acc[k][db], inv_l);
       if (g == 0 && row < M) {
         const int64_t prow = (static_cast<int64_t>(h) * T.nsplit_cap + s) * T.rows_cap + row;
-        st_agent(T.part_ml + prow * 2, make_float2(st.m[k], st.l[k]));
+        *reinterpret_cast<float2 *>(T.part_ml + prow * 2) = make_float2(st.m[k], st.l[k]);
       }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // the wave's staged rows are in LDS
+      unsigned char *po = static_cast<unsigned char *>(T.part_o);
+#pragma unroll
+      for (int i = 0; i < 16 * C::CPR / 64; ++i) {
+        const int x = 64 * i + lane, rl = x / C::CPR, cc = x % C::CPR;
+        const uint4 v = *reinterpret_cast<const uint4 *>(stage_w + rl * SROW + cc * 16);
+        if (16 * blk + rl < M) *reinterpret_cast<uint4 *>(po + part_off<D>(T, h, s, 16 * blk + rl, cc * 8)) = v;
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // read back before the next block reuses the region
     } else if (row < M) {
       const int64_t crow = static_cast<int64_t>(h) * T.rows_cap + row;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
-        st_agent(T.carry_acc + crow * D + 16 * db + 4 * g, st.acc[k][db]);
-      if (g == 0) st_agent(T.carry_ml + crow * 2, make_float2(st.m[k], st.l[k]));
+        *reinterpret_cast<floatx4 *>(T.carry_acc + crow * D + 16 * db + 4 * g) = st.acc[k][db];
+      if (g == 0) *reinterpret_cast<float2 *>(T.carry_ml + crow * 2) = make_float2(st.m[k], st.l[k]);
     }
   }
 }
@@ -534,19 +546,24 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
 #pragma unroll
     for (int j = 0; j < QDB; ++j)
       cacc[j] = *reinterpret_cast<const floatx4 *>(T.carry_acc + crow * D + 16 * (qd * QDB + j) + 4 * g);
-    // ---- gather the node's tiles into LDS: committed rows below L, the
-    // ancestors' tree rows, then the node's own row as the filler of masked slots.
-    // Rows are counted from tb0 in 32-bit; lane d of trow_v holds the byte offset of
-    // the tree row at depth d.  A wave-wide load covers RPL rows, whose depths are
-    // uniform, so their tree rows come from readlane.
+    // ---- gather the node's tiles into LDS: committed rows from tb0 below L, then
+    // the ancestors' tree rows up to the node's own (position pos).  Only those rows
+    // are loaded (a wave-wide load covers RPL rows; a part-filled last one takes the
+    // node's own row); the masked value rows past them are zeroed so that their
+    // zero probabilities multiply finite values.  Rows are counted from tb0 in
+    // 32-bit; lane d of trow_v holds the byte offset of the tree row at depth d.  The
+    // RPL rows of a load have uniform depths, so their tree rows come from readlane.
     const int lres = static_cast<int>(L - tb0);  // committed rows in the first tile
+    const int nreal = lres + dep + 1;            // rows tb0 .. pos
     const int trow_v = ((lane <= dep ? anc_v : node) * P.hkv + h) * C::ROWB;
     const unsigned char *kres0 = kc + tb0 * C::ROWB;
     const unsigned char *vres0 = vc + tb0 * C::ROWB;
     const int rr = lane / C::CPR, cs = lane % C::CPR;
     for (int tt = 0; tt < ntree; ++tt) {
-#pragma unroll
-      for (int li = 0; li < C::LOADS / 2; ++li) {
+      const int nl = (min(kKvTile, nreal - kKvTile * tt) + C::RPL - 1) / C::RPL;  // loads per half
+      for (int x = nl * 64 + lane; x < C::LOADS / 2 * 64; x += 64)
+        *reinterpret_cast<uint4 *>(tiles[tt] + C::HALF + 16 * x) = make_uint4(0, 0, 0, 0);
+      for (int li = 0; li < nl; ++li) {
         const int row = li * C::RPL + rr;  // row within the tile
         const int rbase = kKvTile * tt + li * C::RPL;
         int toff = 0;
@@ -640,16 +657,15 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
   Fold8 acc8;
   fold8_empty(acc8);
   float2 mlv[kFoldChunk];
-  uint2 ov0[kFoldChunk], ov1[kFoldChunk];
+  uint4 ov[kFoldChunk];
   auto load_chunk = [&](int c0, int nm) {  // loads past the memory splits repeat the last one
 #pragma unroll
     for (int j = 0; j < kFoldChunk; ++j) {
       const int sj = c0 + max(0, min(j, nm - 1));
       const int64_t prow = (static_cast<int64_t>(h) * T.nsplit_cap + sj) * T.rows_cap + R;
       mlv[j] = *reinterpret_cast<const float2 *>(T.part_ml + prow * 2);
-      const unsigned char *po = static_cast<const unsigned char *>(T.part_o);
-      ov0[j] = *reinterpret_cast<const uint2 *>(po + part_off<D>(T, h, sj, R >> 4, col >> 4, ((col & 15) >> 2) * 16 + (R & 15)));
-      ov1[j] = *reinterpret_cast<const uint2 *>(po + part_off<D>(T, h, sj, R >> 4, col >> 4, (((col & 15) >> 2) + 1) * 16 + (R & 15)));
+      ov[j] = *reinterpret_cast<const uint4 *>(static_cast<const unsigned char *>(T.part_o) +
+                                               part_off<D>(T, h, sj, R, col));
     }
   };
   // fold splits [c0, c0 + ns) of the loaded chunk; index jx (if >= 0) is the
@@ -672,14 +688,14 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) o[e] = x_o[r][8 * co + e];
         } else {
-          o[0] = half_lo(ov0[j].x);
-          o[1] = half_hi(ov0[j].x);
-          o[2] = half_lo(ov0[j].y);
-          o[3] = half_hi(ov0[j].y);
-          o[4] = half_lo(ov1[j].x);
-          o[5] = half_hi(ov1[j].x);
-          o[6] = half_lo(ov1[j].y);
-          o[7] = half_hi(ov1[j].y);
+          o[0] = half_lo(ov[j].x);
+          o[1] = half_hi(ov[j].x);
+          o[2] = half_lo(ov[j].y);
+          o[3] = half_hi(ov[j].y);
+          o[4] = half_lo(ov[j].z);
+          o[5] = half_hi(ov[j].z);
+          o[6] = half_lo(ov[j].w);
+          o[7] = half_hi(ov[j].w);
         }
         ch.l = ch.l + w;
 #pragma unroll

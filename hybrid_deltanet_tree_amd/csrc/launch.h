@@ -22,8 +22,12 @@ constexpr int kKvWaves = 4;        // bf16 attention: waves per tree-pass workgr
 constexpr int kKvThreads = kKvWaves * 64;
 constexpr int kKvStages = 5;       // bf16 attention: LDS tile ring of the split pass
 constexpr int kKvQuarters = 4;     // bf16 attention: output columns split over this many blocks
-constexpr int kGdnThreads = 256;   // 4 waves x 4 value columns x 16 lanes per column
+constexpr int kGdnThreads = 256;   // commit: 4 waves
 constexpr int kGdnCols = 16;       // value columns per GDN workgroup
+// GDN walk: lanes per value column (16: one DPP row; 32 would put two waves on a
+// SIMD, which measured no faster: the per-column reduction work doubles)
+constexpr int kGdnLanes = 16;
+constexpr int gdn_threads(int dk) { return (void)dk, kGdnCols * kGdnLanes; }
 constexpr int kGdnSaves = 8;       // GDN: states kept in LDS for later siblings (branch points)
 constexpr int kFoldThreads = 256;  // 4 waves per output row
 
@@ -99,7 +103,7 @@ struct KvTree {
   const void *kt, *vt;                    // tree rows [n][hkv][D]
   void *kc, *vc;                          // cache of this layer [hkv][cap][D]
   void *o;                                // [n][hq][D]
-  void *part_o;                           // fp16 [hkv][nsplit_cap][rows_cap/16][D/16][64][4] (MFMA layout)
+  void *part_o;                           // fp16 [hkv][nsplit_cap][rows_cap][D]
   float *part_ml;                         // [hkv][nsplit_cap][rows_cap][2]: max (base 2), sum
   float *carry_acc;                       // [hkv][rows_cap][D]
   float *carry_ml;                        // [hkv][rows_cap][2]
