@@ -179,7 +179,8 @@ __device__ __forceinline__ void kv_tile(KvRows<D, NB, NDB> &st, uint32_t tile, c
     va[j] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
                                            lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
   }
-  // ---- online softmax, base 2, lazy max
+  // ---- online softmax, base 2, lazy max.  The running max is taken on the raw
+  // scores (c2 > 0 keeps their order) and each exponent is one fused c2 s - m.
   bf16x8 pb[NB];
   float corr[NB];
   bool any_corr = false;
@@ -191,14 +192,14 @@ __device__ __forceinline__ void kv_tile(KvRows<D, NB, NDB> &st, uint32_t tile, c
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float x = s[b][kb][i] * c2;
+        float x = s[b][kb][i];
         if constexpr (MASK) {
           if (tb + 16 * kb + 4 * g + i > pos) x = -INFINITY;
         }
         z[kb][i] = x;
         mt = fmaxf(mt, x);
       }
-    mt = rows4_max(mt);
+    mt = rows4_max(mt) * c2;
     const bool move = mt > st.m[b] + kLazyMax;  // always true on a row's first tile
     const float mn = move ? mt : st.m[b];
     corr[b] = (move && st.m[b] != -INFINITY) ? exp2_fast(st.m[b] - mn) : 1.0f;
@@ -208,7 +209,7 @@ __device__ __forceinline__ void kv_tile(KvRows<D, NB, NDB> &st, uint32_t tile, c
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const __bf16 e = static_cast<__bf16>(exp2_fast(z[kb][i] - mn));
+        const __bf16 e = static_cast<__bf16>(exp2_fast(fmaf(z[kb][i], c2, -mn)));
         lt = lt + static_cast<float>(e);
         pb[b][4 * kb + i] = e;
       }
@@ -342,13 +343,14 @@ __global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
   const __amdgpu_buffer_rsrc_t kres = make_rsrc(kc, T.L * C::ROWB);
   const __amdgpu_buffer_rsrc_t vres = make_rsrc(vc, T.L * C::ROWB);
 
-  // ---- prologue: the producers load tile 0 while the computing waves load their
-  // query rows straight into registers (rows past the tree's repeat its last row);
-  // the other tiles go out once tile 0 is in, so that every workgroup's first tile
-  // is not queued behind the rest of the burst.
+  // ---- prologue: the producers put tiles 0 .. S - 2 in flight while the computing
+  // waves load their query rows straight into registers (rows past the tree's
+  // repeat its last row); everyone waits for tile 0.
   KvDma<D, NP> dma;
   dma.init(pw);
-  if (producer) dma.issue(ring[0], kres, vres, tile0 * kKvTile);
+  const int first = min(S - 1, ntiles);
+  if (producer)
+    for (int x = 0; x < first; ++x) dma.issue(ring[x], kres, vres, (tile0 + x) * kKvTile);
   KvRows<D, NB, C::DB> st;
   KvLane<D, C::DB> ofs;
   ofs.init(0);
@@ -362,7 +364,16 @@ __global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
       for (int kk = 0; kk < C::KQ; ++kk) st.q[k][kk] = *reinterpret_cast<const bf16x8 *>(qr + (4 * kk + g) * 16);
     }
   }
-  wait_vm<0>();
+  if (producer) {
+    switch (first - 1) {  // tiles 1 .. first - 1 stay in flight
+      case 3: wait_vm<3 * IPW>(); break;
+      case 2: wait_vm<2 * IPW>(); break;
+      case 1: wait_vm<IPW>(); break;
+      default: wait_vm<0>(); break;
+    }
+  } else {
+    wait_vm<0>();  // the query rows
+  }
   bare_barrier();  // tile 0 is in LDS
   st.reset();
   const uint32_t ring0 = lds_addr(ring[0]);
@@ -382,13 +393,8 @@ __global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
       }
       bare_barrier();  // tile tt landed for every wave; tile tt - 1 is no longer read
     }
-    if (producer) {
-      if (tt == 0) {
-        for (int x = 1; x < S && x < ntiles; ++x) dma.issue(ring[x], kres, vres, (tile0 + x) * kKvTile);
-      } else if (tt + S - 1 < ntiles) {
-        dma.issue(ring[stage == 0 ? S - 1 : stage - 1], kres, vres, (tile0 + tt + S - 1) * kKvTile);
-      }
-    }
+    if (producer && tt + S - 1 < ntiles)
+      dma.issue(ring[stage == 0 ? S - 1 : stage - 1], kres, vres, (tile0 + tt + S - 1) * kKvTile);
     if (computes) kv_tile<D, NB, C::DB, false>(st, ring0 + stage * C::TILE, ofs, 0, 0, P.c2);
     stage = stage == S - 1 ? 0 : stage + 1;
   }
