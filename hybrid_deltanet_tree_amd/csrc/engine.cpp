@@ -94,16 +94,26 @@ int64_t pow2_floor(int64_t x) {
   return p;
 }
 
-// Split size of a slot.  It depends on the capacity alone, never on the current
-// length, so a row's fold structure is fixed for the life of the slot.
+// Split size of a slot.  It depends on the capacity (and on the engine's largest
+// tree, for bf16), never on the current length, so a row's fold structure is fixed
+// for the life of the slot.
 //  float32 storage: a power of two between kSplitMin and kSplitMax chosen so that
 //    a full cache gives about kSplitCUs (kv head, split) items;
 //  bf16 storage: the smallest multiple of kKvTile (at least kKvSplitMin) for which
-//    a full cache gives at most kSplitCUs (kv head, split) items, one wave of
-//    workgroups over the chip.
-int32_t split_for(int64_t capacity, int32_t hkv, bool bf16) {
+//    a full cache gives at most kSplitCUs (kv head, split, row group) items, one
+//    wave of workgroups over the chip; row_groups is the number of kKvRowsPerItem-row
+//    groups that the engine's largest tree needs.
+// Row groups of the split pass for the engine's largest tree (bf16 attention).
+int32_t kv_row_groups(const hdt_model_desc &m) {
+  if (m.attn_hkv <= 0) return 1;
+  const int64_t rows = static_cast<int64_t>(m.max_nodes) * (m.attn_hq / m.attn_hkv);
+  return static_cast<int32_t>(std::max<int64_t>(1, (rows + kKvRowsPerItem - 1) / kKvRowsPerItem));
+}
+
+int32_t split_for(int64_t capacity, int32_t hkv, bool bf16, int32_t row_groups) {
   if (bf16) {
-    int64_t s = (capacity * hkv + kSplitCUs - 1) / kSplitCUs;
+    const int64_t per_head = std::max<int64_t>(1, kSplitCUs / (static_cast<int64_t>(hkv) * row_groups));
+    int64_t s = (capacity + per_head - 1) / per_head;
     s = (s + kKvTile - 1) / kKvTile * kKvTile;
     return static_cast<int32_t>(std::max(kKvSplitMin, s));
   }
@@ -243,16 +253,10 @@ hdt_status launch_kv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *trees
   a.hq = m.attn_hq;
   a.hkv = m.attn_hkv;
   a.c2 = m.attn_scale * 1.4426950408889634f;
-  // Split-pass shape: up to 96 rows (6 blocks of 16), 6 waves that compute one
-  // block each beside 2 waves that only issue the tile loads; up to 128 rows, 8
-  // waves that do both; 129..192 rows, 4 waves of three blocks; more, row groups
-  // of 128.
-  int max_blocks = 1;
-  for (int t = 0; t < n_trees; ++t) max_blocks = std::max(max_blocks, (trees[t].n_nodes * G + 15) / 16);
-  const int waves = (max_blocks > 8 && max_blocks <= 12) ? 4 : 8;
-  const int nb = waves == 4 ? 3 : 1;
-  const int pw = max_blocks <= 6 ? 2 : 0;
-  const int cw = waves - pw;
+  // Split-pass shape: 6 waves that compute one 16-row block each beside 2 waves that
+  // only issue the tile loads, kKvRowsPerItem rows per workgroup; a tree with more
+  // rows takes several row groups, placed on one XCD so that they read each tile
+  // through the same L2.
   int32_t items_a = 0, items_b = 0;
   for (int t = 0; t < n_trees; ++t) {
     const hdt_tree &tr = trees[t];
@@ -279,17 +283,17 @@ hdt_status launch_kv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *trees
     x.n_full = static_cast<int32_t>(s.d.length / s.split);
     const int64_t tb0 = s.d.length / kKvTile * kKvTile;
     x.carry_tiles = static_cast<int32_t>((tb0 - static_cast<int64_t>(x.n_full) * s.split) / kKvTile);
-    const int blocks = (tr.n_nodes * G + 15) / 16;
-    x.row_groups = (blocks + cw * nb - 1) / (cw * nb);
-    x.a_per_head = (x.n_full + (x.carry_tiles > 0 ? 1 : 0)) * x.row_groups;
-    items_a = std::max(items_a, m.attn_hkv * x.a_per_head);
+    x.row_groups = (tr.n_nodes * G + kKvRowsPerItem - 1) / kKvRowsPerItem;
+    x.a_splits = x.n_full + (x.carry_tiles > 0 ? 1 : 0);
+    const int pairs = m.attn_hkv * x.a_splits;  // (kv head, split)
+    items_a = std::max(items_a, (pairs + 7) / 8 * 8 * x.row_groups);
     items_b = std::max(items_b, m.attn_hkv * tr.n_nodes * kKvQuarters);
     std::memcpy(x.parent, par[t], kMaxNodes);
     std::memcpy(x.depth, dep[t], kMaxNodes);
   }
   if (items_a > 0) {
     ProfScope p(e, 1);
-    hdt_status st = check_hip(e, launch_kv_split(a, m.attn_d, waves, nb, pw, items_a, stream, p.events()),
+    hdt_status st = check_hip(e, launch_kv_split(a, m.attn_d, items_a, stream, p.events()),
                               "attention split launch");
     if (st != HDT_OK) return st;
   }
@@ -515,7 +519,7 @@ hdt_status hdt_create(const hdt_model_desc *desc, int32_t n_slots, const hdt_slo
   for (int i = 0; i < n_slots; ++i) {
     SlotState &s = e->slots[i];
     s.d = slots[i];
-    s.split = split_for(s.d.capacity, std::max(1, m.attn_hkv), m.io_dtype == HDT_BF16);
+    s.split = split_for(s.d.capacity, std::max(1, m.attn_hkv), m.io_dtype == HDT_BF16, kv_row_groups(m));
     s.nsplit_cap = static_cast<int32_t>((s.d.capacity + s.split - 1) / s.split);
   }
   *out = e;

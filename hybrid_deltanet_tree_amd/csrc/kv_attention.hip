@@ -319,10 +319,15 @@ __global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
   // grid: x = item of the tree, y = tree
   const KvTree &T = P.t[blockIdx.y];
   scalar_touch(&T, sizeof(KvTree), &P.n_trees);
+  // Workgroup x covers (kv head, split) pair p and row group rg: pairs go in runs of
+  // 8, and the row groups of a run follow one another 8 apart, so that the row groups
+  // of one split land on one XCD (workgroups are dealt to the 8 XCDs in turn) and
+  // read its tiles through one L2.
   const int local = blockIdx.x;
-  if (local >= P.hkv * T.a_per_head) return;
-  const int h = local / T.a_per_head, r = local % T.a_per_head;
-  const int rg = r % T.row_groups, s = r / T.row_groups;
+  const int run = local / (8 * T.row_groups), rem = local % (8 * T.row_groups);
+  const int rg = rem / 8, pair = run * 8 + rem % 8;
+  if (pair >= P.hkv * T.a_splits) return;
+  const int h = pair / T.a_splits, s = pair % T.a_splits;
   const bool carry = s == T.n_full;  // the tiles of split n_full below tb0
   const int G = P.hq / P.hkv;
   const int M = T.n * G;
@@ -780,25 +785,16 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
 
 }  // namespace
 
-hipError_t launch_kv_split(const KvLaunch &a, int D, int waves, int nb, int pw, int max_items, hipStream_t s,
-                           KernelEvents ev) {
+hipError_t launch_kv_split(const KvLaunch &a, int D, int max_items, hipStream_t s, KernelEvents ev) {
   const dim3 grid(max_items, a.n_trees);
-#define HDT_KV_SPLIT(DD, W, NB, PW)                                                                         \
-  hipExtLaunchKernelGGL((kv_split_kernel<DD, W, NB, PW>), grid, dim3(W * 64), 0, s, ev.start, ev.stop, 0, a)
+  static_assert(kKvRowsPerItem == 6 * 16, "six computing waves of one block");
   if (D == 256) {
-    if (waves == 8 && nb == 1 && pw == 2) HDT_KV_SPLIT(256, 8, 1, 2);
-    else if (waves == 8 && nb == 1 && pw == 0) HDT_KV_SPLIT(256, 8, 1, 0);
-    else if (waves == 4 && nb == 3 && pw == 0) HDT_KV_SPLIT(256, 4, 3, 0);
-    else return hipErrorInvalidValue;
+    hipExtLaunchKernelGGL((kv_split_kernel<256, 8, 1, 2>), grid, dim3(8 * 64), 0, s, ev.start, ev.stop, 0, a);
   } else if (D == 64) {
-    if (waves == 8 && nb == 1 && pw == 2) HDT_KV_SPLIT(64, 8, 1, 2);
-    else if (waves == 8 && nb == 1 && pw == 0) HDT_KV_SPLIT(64, 8, 1, 0);
-    else if (waves == 4 && nb == 3 && pw == 0) HDT_KV_SPLIT(64, 4, 3, 0);
-    else return hipErrorInvalidValue;
+    hipExtLaunchKernelGGL((kv_split_kernel<64, 8, 1, 2>), grid, dim3(8 * 64), 0, s, ev.start, ev.stop, 0, a);
   } else {
     return hipErrorInvalidValue;
   }
-#undef HDT_KV_SPLIT
   return hipGetLastError();
 }
 

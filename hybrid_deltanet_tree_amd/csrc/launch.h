@@ -20,6 +20,7 @@ constexpr int kAttnThreads = kAttnWaves * 64;
 constexpr int kKvTile = 32;        // bf16 attention: keys per tile, anchored at absolute positions
 constexpr int kKvWaves = 4;        // bf16 attention: waves per tree-pass workgroup, one per SIMD
 constexpr int kKvThreads = kKvWaves * 64;
+constexpr int kKvRowsPerItem = 96; // bf16 attention: query rows per split-pass workgroup (6 blocks of 16)
 constexpr int kKvStages = 5;       // bf16 attention: LDS tile ring of the split pass
 constexpr int kKvQuarters = 4;     // bf16 attention: output columns split over this many blocks
 constexpr int kGdnThreads = 256;   // commit: 4 waves
@@ -113,8 +114,8 @@ struct KvTree {
   int32_t nsplit_cap, rows_cap;
   int32_t n_full;                         // splits wholly below L
   int32_t carry_tiles;                    // tiles of split n_full below tb0
-  int32_t row_groups;                     // split-pass items per split (row blocks / blocks per item)
-  int32_t a_per_head;                     // split pass: items per kv head
+  int32_t row_groups;                     // split pass: row groups of kKvRowsPerItem rows
+  int32_t a_splits;                       // split pass: splits per kv head (n_full, + 1 with a carry)
   alignas(4) int8_t parent[kMaxNodes];    // read as 32-bit words
   alignas(4) int8_t depth[kMaxNodes];
 };
@@ -172,7 +173,7 @@ hipError_t launch_attn_split(const AttnLaunch &a, int D, int bf16, int n_blocks,
 hipError_t launch_attn_fold(const FoldLaunch &a, int D, int bf16, int n_blocks, hipStream_t s,
                             KernelEvents ev);
 // Split pass with `waves` waves of `nb` 16-row blocks each: (8, 1) or (4, 3).
-hipError_t launch_kv_split(const KvLaunch &a, int D, int waves, int nb, int pw, int max_items, hipStream_t s,
+hipError_t launch_kv_split(const KvLaunch &a, int D, int max_items, hipStream_t s,
                            KernelEvents ev);
 hipError_t launch_kv_tree(const KvLaunch &a, int D, int max_items, hipStream_t s, KernelEvents ev);
 hipError_t launch_commit(const CommitLaunch &a, int dk, int bf16, int n_blocks, hipStream_t s,

@@ -206,8 +206,10 @@ hdt_status hdt_tree_meta(int32_t n, const int32_t *parent, int64_t L, int32_t *d
 /*
  * Attention split size of a slot: the resident keys are cut into splits of this
  * many positions anchored at position 0, each reduced on its own and folded in
- * ascending order.  It depends only on the slot's capacity, so a row's bits
- * depend only on its inputs.  Errors: HDT_E_INVALID.
+ * ascending order.  It depends only on the slot's capacity and, for bf16 storage,
+ * on the engine's max_nodes (a tree of more than 96 query rows per kv head takes
+ * several row groups per split), all fixed at create, so a row's bits depend only
+ * on its inputs.  Errors: HDT_E_INVALID.
  */
 hdt_status hdt_split_size(const hdt_engine *eng, int32_t slot, int64_t *out);
 

@@ -133,7 +133,8 @@ def test_sequencing_rules_without_pending_round():
 
 def test_split_size_depends_on_capacity_only():
     # bf16 storage: the smallest multiple of 32 keys (at least 128) for which a full
-    # cache gives at most 256 (kv head, split) items; float32: a power of two.
+    # cache gives at most 256 (kv head, split, row group) items, a row group being 96
+    # query rows of the engine's largest tree; float32: a power of two.
     e = make_engine()
     assert e.split_size(0) == 128 and e.split_size(1) == 128
     big = [dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=65536 + 1024, length=65536),
@@ -149,6 +150,14 @@ def test_split_size_depends_on_capacity_only():
             assert s % 32 == 0 and s >= 128
             assert hkv * -(-cap // s) <= 256 or s == 128
             assert s == 128 or hkv * -(-cap // (s - 32)) > 256
+    # 32-node trees at 6 q heads per kv head: 192 rows, two row groups per split
+    e3 = make_engine(attn_hkv=4, attn_hq=24, attn_d=256, max_nodes=32, slots=big)
+    assert e3.split_size(0) == 2080 and e3.split_size(1) == 8224
+    for mn in (1, 16, 17, 33, 64):
+        rg = -(-(mn * 6) // 96)
+        s = make_engine(attn_hkv=4, attn_hq=24, attn_d=256, max_nodes=mn, slots=big[1:]).split_size(0)
+        assert s % 32 == 0 and 4 * rg * -(-(262144 + 1024) // s) <= 256
+        assert 4 * rg * -(-(262144 + 1024) // (s - 32)) > 256
     f32 = make_engine(io_dtype=hdt.HDT_F32, slots=big[:1])
     assert f32.split_size(0) == 512
     f32b = make_engine(io_dtype=hdt.HDT_F32, attn_hkv=4, attn_hq=8, slots=big)

@@ -32,6 +32,9 @@ W = synth.WORKLOADS
 # Small bf16 workload with the 27B-like head shapes: 2 GDN + 2 attention layers.
 MINI = synth.Workload("mini", [0, 1, 0, 1], 16, 32, 128, 128, 24, 4, 256, "bf16", [1000], 16,
                       "draft")
+# 20-node trees at 6 q heads per kv head: 120 query rows, two row groups per split
+RG2 = synth.Workload("rg2", [0, 1, 0, 1], 16, 32, 128, 128, 24, 4, 256, "bf16", [1300], 20,
+                     "draft")
 
 
 def run_verify(inst, eng, slots=None):
@@ -49,6 +52,19 @@ def test_forward_matches_oracle(wname, L):
     run_verify(inst, eng)
     got = gu.outputs(inst, 0)
     for l in range(len(inst.w.layer_kind)):
+        gu.check_layer(inst, 0, l, got[l])
+
+
+@pytest.mark.parametrize("L", [1300, 2017])
+def test_two_row_groups_match_oracle(L):
+    """More than 96 query rows per kv head: the split pass runs two row groups per split
+    (on one XCD), with the split size scaled to keep one wave of workgroups."""
+    inst = Instance(RG2, SEED, lengths=[L])
+    eng = inst.engine(max_nodes=20)
+    assert eng.split_size(0) % 32 == 0
+    run_verify(inst, eng)
+    got = gu.outputs(inst, 0)
+    for l in range(len(RG2.layer_kind)):
         gu.check_layer(inst, 0, l, got[l])
 
 
@@ -125,9 +141,10 @@ def decode_rows_along(inst, eng, node, s=0):
 
 
 @pytest.mark.parametrize("wname,L,tree", [("tiny", 256, "chain"), ("tiny", 250, "random"),
-                                          ("mini", 1000, "draft"), ("mini", 1275, "draft")])
+                                          ("mini", 1000, "draft"), ("mini", 1275, "draft"),
+                                          ("rg2", 1300, "draft")])
 def test_verify_row_equals_decode_row(wname, L, tree):
-    w = MINI if wname == "mini" else W[wname]
+    w = {"mini": MINI, "rg2": RG2}.get(wname) or W[wname]
     parent = synth.chain_tree(8) if tree == "chain" else w.tree(SEED + L)
     inst = Instance(w, SEED, lengths=[L], trees=[parent])
     eng = inst.engine(max_nodes=len(parent))
