@@ -579,6 +579,13 @@ hdt_status hdt_forward_tree(hdt_engine *e, int32_t n_trees, const hdt_tree *tree
                     t, l);
     }
   }
+  if (!e->allocated) {
+    // the scratch is allocated by the first forward, which must not be captured
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) != hipSuccess ||
+        cs != hipStreamCaptureStatusNone)
+      return fail(e, HDT_E_ORDER, "the first forward allocates scratch: run it outside graph capture");
+  }
   hdt_status st = ensure_alloc(e);
   if (st != HDT_OK) return st;
   {

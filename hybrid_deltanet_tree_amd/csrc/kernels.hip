@@ -1079,8 +1079,14 @@ __global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch 
 
 template <typename K>
 hipError_t set_lds(K kernel, size_t bytes) {
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+  // Raised once per kernel to the largest dynamic LDS any launch asks for (the whole
+  // 160 KiB), at the first launch: later launches, graph capture included, then make
+  // no attribute call.
+  static const hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     kMaxDynamicLds);
+  (void)bytes;
+  return once;
 }
 
 }  // namespace

@@ -20,6 +20,7 @@ constexpr int kAttnThreads = kAttnWaves * 64;
 constexpr int kKvTile = 32;        // bf16 attention: keys per tile, anchored at absolute positions
 constexpr int kKvWaves = 4;        // bf16 attention: waves per tree-pass workgroup, one per SIMD
 constexpr int kKvThreads = kKvWaves * 64;
+constexpr int kMaxDynamicLds = 160 * 1024;  // gfx950 LDS per workgroup
 constexpr int kKvRowsPerItem = 96; // bf16 attention: query rows per split-pass workgroup (6 blocks of 16)
 constexpr int kKvStages = 5;       // bf16 attention: LDS tile ring of the split pass
 constexpr int kKvQuarters = 4;     // bf16 attention: output columns split over this many blocks

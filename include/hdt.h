@@ -155,6 +155,10 @@ void hdt_destroy(hdt_engine *eng);
  * Afterwards each slot has a pending round.  Several trees in one call give
  * every row the same bits as verifying each tree alone ("Parallel requests",
  * "On Flash-Next": the joint pass equals each lone verify bit for bit).
+ * The call enqueues kernels only (no allocation, copy or fill once the engine's
+ * scratch exists), so it may be captured into a HIP graph and replayed; a replay
+ * repeats this round's pass at the same lengths.  The first launching call
+ * allocates the scratch and must not be captured (HDT_E_ORDER).
  * Errors: HDT_E_INVALID, HDT_E_TREE, HDT_E_CAPACITY, HDT_E_ORDER, HDT_E_HIP.
  */
 hdt_status hdt_forward_tree(hdt_engine *eng, int32_t n_trees, const hdt_tree *trees,
