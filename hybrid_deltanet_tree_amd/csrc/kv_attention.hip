@@ -151,9 +151,12 @@ __device__ __forceinline__ void kv_tile(KvRows<D, NB, NDB> &st, uint32_t tile, c
     ka[1][kk] = *(lds_b8)(lds_ptr(a + KB1));
   }
   __builtin_amdgcn_sched_barrier(0);
-  floatx4 s[NB][2];
+  // Even and odd k-steps accumulate separately (four independent MFMA chains per
+  // block instead of two: one wave cannot issue a dependent MFMA until the previous
+  // one is done), then the two halves are added.
+  floatx4 s[NB][2], s2[NB][2];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) s[b][0] = s[b][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < NB; ++b) s[b][0] = s[b][1] = s2[b][0] = s2[b][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < KQ; ++kk) {
     if (kk + KPRE < KQ) {
@@ -164,9 +167,17 @@ __device__ __forceinline__ void kv_tile(KvRows<D, NB, NDB> &st, uint32_t tile, c
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-        s[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][kk], st.q[b][kk], s[b][kb], 0, 0, 0);
+      for (int b = 0; b < NB; ++b) {
+        if (kk & 1)
+          s2[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][kk], st.q[b][kk], s2[b][kb], 0, 0, 0);
+        else
+          s[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][kk], st.q[b][kk], s[b][kb], 0, 0, 0);
+      }
   }
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s[b][kb] = s[b][kb] + s2[b][kb];
   // ---- value operands for O^T += V^T P^T.  The transposed read gives lane (g, m)
   // the values of keys 4 g + e (lo) and 16 + 4 g + e (hi), e = 0..3, at column
   // 16 db + m: the same key order as the probabilities below.
@@ -204,14 +215,19 @@ __device__ __forceinline__ void kv_tile(KvRows<D, NB, NDB> &st, uint32_t tile, c
     const float mn = move ? mt : st.m[b];
     corr[b] = (move && st.m[b] != -INFINITY) ? exp2_fast(st.m[b] - mn) : 1.0f;
     any_corr = any_corr || corr[b] != 1.0f;
+    // probabilities rounded to bf16 in pairs; the row sum adds those rounded values
+    // two at a time (a bf16 dot product with (1, 1), accumulated in float32)
     float lt = 0.0f;
+    const bf16x2 ones2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const __bf16 e = static_cast<__bf16>(exp2_fast(fmaf(z[kb][i], c2, -mn)));
-        lt = lt + static_cast<float>(e);
-        pb[b][4 * kb + i] = e;
+      for (int i = 0; i < 4; i += 2) {
+        const floatx2 e = {exp2_fast(fmaf(z[kb][i], c2, -mn)), exp2_fast(fmaf(z[kb][i + 1], c2, -mn))};
+        const bf16x2 pp = __builtin_convertvector(e, bf16x2);
+        lt = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, lt, false);
+        pb[b][4 * kb + i] = pp[0];
+        pb[b][4 * kb + i + 1] = pp[1];
       }
     lt = rows4_sum(lt);
     st.l[b] = st.l[b] * corr[b] + lt;
