@@ -172,26 +172,32 @@ def main():
     import hybrid_deltanet_tree_amd as hdt
 
     w = synth.WORKLOADS[args.workload]
-    if w.n_slots != 1:
-        raise SystemExit("bench.py times single-slot workloads; joint workloads are parity cases")
+    ns = w.n_slots  # several slots: one joint pass over every slot's tree
     L0 = w.lengths[0]
-    parent = w.tree(args.seed, 0)
+    parents = [w.tree(args.seed, s) for s in range(ns)]
+    parent = parents[0]
     n = len(parent)
-    path = synth.accepted_path(args.seed, f"{w.name}/bench-path", parent)
+    paths = [synth.accepted_path(args.seed, f"{w.name}/bench-path" + (f"/{s}" if s else ""), parents[s])
+             for s in range(ns)]
+    path = paths[0]
     steps_total = args.warmup + 2 * args.steps
-    cap = L0 + steps_total * len(path) + 64
+    caps = [w.lengths[s] + steps_total * len(paths[s]) + 64 for s in range(ns)]
     t_setup = time.perf_counter()
-    inst = Instance(w, args.seed, lengths=[L0], trees=[parent], capacity=[cap], keep_host=False)
-    eng = inst.engine(max_nodes=n)
+    inst = Instance(w, args.seed, lengths=list(w.lengths), trees=parents, capacity=caps, keep_host=False)
+    eng = inst.engine(max_nodes=max(len(p) for p in parents))
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    tree = [inst.tree_arg(0)]
+    tree = [inst.tree_arg(s) for s in range(ns)]
+
+    def lens():
+        return [eng.kv_length(s) for s in range(ns)]
 
     def step():
         eng.forward_tree(tree, sp)
-        eng.commit_tree(0, path, sp)
+        for s in range(ns):
+            eng.commit_tree(s, paths[s], sp)
 
     for _ in range(args.warmup):
         step()
@@ -204,11 +210,12 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        lengths.append(eng.kv_length(0))
+        lengths.append(lens())
         ev[i][0].record(stream)
         eng.forward_tree(tree, sp)
         ev[i][1].record(stream)
-        eng.commit_tree(0, path, sp)
+        for s in range(ns):
+            eng.commit_tree(s, paths[s], sp)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     verify_ms = [a.elapsed_time(b) for a, b in ev]
@@ -217,7 +224,7 @@ def main():
     # ---- the same pass captured as one HIP graph and replayed at a fixed length:
     # forward_tree enqueues only kernels, and a replay repeats the round's pass
     graph_ms = []
-    L_graph = eng.kv_length(0)
+    L_graph = lens()
     if not args.no_graph:
         g = torch.cuda.CUDAGraph()
         torch.cuda.synchronize()
@@ -234,13 +241,14 @@ def main():
             b.record(stream)
         torch.cuda.synchronize()
         graph_ms = [a.elapsed_time(b) for a, b in gev]
-        eng.rollback_to(0, eng.kv_length(0), sp)
+        for s in range(ns):
+            eng.rollback_to(s, eng.kv_length(s), sp)
         del g
 
     # ---- per-kernel HIP events (library-recorded, on the launch stream) over K more steps
     eng.profile(True)
     for i in range(args.steps):
-        lengths.append(eng.kv_length(0))
+        lengths.append(lens())
         step()
     prof = {k: eng.profile_read(k) for k in (0, 1, 2, 3)}
     eng.profile(False)
@@ -249,10 +257,17 @@ def main():
     eager_med = statistics.median(verify_ms)
     times = graph_ms if graph_ms else verify_ms
     med = statistics.median(times)
-    Lm = sum(lengths) / len(lengths)
-    attn_b, gdn_b, split_b = algorithmic_bytes(w, Lm, n)
-    attn_g, gdn_g, _ = algorithmic_bytes(w, L_graph, n)
-    verify_bytes = (w.n_attn * attn_g + w.n_gdn * gdn_g) if graph_ms else (w.n_attn * attn_b + w.n_gdn * gdn_b)
+    def pass_bytes(Ls):
+        """(whole-pass bytes, split-pass bytes per launch) summed over the slots."""
+        tot = spl = 0
+        for s, L in enumerate(Ls):
+            a_b, g_b, s_b = algorithmic_bytes(w, L, len(parents[s]))
+            tot += w.n_attn * a_b + w.n_gdn * g_b
+            spl += s_b
+        return tot, spl
+    Lm = [sum(x[s] for x in lengths) / len(lengths) for s in range(ns)]
+    eager_bytes, split_b = pass_bytes(Lm)
+    verify_bytes = pass_bytes(L_graph)[0] if graph_ms else eager_bytes
     ms_split, cnt_split = prof[1]
     avg_split_ms = ms_split / max(1, cnt_split)
     achieved = split_b / (avg_split_ms * 1e-3) / 1e9
@@ -281,8 +296,12 @@ def main():
         "dtype": "bf16",
         "data": "synthetic: seeded counter-based inputs (SplitMix64, Box-Muller); projections "
                 "and weights excluded",
-        "config": {"workload": f"{w.name}: {w.n_gdn} GDN + {w.n_attn} attention layers (3:1), "
-                               f"{L0} resident tokens, {n}-node draft tree, commit of {len(path)}",
+        "config": {"workload": (f"{w.name}: {w.n_gdn} GDN + {w.n_attn} attention layers (3:1), "
+                                f"{L0} resident tokens, {n}-node draft tree, commit of {len(path)}")
+                   if ns == 1 else
+                               (f"{w.name}: {w.n_gdn} GDN + {w.n_attn} attention layers (3:1), one joint "
+                                f"pass over {ns} slots of {', '.join(str(x) for x in w.lengths)} resident "
+                                f"tokens, a {n}-node draft tree each, then per-slot commits"),
                    "gdn": f"{w.gdn_hk} qk / {w.gdn_hv} v heads, dk=dv={w.gdn_dk}, fp32 state",
                    "attention": f"{w.attn_hq} q / {w.attn_hkv} kv heads, D={w.attn_d}, bf16 KV",
                    "parallelism": "single GPU"},
@@ -292,14 +311,15 @@ def main():
                    "eager_median_ms": round(eager_med, 4),
                    "algorithmic_bytes": int(verify_bytes), "achieved_gbps": round(verify_gbps, 1),
                    "frac_of_peak": round(verify_gbps / PEAK_HBM_GBS, 4),
-                   "context": L_graph if graph_ms else round(Lm, 1)},
+                   "context": (L_graph if graph_ms else [round(x, 1) for x in Lm]) if ns > 1
+                   else (L_graph[0] if graph_ms else round(Lm[0], 1))},
         "kernels": kernels,
         "roofline": {"bound": "hbm", "kernel": SPLIT_KERNEL, "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": int(split_b)},
         "setup_s": round(t_setup, 1),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and ns == 1:
         out["cpu_baseline"] = cpu_baseline(w, args.seed, L0, parent)
     eng.close()
     print(json.dumps(out))
