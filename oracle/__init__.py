@@ -14,11 +14,18 @@ layer: architecture registry and per-model state"), and the round of "One
 request, end to end" (section 2.6, "The decode loop").  The Gated DeltaNet
 step is the published recurrence (Yang, Kautz, Hatamizadeh, ICLR 2025).
 
+The short causal convolution in front of a GDN layer (``gdn_conv``, the gdn.conv
+state section of "Adding a model", "The model layer: architecture registry and
+per-model state") is the published Gated DeltaNet block's depthwise conv + SiLU +
+q/k L2 norm, taken along each node's root path with the slot's committed tail
+before the root; ``conv_tail_commit`` is its commit.
+
 Pins (tests that tie this oracle to something other than itself) live in
 ``tests/test_oracle_pins.py``: hand-worked examples in ``tests/golden/``,
 closed forms, a float64 brute force written in a different formulation
 (matrix form of the recurrence per root path; dense softmax over an explicit
-mask), and library softmax attention.
+mask), library softmax attention, library depthwise conv1d (chains, and every
+root path of a tree), and torch's bfloat16 conversion for ``to_storage``.
 """
 from __future__ import annotations
 
@@ -65,6 +72,9 @@ def configure(lib):
     lib.orc_attn_tree.restype = None
     lib.orc_attn_tree.argtypes = [_I, _I, _I, _I, _P, _I64, _I64, _P, _P, _P, _P, _P, _I,
                                   _F, _P]
+    lib.orc_gdn_conv.restype = None
+    lib.orc_gdn_conv.argtypes = [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _F, _P,
+                                 _P, _P]
     return lib
 
 
@@ -206,3 +216,65 @@ def rollback_plan(parent, L: int, n: int):
     if L < n <= L + c:
         return list(range(n - L))
     return None
+
+
+CONV_EPS = 1e-6  # L2-norm epsilon of the published Gated DeltaNet q/k normalisation
+
+
+def gdn_conv(parent, tail, q, k, v, W, eps=CONV_EPS):
+    """Short causal conv + SiLU (+ per-head L2 norm of q and k) of one GDN layer over a
+    tree.  tail [w-1][C] committed pre-conv inputs (row w-2 newest); q,k [n][hk][dk],
+    v [n][hv][dv] pre-conv inputs; W [C][w] float32, C = 2 hk dk + hv dv (q, k, v
+    channels in that order).  Returns float32 (q', k', v') of the input shapes."""
+    par = np.asarray(parent, dtype=np.int32)
+    n, hk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    W = _c(np.asarray(W, dtype=np.float32))
+    w = W.shape[1]
+    C = 2 * hk * dk + hv * dv
+    assert W.shape == (C, w)
+    if tail is None or w == 1:
+        tail = np.zeros((max(w - 1, 1), C), q.dtype)
+    assert tail.shape[1] == C
+    dt = _dtype_code(tail, q, k, v)
+    tail, q, k, v = map(_c, (tail, q, k, v))
+    qo = np.zeros((n, hk, dk), np.float32)
+    ko = np.zeros((n, hk, dk), np.float32)
+    vo = np.zeros((n, hv, dv), np.float32)
+    _load().orc_gdn_conv(hk, dk, hv, dv, w, n, par.ctypes.data, tail.ctypes.data, q.ctypes.data,
+                         k.ctypes.data, v.ctypes.data, W.ctypes.data, dt, eps, qo.ctypes.data,
+                         ko.ctypes.data, vo.ctypes.data)
+    return qo, ko, vo
+
+
+def conv_rows(q, k, v) -> np.ndarray:
+    """Pre-conv inputs of each node as one channel row: [n][C] = q | k | v."""
+    n = q.shape[0]
+    return np.concatenate([q.reshape(n, -1), k.reshape(n, -1), v.reshape(n, -1)], axis=1)
+
+
+def conv_tail_commit(tail: np.ndarray, q, k, v, path) -> np.ndarray:
+    """Conv tail after commit_tree(path): the last w-1 rows of the committed tail followed
+    by the path's pre-conv input rows (bit copies).  tail [w-1][C] -> [w-1][C]."""
+    rows = conv_rows(q, k, v)[np.asarray(path, dtype=np.int64)]
+    seq = np.concatenate([tail, rows.astype(tail.dtype, copy=False)], axis=0)
+    return np.ascontiguousarray(seq[len(seq) - tail.shape[0]:])
+
+
+def to_storage(x: np.ndarray, like: np.ndarray) -> np.ndarray:
+    """float32 values in the storage dtype of `like`: unchanged for float32, else bfloat16
+    bit patterns rounded to nearest even (NaN is not expected here)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if like.dtype == np.float32:
+        return x
+    b = x.view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def gdn_conv_layer(parent, S_base, tail, q, k, v, alpha, beta, W, scale=None, want_states=False):
+    """A GDN layer whose q, k, v arrive before the short conv: gdn_conv, its outputs stored
+    in the input dtype (as the layer's activations are), then gdn_tree.  Returns what
+    gdn_tree returns, plus the stored post-conv (q', k', v')."""
+    qc, kc, vc = (to_storage(x, q) for x in gdn_conv(parent, tail, q, k, v, W))
+    out = gdn_tree(parent, S_base, qc, kc, vc, alpha, beta, scale=scale, want_states=want_states)
+    return out, (qc, kc, vc)

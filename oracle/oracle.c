@@ -256,3 +256,71 @@ void orc_attn_tree(int hq, int hkv, int D, int n, const int32_t *parent, int64_t
       orc_attn_row(hq, hkv, D, n, parent, L, cap, Kc, Vc, q, kt, vt, dtype, scale, i, j,
                    o + ((size_t)i * hq + j) * D);
 }
+
+/*
+ * Short causal convolution of a Gated DeltaNet layer over a tree (the gdn.conv
+ * state section of "Adding a model", "The model layer: architecture registry
+ * and per-model state": the conv tails kept beside the recurrent state).  The
+ * layer's q, k, v channels pass through a depthwise causal convolution of width
+ * w along the token axis, then SiLU, and q and k are L2-normalised per head
+ * (the published Gated DeltaNet block; the pages name only the section).  Along
+ * a tree, the inputs a node sees are those of its root path: its own, its
+ * ancestors', and before the root the slot's committed tail.
+ *
+ * Channel space (C = 2 hk dk + hv dv channels): q channels (head-major), then k,
+ * then v.  For node i at depth d and channel c:
+ *   x(r) = input of the ancestor-or-self r steps above i  for 0 <= r <= d,
+ *          tail[(w-1) - (r - d)][c]                        for r > d
+ *   acc  = sum_{j=0}^{w-1} W[c][j] * x(w-1-j)   (ascending j; tap w-1 is the node)
+ *   y    = acc / (1 + exp(-acc))                (SiLU)
+ * and for every q or k head, y <- y / sqrt(sum_a y_a^2 + eps), the sum ascending.
+ *   W [C][w] float32; tail [w-1][C] (row w-2 is the newest committed input);
+ *   q,k [n][hk][dk], v [n][hv][dv] pre-conv inputs; outputs float32, same shapes.
+ */
+void orc_gdn_conv(int hk, int dk, int hv, int dv, int w, int n, const int32_t *parent,
+                  const void *tail, const void *q, const void *k, const void *v,
+                  const float *W, int dtype, float eps, float *qo, float *ko, float *vo) {
+  const int64_t CQ = (int64_t)hk * dk, C = 2 * CQ + (int64_t)hv * dv;
+  int32_t path[ORC_MAX_NODES];
+  for (int i = 0; i < n; ++i) {
+    int d = 0;
+    for (int x = i; x >= 0; x = parent[x]) ++d;
+    for (int x = i, p = d - 1; x >= 0; x = parent[x], --p) path[p] = x;  /* root..i */
+    d -= 1;                                                               /* depth of i */
+    for (int64_t c = 0; c < C; ++c) {
+      float acc = 0.0f;
+      for (int j = 0; j < w; ++j) {
+        const int r = w - 1 - j;  /* steps above node i */
+        float xin;
+        if (r <= d) {
+          const int node = path[d - r];
+          if (c < CQ)
+            xin = ld(q, dtype, (int64_t)node * CQ + c);
+          else if (c < 2 * CQ)
+            xin = ld(k, dtype, (int64_t)node * CQ + (c - CQ));
+          else
+            xin = ld(v, dtype, (int64_t)node * hv * dv + (c - 2 * CQ));
+        } else {
+          xin = ld(tail, dtype, (int64_t)((w - 1) - (r - d)) * C + c);
+        }
+        acc = acc + W[c * w + j] * xin;
+      }
+      const float y = acc / (1.0f + expf(-acc));
+      if (c < CQ)
+        qo[(int64_t)i * CQ + c] = y;
+      else if (c < 2 * CQ)
+        ko[(int64_t)i * CQ + (c - CQ)] = y;
+      else
+        vo[(int64_t)i * hv * dv + (c - 2 * CQ)] = y;
+    }
+    for (int which = 0; which < 2; ++which) {
+      float *base = (which == 0 ? qo : ko) + (int64_t)i * CQ;
+      for (int g = 0; g < hk; ++g) {
+        float ss = 0.0f;
+        for (int a = 0; a < dk; ++a) ss = ss + base[g * dk + a] * base[g * dk + a];
+        const float inv = 1.0f / sqrtf(ss + eps);
+        for (int a = 0; a < dk; ++a) base[g * dk + a] = base[g * dk + a] * inv;
+      }
+    }
+  }
+}

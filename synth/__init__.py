@@ -297,3 +297,45 @@ def kv_rows(w: Workload, seed: int, slot: int, layer: int, head: int, row0: int,
     V = fill(seed, base + "/V", NORMAL, (row0 + rows, w.attn_d), dtype=w.dtype, row0=row0,
              rows=rows)
     return K, V
+
+
+# --------------------------------------------------------------------------------------------
+# Short causal convolution of the GDN layers (pre-conv inputs, taps, committed tails)
+# --------------------------------------------------------------------------------------------
+
+def conv_channels(w: Workload) -> int:
+    """Channels of one token through the conv: q (hk dk), k (hk dk), v (hv dv)."""
+    return 2 * w.gdn_hk * w.gdn_dk + w.gdn_hv * w.gdn_dv
+
+
+def conv_width(w: Workload) -> int:
+    return int(w.extra.get("conv", 0))
+
+
+def conv_inputs(w: Workload, seed: int, slot: int, layer: int, n: int, tag: str = "verify"):
+    """Pre-conv q, k [n][hk][dk], v [n][hv][dv] (projection outputs, N(0,1)) and the gates
+    alpha, beta [n][hv], in the storage dtype."""
+    base = f"{w.name}/s{slot}/l{layer}/{tag}/conv"
+    dt = w.dtype
+    q = fill(seed, base + "/q", NORMAL, (n, w.gdn_hk, w.gdn_dk), dtype=dt)
+    k = fill(seed, base + "/k", NORMAL, (n, w.gdn_hk, w.gdn_dk), dtype=dt)
+    v = fill(seed, base + "/v", NORMAL, (n, w.gdn_hv, w.gdn_dv), dtype=dt)
+    a = fill(seed, base + "/alpha", EXP_NEG_SOFTPLUS, (n, w.gdn_hv), dtype=dt)
+    b = fill(seed, base + "/beta", SIGMOID, (n, w.gdn_hv), dtype=dt)
+    return q, k, v, a, b
+
+
+def conv_weight(w: Workload, seed: int, layer: int) -> np.ndarray:
+    """Depthwise taps of one GDN layer, float32 [C][width], N(0, 1/width): a conv output
+    over N(0,1) inputs has unit variance."""
+    width = conv_width(w)
+    return fill(seed, f"{w.name}/l{layer}/conv_w", NORMAL, (conv_channels(w), width),
+                dtype="f32", scale=float(np.sqrt(1.0 / width)))
+
+
+def conv_tail(w: Workload, seed: int, slot: int, layer: int) -> np.ndarray:
+    """Committed pre-conv inputs of the last width-1 tokens, [width-1][C] (row width-2 is
+    the newest), in the storage dtype."""
+    width = conv_width(w)
+    return fill(seed, f"{w.name}/s{slot}/l{layer}/conv_tail", NORMAL,
+                (max(width - 1, 1), conv_channels(w)), dtype=w.dtype)[:width - 1]

@@ -39,6 +39,18 @@ MUTANTS = {
                           "mask[i] = ((p < 0) ? 0 : mask[p]);"),
     "softmax_unnormalised": ("for (int d = 0; d < D; ++d) o[d] = o[d] / l;",
                              "for (int d = 0; d < D; ++d) o[d] = o[d];"),
+    "conv_taps_reversed": ("acc = acc + W[c * w + j] * xin;",
+                           "acc = acc + W[c * w + (w - 1 - j)] * xin;"),
+    "conv_tail_rows_reversed": ("xin = ld(tail, dtype, (int64_t)((w - 1) - (r - d)) * C + c);",
+                                "xin = ld(tail, dtype, (int64_t)((r - d) - 1) * C + c);"),
+    "conv_path_from_root": ("const int node = path[d - r];", "const int node = path[r];"),
+    "conv_silu_sign": ("const float y = acc / (1.0f + expf(-acc));",
+                       "const float y = acc / (1.0f + expf(acc));"),
+    "conv_no_activation": ("const float y = acc / (1.0f + expf(-acc));",
+                           "const float y = acc;"),
+    "conv_norm_dropped": ("const float inv = 1.0f / sqrtf(ss + eps);", "const float inv = 1.0f;"),
+    "conv_k_channels_shifted": ("xin = ld(k, dtype, (int64_t)node * CQ + (c - CQ));",
+                                "xin = ld(q, dtype, (int64_t)node * CQ + (c - CQ));"),
 }
 
 

@@ -260,6 +260,114 @@ def pin_commit_and_rollback_rules():
     assert rows.shape == (2, 3, 3) and np.array_equal(rows[1, 2], kt[4, 1])
 
 
+# ---------------------------------------------------------------------------------------------
+# Short causal convolution of the GDN layers
+# ---------------------------------------------------------------------------------------------
+
+def _conv_case(seed, n=7, width=4, dtype="f32", tree="random"):
+    w = synth.Workload("pin", [0], 2, 4, 8, 6, 2, 1, 8, dtype, [0], n, "random4",
+                       extra={"conv": width})
+    parent = synth.random_tree(seed, f"pin/conv/{seed}", n, 5) if tree == "random" \
+        else synth.chain_tree(n)
+    q, k, v, _, _ = synth.conv_inputs(w, seed, 0, 0, n)
+    return parent, synth.conv_tail(w, seed, 0, 0), q, k, v, synth.conv_weight(w, seed, 0)
+
+
+def _wide(x):
+    return synth.bf16_bits_to_f32(x) if x.dtype == np.uint16 else x
+
+
+def _library_conv_chain(tail, rows, W, hk=2, dk=8):
+    """torch (float64) depthwise conv1d over [tail; rows], then SiLU, then F.normalize of
+    every q and k head: [len(rows)][C]."""
+    import torch
+    import torch.nn.functional as F
+    seq = np.concatenate([_wide(tail), _wide(rows)], axis=0).astype(np.float64)
+    C, w = W.shape
+    x = torch.from_numpy(seq.T.copy())[None]                        # [1][C][T]
+    y = F.conv1d(x, torch.from_numpy(W.astype(np.float64))[:, None, :], groups=C)[0].T
+    y = F.silu(y)
+    cq = hk * dk
+    for lo in range(0, 2 * cq, dk):
+        y[:, lo:lo + dk] = F.normalize(y[:, lo:lo + dk], dim=1)
+    return y.numpy()
+
+
+def pin_conv_library_chain():
+    # A chain over the committed tail is the textbook causal depthwise conv1d.
+    for seed, dtype, width in ((21, "f32", 4), (22, "bf16", 4), (23, "f32", 3), (24, "f32", 1)):
+        parent, tail, q, k, v, W = _conv_case(seed, n=6, width=width, dtype=dtype, tree="chain")
+        got = oracle.conv_rows(*oracle.gdn_conv(parent, tail, q, k, v, W))
+        want = _library_conv_chain(tail, oracle.conv_rows(q, k, v), W)
+        assert brute.rel_err(got, want) < 1e-5, (seed, brute.rel_err(got, want))
+
+
+def pin_conv_tree_brute():
+    # Every node of a tree equals the library chain conv over its own root path.
+    for seed, dtype in ((25, "f32"), (26, "bf16")):
+        parent, tail, q, k, v, W = _conv_case(seed, n=9, dtype=dtype)
+        got = oracle.conv_rows(*oracle.gdn_conv(parent, tail, q, k, v, W))
+        rows = oracle.conv_rows(q, k, v)
+        for i in range(len(parent)):
+            want = _library_conv_chain(tail, rows[synth.root_path(parent, i)], W)[-1]
+            assert brute.rel_err(got[i], want) < 1e-5, (seed, i)
+
+
+def pin_conv_single_taps():
+    # One nonzero tap reads one input: the node itself, or r steps up the path / the tail.
+    parent, tail, q, k, v, W = _conv_case(27, n=9)
+    d = synth.depths(parent)
+    rows, tl = oracle.conv_rows(q, k, v), _wide(tail)
+    cq = 2 * 8
+    for j in range(4):
+        Wj = np.zeros_like(W)
+        Wj[:, j] = 1.0
+        got = oracle.conv_rows(*oracle.gdn_conv(parent, tail, q, k, v, Wj))
+        r = 3 - j
+        for i in range(len(parent)):
+            path = synth.root_path(parent, i)
+            x = rows[path[d[i] - r]] if r <= d[i] else tl[3 - (r - d[i])]
+            y = x.astype(np.float64) / (1.0 + np.exp(-x.astype(np.float64)))
+            for lo in range(0, 2 * cq, 8):
+                y[lo:lo + 8] /= np.sqrt((y[lo:lo + 8] ** 2).sum() + oracle.CONV_EPS)
+            np.testing.assert_allclose(got[i], y, rtol=2e-6, atol=1e-7)
+
+
+def pin_conv_commit_then_decode():
+    # Verifying a chain equals decoding it token by token, committing each token's
+    # pre-conv row into the tail in between: bit for bit.
+    parent, tail, q, k, v, W = _conv_case(28, n=6, dtype="bf16", tree="chain")
+    whole = oracle.gdn_conv(parent, tail, q, k, v, W)
+    cur = tail.copy()
+    for i in range(6):
+        sl = slice(i, i + 1)
+        one = oracle.gdn_conv([-1], cur, q[sl], k[sl], v[sl], W)
+        for a, b in zip(one, whole):
+            assert np.array_equal(a[0], b[i])
+        cur = oracle.conv_tail_commit(cur, q[sl], k[sl], v[sl], [0])
+    # one commit of the whole chain lands on the same tail
+    assert np.array_equal(oracle.conv_tail_commit(tail, q, k, v, list(range(6))), cur)
+    # hand-checked tail bookkeeping: 3 rows, paths of 1 and of 4 nodes
+    t = np.array([[1], [2], [3]], np.float32)
+    x = np.array([[10], [11], [12], [13], [14]], np.float32)
+    one_col = (x[:, None, :1], x[:, None, :0], x[:, None, :0])  # q only, C = 1
+    assert oracle.conv_tail_commit(t, *one_col, [0]).ravel().tolist() == [2, 3, 10]
+    assert oracle.conv_tail_commit(t, *one_col, [0, 2, 3, 4]).ravel().tolist() == [12, 13, 14]
+
+
+def pin_storage_rounding():
+    # float32 -> bfloat16 storage rounding equals torch's conversion (nearest even), ties
+    # included.
+    import torch
+    rng = np.random.default_rng(29)
+    x = rng.standard_normal(4096).astype(np.float32) * 10
+    ties = (rng.integers(0, 0x7F00, 512).astype(np.uint32) << 16 | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties, np.float32([0.0, -0.0, 1e-40, 3.4e38])])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.to_storage(x, np.zeros(1, np.uint16)), want)
+    assert oracle.to_storage(x, x) is not None and np.array_equal(oracle.to_storage(x, x), x)
+
+
 PINS = {name[4:]: fn for name, fn in list(globals().items()) if name.startswith("pin_")}
 
 
