@@ -97,6 +97,12 @@ def algorithmic_bytes(w, L, n):
             + 2 * 2 * n * w.attn_hkv * w.attn_d * 2 + n * w.attn_hq * w.attn_d * 2)
     gdn = (w.gdn_hv * w.gdn_dk * w.gdn_dv * 4 + 2 * n * w.gdn_hk * w.gdn_dk * 2
            + n * w.gdn_hv * w.gdn_dv * 2 + 2 * n * w.gdn_hv * 2 + n * w.gdn_hv * w.gdn_dv * 2)
+    width = w.extra.get("conv", 0)
+    if width:
+        # the conv in front of each GDN layer: pre-conv rows and taps read, the committed
+        # tail read, the post-conv rows written (the walk then reads them, counted above)
+        C = 2 * w.gdn_hk * w.gdn_dk + w.gdn_hv * w.gdn_dv
+        gdn += n * C * 2 + C * width * 4 + (width - 1) * C * 2 + n * C * 2
     # the split pass's share of an attention layer: the resident K/V rows below the
     # last 32-key tile boundary under L, and the queries (the tree pass reads the rest
     # and writes the tree rows and the outputs)
@@ -113,11 +119,18 @@ def cpu_baseline(w, seed, L, parent, gdn_layers=3, attn_heads=4):
     n = len(parent)
     t_gdn = 0.0
     gdn_ids = [l for l, k in enumerate(w.layer_kind) if k == 0][:gdn_layers]
+    conv = synth.conv_width(w)
     for l in gdn_ids:
         S = synth.gdn_state(w, seed, 0, l)
-        q, k, v, a, b = synth.gdn_inputs(w, seed, 0, l, n)
-        t0 = time.perf_counter()
-        oracle.gdn_tree(parent, S, q, k, v, a, b)
+        if conv:
+            q, k, v, a, b = synth.conv_inputs(w, seed, 0, l, n)
+            tail, W = synth.conv_tail(w, seed, 0, l), synth.conv_weight(w, seed, l)
+            t0 = time.perf_counter()
+            oracle.gdn_conv_layer(parent, S, tail, q, k, v, a, b, W)
+        else:
+            q, k, v, a, b = synth.gdn_inputs(w, seed, 0, l, n)
+            t0 = time.perf_counter()
+            oracle.gdn_tree(parent, S, q, k, v, a, b)
         t_gdn += time.perf_counter() - t0
     l_att = [l for l, k in enumerate(w.layer_kind) if k == 1][0]
     q, kt, vt = synth.attn_inputs(w, seed, 0, l_att, n)
@@ -250,7 +263,7 @@ def main():
     for i in range(args.steps):
         lengths.append(lens())
         step()
-    prof = {k: eng.profile_read(k) for k in (0, 1, 2, 3)}
+    prof = {k: eng.profile_read(k) for k in (0, 1, 2, 3, 4)}
     eng.profile(False)
 
     import statistics
@@ -274,7 +287,8 @@ def main():
     verify_gbps = verify_bytes / (med * 1e-3) / 1e9
     kernels = {name: {"avg_us": round(1e3 * prof[k][0] / max(1, prof[k][1]), 2),
                       "launches_per_step": prof[k][1] // args.steps}
-               for k, name in ((0, "gdn_tree"), (1, "attn_split"), (2, "attn_tree"), (3, "commit"))}
+               for k, name in ((0, "gdn_tree"), (1, "attn_split"), (2, "attn_tree"), (3, "commit"),
+                               (4, "gdn_conv")) if prof[k][1] > 0}
 
     traffic = None   # measured bytes are stale once the kernels change
     if args.workload == "stack_65k" and os.path.exists(TRAFFIC_FILE):
@@ -295,9 +309,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic: seeded counter-based inputs (SplitMix64, Box-Muller); projections "
-                "and weights excluded",
+                "and weights excluded" + ("; conv taps synthetic N(0, 1/width)"
+                                          if synth.conv_width(w) else ""),
         "config": {"workload": (f"{w.name}: {w.n_gdn} GDN + {w.n_attn} attention layers (3:1), "
-                                f"{L0} resident tokens, {n}-node draft tree, commit of {len(path)}")
+                                f"{L0} resident tokens, {n}-node draft tree, commit of {len(path)}"
+                                + (f"; width-{synth.conv_width(w)} causal conv in front of every "
+                                   "GDN layer" if synth.conv_width(w) else ""))
                    if ns == 1 else
                                (f"{w.name}: {w.n_gdn} GDN + {w.n_attn} attention layers (3:1), one joint "
                                 f"pass over {ns} slots of {', '.join(str(x) for x in w.lengths)} resident "

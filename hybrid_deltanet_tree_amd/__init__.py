@@ -23,7 +23,7 @@ HDT_MAX_TREES = 8
 HDT_F32, HDT_BF16 = 0, 1
 STATUS = {0: "HDT_OK", -1: "HDT_E_INVALID", -2: "HDT_E_TREE", -3: "HDT_E_PATH",
           -4: "HDT_E_CAPACITY", -5: "HDT_E_ORDER", -6: "HDT_E_HIP", -7: "HDT_E_UNSUPPORTED"}
-KIND_GDN, KIND_ATTN_SPLIT, KIND_ATTN_FOLD, KIND_COMMIT = 0, 1, 2, 3
+KIND_GDN, KIND_ATTN_SPLIT, KIND_ATTN_FOLD, KIND_COMMIT, KIND_CONV = 0, 1, 2, 3, 4
 
 # PyTorch owns the device memory and the streams, so libhdt must run on the same
 # HIP runtime instance.  PyTorch ships its own libamdhip64 under the same soname;
@@ -45,13 +45,14 @@ class hdt_model_desc(ctypes.Structure):
                 ("attn_hq", ctypes.c_int32), ("attn_hkv", ctypes.c_int32),
                 ("attn_d", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
                 ("gdn_scale", ctypes.c_float), ("attn_scale", ctypes.c_float),
-                ("max_nodes", ctypes.c_int32)]
+                ("max_nodes", ctypes.c_int32), ("gdn_conv", ctypes.c_int32),
+                ("gdn_conv_weight", ctypes.c_void_p)]
 
 
 class hdt_slot_desc(ctypes.Structure):
     _fields_ = [("gdn_state", ctypes.c_void_p), ("k_cache", ctypes.c_void_p),
                 ("v_cache", ctypes.c_void_p), ("capacity", ctypes.c_int64),
-                ("length", ctypes.c_int64)]
+                ("length", ctypes.c_int64), ("gdn_conv_state", ctypes.c_void_p)]
 
 
 class hdt_layer_io(ctypes.Structure):
@@ -135,22 +136,24 @@ class Engine:
 
     layer_kind: list of 0 (GDN) / 1 (attention).  slots: list of dicts with
     'gdn_state', 'k_cache', 'v_cache' (tensors or device pointers), 'capacity'
-    and 'length'.
+    and 'length', and 'conv_state' when gdn_conv > 1.  gdn_conv_weight: the
+    [n_gdn][C][gdn_conv] float32 taps when gdn_conv > 0.
     """
 
     def __init__(self, layer_kind, *, gdn_hk=0, gdn_hv=0, gdn_dk=0, gdn_dv=0, attn_hq=0,
                  attn_hkv=0, attn_d=0, io_dtype=HDT_BF16, gdn_scale=0.0, attn_scale=0.0,
-                 max_nodes=16, slots=()):
+                 max_nodes=16, slots=(), gdn_conv=0, gdn_conv_weight=None):
         self._kinds = (ctypes.c_uint8 * len(layer_kind))(*layer_kind)
         self.layer_kind = list(layer_kind)
         self.desc = hdt_model_desc(len(layer_kind), self._kinds, gdn_hk, gdn_hv, gdn_dk, gdn_dv,
                                    attn_hq, attn_hkv, attn_d, io_dtype, gdn_scale, attn_scale,
-                                   max_nodes)
+                                   max_nodes, gdn_conv, _ptr(gdn_conv_weight))
         arr = (hdt_slot_desc * max(1, len(slots)))()
         for i, s in enumerate(slots):
             arr[i] = hdt_slot_desc(_ptr(s.get("gdn_state")), _ptr(s.get("k_cache")),
-                                   _ptr(s.get("v_cache")), int(s["capacity"]), int(s["length"]))
-        self._keep = [slots]
+                                   _ptr(s.get("v_cache")), int(s["capacity"]), int(s["length"]),
+                                   _ptr(s.get("conv_state")))
+        self._keep = [slots, gdn_conv_weight]
         h = _E()
         st = hdt_create(ctypes.byref(self.desc), len(slots), arr, ctypes.byref(h))
         if st != 0:

@@ -27,6 +27,7 @@ namespace {
 constexpr int kSplitCUs = 256;      // splits are sized so one layer spreads over this many items
 constexpr int64_t kSplitMin = 256;  // float32 attention: smallest split, in keys
 constexpr int64_t kSplitMax = 16384;
+constexpr float kConvEps = 1e-6f;      // GDN conv: epsilon of the q/k L2 norm, y / sqrt(sum y^2 + eps)
 constexpr int64_t kKvSplitMin = 128;  // bf16 attention: smallest split (> kKvTile - 1 + kMaxNodes - 1)
 
 struct SlotState {
@@ -41,6 +42,8 @@ struct SlotState {
   void *part_o = nullptr;     // bf16 attention: normalised fp16 partials [hkv][nsplit][rows][D]
   float *carry_acc = nullptr; // bf16 attention: state of split n_full below tb0 [hkv][rows][D]
   float *carry_ml = nullptr;  // [hkv][rows][2]
+  void *conv_out = nullptr;   // GDN conv: post-conv q | k | v of one layer [max_nodes][..] each
+  void *x_pend = nullptr;     // GDN conv: pre-conv rows of the tree [n_gdn][max_nodes][C]
   bool pending = false;
   int32_t n = 0;
   int32_t chain = 0;
@@ -68,8 +71,9 @@ struct hdt_engine {
   bool profiling = false;
   std::vector<EventPair> ev_live;
   std::vector<EventPair> ev_pool;
-  double prof_ms[4] = {0, 0, 0, 0};
-  int64_t prof_count[4] = {0, 0, 0, 0};
+  int32_t conv_C = 0;  // channels through the GDN conv: 2 hk dk + hv dv
+  double prof_ms[5] = {0, 0, 0, 0, 0};
+  int64_t prof_count[5] = {0, 0, 0, 0, 0};
 };
 
 namespace {
@@ -172,6 +176,10 @@ hdt_status ensure_alloc(hdt_engine *e) {
           hipMalloc(&s.k_pend, ng * nm * m.gdn_hk * m.gdn_dk * e->esz) != hipSuccess ||
           hipMalloc(&s.a_pend, ng * nm * m.gdn_hv * e->esz) != hipSuccess)
         return fail(e, HDT_E_HIP, "hipMalloc of the pending GDN buffers failed");
+      if (m.gdn_conv > 0 &&
+          (hipMalloc(&s.conv_out, nm * e->conv_C * e->esz) != hipSuccess ||
+           hipMalloc(&s.x_pend, static_cast<size_t>(e->n_gdn) * nm * e->conv_C * e->esz) != hipSuccess))
+        return fail(e, HDT_E_HIP, "hipMalloc of the conv buffers failed");
     }
     if (e->n_attn > 0) {
       const size_t rows = nm * G;
@@ -203,8 +211,10 @@ void free_scratch(hdt_engine *e) {
     (void)hipFree(s.part_o);
     (void)hipFree(s.carry_acc);
     (void)hipFree(s.carry_ml);
+    (void)hipFree(s.conv_out);
+    (void)hipFree(s.x_pend);
     s.u_pend = nullptr;
-    s.k_pend = s.a_pend = s.part_o = nullptr;
+    s.k_pend = s.a_pend = s.part_o = s.conv_out = s.x_pend = nullptr;
     s.part_acc = s.part_ml = s.carry_acc = s.carry_ml = nullptr;
   }
   e->allocated = false;
@@ -301,6 +311,46 @@ hdt_status launch_kv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *trees
   return check_hip(e, launch_kv_tree(a, m.attn_d, items_b, stream, p.events()), "attention tree launch");
 }
 
+// The short causal conv in front of GDN layer l (its ki-th GDN layer), every tree at once.
+hdt_status launch_conv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
+                             const int8_t (*par)[kMaxNodes], const int8_t (*dep)[kMaxNodes], int l,
+                             int ki, int32_t n_max, hipStream_t stream) {
+  const hdt_model_desc &m = e->desc;
+  ConvLaunch c;
+  std::memset(&c, 0, sizeof c);
+  c.n_trees = n_trees;
+  c.n_max = n_max;
+  c.width = m.gdn_conv;
+  c.hk = m.gdn_hk;
+  c.dk = m.gdn_dk;
+  c.hv = m.gdn_hv;
+  c.dv = m.gdn_dv;
+  c.eps = kConvEps;
+  c.weight = m.gdn_conv_weight + static_cast<size_t>(ki) * e->conv_C * m.gdn_conv;
+  const size_t nm = static_cast<size_t>(m.max_nodes);
+  const size_t row = static_cast<size_t>(e->conv_C) * e->esz;
+  const size_t cq = nm * m.gdn_hk * m.gdn_dk * e->esz;
+  for (int t = 0; t < n_trees; ++t) {
+    const hdt_tree &tr = trees[t];
+    SlotState &s = e->slots[tr.slot];
+    const hdt_layer_io &io = tr.io[l];
+    ConvTree &x = c.t[t];
+    x.q = io.q;
+    x.k = io.k;
+    x.v = io.v;
+    x.tail = static_cast<const char *>(s.d.gdn_conv_state) + static_cast<size_t>(ki) * (m.gdn_conv - 1) * row;
+    x.qo = s.conv_out;
+    x.ko = static_cast<char *>(s.conv_out) + cq;
+    x.vo = static_cast<char *>(s.conv_out) + 2 * cq;
+    x.x_pend = static_cast<char *>(s.x_pend) + static_cast<size_t>(ki) * nm * row;
+    x.n = tr.n_nodes;
+    std::memcpy(x.parent, par[t], kMaxNodes);
+    std::memcpy(x.depth, dep[t], kMaxNodes);
+  }
+  ProfScope p(e, 4);
+  return check_hip(e, launch_gdn_conv(c, m.io_dtype == HDT_BF16, stream, p.events()), "GDN conv launch");
+}
+
 hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, const int8_t (*par)[kMaxNodes],
                           const int8_t (*dep)[kMaxNodes], hipStream_t stream) {
   const hdt_model_desc &m = e->desc;
@@ -312,6 +362,10 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
   for (int l = 0; l < m.n_layers; ++l) {
     const int ki = e->kind_index[l];
     if (e->kind[l] == 0) {
+      if (m.gdn_conv > 0) {
+        hdt_status st = launch_conv_layer(e, n_trees, trees, par, dep, l, ki, n_max, stream);
+        if (st != HDT_OK) return st;
+      }
       GdnLaunch a;
       std::memset(&a, 0, sizeof a);
       a.n_trees = n_trees;
@@ -325,9 +379,16 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
         SlotState &s = e->slots[tr.slot];
         const hdt_layer_io &io = tr.io[l];
         GdnTree &g = a.t[t];
-        g.q = io.q;
-        g.k = io.k;
-        g.v = io.v;
+        if (m.gdn_conv > 0) {  // the walk reads the conv output of this layer
+          const size_t cq = static_cast<size_t>(m.max_nodes) * m.gdn_hk * m.gdn_dk * e->esz;
+          g.q = s.conv_out;
+          g.k = static_cast<char *>(s.conv_out) + cq;
+          g.v = static_cast<char *>(s.conv_out) + 2 * cq;
+        } else {
+          g.q = io.q;
+          g.k = io.k;
+          g.v = io.v;
+        }
         g.alpha = io.alpha;
         g.beta = io.beta;
         g.o = io.o;
@@ -446,9 +507,20 @@ hdt_status do_commit(hdt_engine *e, int32_t slot, const int32_t *path, int32_t m
   c.hkv = m.attn_hkv;
   c.D = m.attn_d;
   c.gdn_blocks = e->n_gdn > 0 ? e->n_gdn * m.gdn_hv * (m.gdn_dv / kGdnCols) : 0;
+  c.kv_blocks = e->n_attn > 0 ? e->n_attn * m.attn_hkv : 0;
+  int conv_blocks = 0;
+  if (e->n_gdn > 0 && m.gdn_conv > 1) {
+    c.conv_state = s.d.gdn_conv_state;
+    c.x_pend = s.x_pend;
+    c.conv_width = m.gdn_conv;
+    c.conv_C = e->conv_C;
+    const int64_t chunks = static_cast<int64_t>(e->conv_C) * e->esz / 16;
+    c.conv_blocks_per_layer = static_cast<int32_t>((chunks + kGdnThreads - 1) / kGdnThreads);
+    conv_blocks = e->n_gdn * c.conv_blocks_per_layer;
+  }
   c.m = m_len;
   for (int d = 0; d < m_len; ++d) c.path[d] = static_cast<int8_t>(path[d]);
-  const int blocks = c.gdn_blocks + (e->n_attn > 0 ? e->n_attn * m.attn_hkv : 0);
+  const int blocks = c.gdn_blocks + c.kv_blocks + conv_blocks;
   if (blocks > 0) {
     ProfScope p(e, 3);
     const int dk = e->n_gdn > 0 ? m.gdn_dk : 64;
@@ -483,6 +555,10 @@ hdt_status hdt_create(const hdt_model_desc *desc, int32_t n_slots, const hdt_slo
     if (m.gdn_hk < 1 || m.gdn_hv < m.gdn_hk || m.gdn_hv % m.gdn_hk != 0) return HDT_E_INVALID;
     if (m.gdn_dk != m.gdn_dv || (m.gdn_dk != 64 && m.gdn_dk != 128)) return HDT_E_UNSUPPORTED;
   }
+  if (m.gdn_conv < 0) return HDT_E_INVALID;
+  if (m.gdn_conv > kConvMaxWidth) return HDT_E_UNSUPPORTED;
+  if (m.gdn_conv > 0 && n_gdn > 0 && (!m.gdn_conv_weight || !aligned16(m.gdn_conv_weight)))
+    return HDT_E_INVALID;
   if (n_attn > 0) {
     if (m.attn_hkv < 1 || m.attn_hq < m.attn_hkv || m.attn_hq % m.attn_hkv != 0)
       return HDT_E_INVALID;
@@ -500,6 +576,8 @@ hdt_status hdt_create(const hdt_model_desc *desc, int32_t n_slots, const hdt_slo
     if (n_attn > 0 && s.capacity * m.attn_d * (m.io_dtype == HDT_BF16 ? 2 : 4) > INT32_MAX)
       return HDT_E_UNSUPPORTED;
     if (n_gdn > 0 && (!s.gdn_state || !aligned16(s.gdn_state))) return HDT_E_INVALID;
+    if (n_gdn > 0 && m.gdn_conv > 1 && (!s.gdn_conv_state || !aligned16(s.gdn_conv_state)))
+      return HDT_E_INVALID;
     if (n_attn > 0 && (!s.k_cache || !s.v_cache || !aligned16(s.k_cache) || !aligned16(s.v_cache)))
       return HDT_E_INVALID;
   }
@@ -513,6 +591,8 @@ hdt_status hdt_create(const hdt_model_desc *desc, int32_t n_slots, const hdt_slo
   e->n_gdn = n_gdn;
   e->n_attn = n_attn;
   e->esz = m.io_dtype == HDT_BF16 ? 2 : 4;
+  if (n_gdn == 0) e->desc.gdn_conv = 0;
+  e->conv_C = n_gdn > 0 ? 2 * m.gdn_hk * m.gdn_dk + m.gdn_hv * m.gdn_dv : 0;
   int gi = 0, ai = 0;
   for (int l = 0; l < m.n_layers; ++l) e->kind_index.push_back(m.layer_kind[l] == 0 ? gi++ : ai++);
   e->slots.resize(n_slots);
@@ -573,6 +653,8 @@ hdt_status hdt_forward_tree(hdt_engine *e, int32_t n_trees, const hdt_tree *tree
         return fail(e, HDT_E_INVALID, "tree %d layer %d: NULL q/k/v/o", t, l);
       if (e->kind[l] == 0 && (!io.alpha || !io.beta))
         return fail(e, HDT_E_INVALID, "tree %d layer %d: NULL alpha/beta", t, l);
+      if (e->kind[l] == 0 && m.gdn_conv > 0 && (!aligned16(io.q) || !aligned16(io.k) || !aligned16(io.v)))
+        return fail(e, HDT_E_INVALID, "tree %d layer %d: conv inputs must be 16-byte aligned", t, l);
       if (e->kind[l] == 1 && (!aligned16(io.q) || !aligned16(io.k) || !aligned16(io.v) ||
                               !aligned16(io.o)))
         return fail(e, HDT_E_INVALID, "tree %d layer %d: attention buffers must be 16-byte aligned",
@@ -717,7 +799,7 @@ hdt_status hdt_profile(hdt_engine *e, int32_t enable) {
 }
 
 hdt_status hdt_profile_read(hdt_engine *e, int32_t kind, double *ms, int64_t *launches) {
-  if (!e || kind < 0 || kind > 3 || !ms || !launches) return HDT_E_INVALID;
+  if (!e || kind < 0 || kind > 4 || !ms || !launches) return HDT_E_INVALID;
   for (auto &p : e->ev_live) {
     if (hipEventSynchronize(p.b) != hipSuccess) return fail(e, HDT_E_HIP, "event wait failed");
     float t = 0.0f;

@@ -12,8 +12,9 @@
 //                     bf16 storage runs the kernels of kv_attention.hip.
 //  attn_fold_kernel   folds a row's split partials in ascending split order.
 //  commit_kernel      commit_tree: replays the accepted path's rank-1 steps into
-//                     every GDN layer's committed state and gathers the path's
-//                     pending K/V rows into place ("One request, end to end", 2.6).
+//                     every GDN layer's committed state, gathers the path's
+//                     pending K/V rows into place ("One request, end to end", 2.6)
+//                     and rolls the path's pre-conv rows into the conv tails.
 //
 // Bit-exactness (a verified row equals the decode step's row, "Adding a model",
 // step 4 of "The adapter path in ten steps"): every value a row gets is a
@@ -1050,6 +1051,33 @@ __global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch 
 #pragma unroll
     for (int a = 0; a < R; a += 4)
       *reinterpret_cast<float4 *>(sp + a) = make_float4(cur[a], cur[a + 1], cur[a + 2], cur[a + 3]);
+    return;
+  }
+  if (bid >= P.gdn_blocks + P.kv_blocks) {
+    // Conv tail of one GDN layer, 16 bytes of channels per thread: the new tail is
+    // the last width-1 rows of (old tail, the path's pre-conv rows), bit copies.
+    // A thread reads every source of its channels before it writes any row.
+    const int cb = bid - P.gdn_blocks - P.kv_blocks;
+    const int lg = cb / P.conv_blocks_per_layer;
+    const int64_t row_bytes = static_cast<int64_t>(P.conv_C) * (BF ? 2 : 4);
+    const int64_t byte = (static_cast<int64_t>(cb % P.conv_blocks_per_layer) * kGdnThreads + tid) * 16;
+    if (byte >= row_bytes) return;
+    const int keep = P.conv_width - 1;
+    unsigned char *tail = static_cast<unsigned char *>(P.conv_state) + lg * keep * row_bytes + byte;
+    const unsigned char *xp = static_cast<const unsigned char *>(P.x_pend) +
+                              static_cast<int64_t>(lg) * P.max_nodes * row_bytes + byte;
+    uint4 rows[kConvMaxWidth - 1];
+#pragma unroll
+    for (int r = 0; r < kConvMaxWidth - 1; ++r) {
+      if (r < keep) {
+        const int src = P.m + r;  // index into (old tail rows, path rows)
+        rows[r] = src < keep ? *reinterpret_cast<const uint4 *>(tail + src * row_bytes)
+                             : *reinterpret_cast<const uint4 *>(xp + P.path[src - keep] * row_bytes);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kConvMaxWidth - 1; ++r)
+      if (r < keep) *reinterpret_cast<uint4 *>(tail + r * row_bytes) = rows[r];
     return;
   }
   // K/V gather: row L+d <- row L+path[d] of one (attention layer, kv head).

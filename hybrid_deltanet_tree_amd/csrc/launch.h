@@ -56,6 +56,30 @@ struct GdnLaunch {
   float scale;
 };
 
+// ---------------------------------------------------------------- GDN short conv
+// Depthwise causal convolution of width `width` over each tree node's root path
+// (ancestors, then the committed tail before the root), SiLU, and per-head L2
+// norm of q and k.  Channels of a token: q (hk*dk), k (hk*dk), v (hv*dv).
+constexpr int kConvMaxWidth = 4;
+constexpr int kConvThreads = 256;
+struct ConvTree {
+  const void *q, *k, *v;                 // pre-conv inputs [n][hk][dk], [n][hk][dk], [n][hv][dv]
+  const void *tail;                      // committed tail of this layer [width-1][C]
+  void *qo, *ko, *vo;                    // post-conv outputs, same layouts as the inputs
+  void *x_pend;                          // [max_nodes][C]: the tree's pre-conv rows, for commit
+  int32_t n;
+  int8_t parent[kMaxNodes];
+  int8_t depth[kMaxNodes];
+};
+
+struct ConvLaunch {
+  ConvTree t[kMaxTrees];
+  const float *weight;                   // this layer's taps [C][width]
+  int32_t n_trees, n_max;
+  int32_t width, hk, dk, hv, dv;
+  float eps;
+};
+
 // ---------------------------------------------------------------- attention split pass
 // Work items of one tree, in block order: first the tail items (kv head x group of
 // up to kAttnWaves nodes), which cover every position from the first split that is
@@ -156,6 +180,11 @@ struct CommitLaunch {
   int32_t hk, hv, dv;
   int32_t hkv, D;
   int32_t gdn_blocks;                     // blocks [0, gdn_blocks) commit states
+  int32_t kv_blocks;                      // then kv_blocks gather K/V rows
+  // then conv_blocks roll the conv tails: tail <- last width-1 rows of (tail, path rows)
+  void *conv_state;                       // [n_gdn][width-1][C]
+  const void *x_pend;                     // [n_gdn][max_nodes][C]
+  int32_t conv_width, conv_C, conv_blocks_per_layer;
   int32_t m;
   int8_t path[kMaxNodes];
 };
@@ -179,6 +208,9 @@ hipError_t launch_kv_split(const KvLaunch &a, int D, int max_items, hipStream_t 
 hipError_t launch_kv_tree(const KvLaunch &a, int D, int max_items, hipStream_t s, KernelEvents ev);
 hipError_t launch_commit(const CommitLaunch &a, int dk, int bf16, int n_blocks, hipStream_t s,
                          KernelEvents ev);
+hipError_t launch_gdn_conv(const ConvLaunch &a, int bf16, hipStream_t s, KernelEvents ev);
+// Channels one conv thread handles (16 bytes of io dtype).
+constexpr int conv_channels_per_thread(int bf16) { return bf16 ? 8 : 4; }
 
 // Dynamic LDS bytes each kernel asks for (the host checks them against the device).
 size_t gdn_lds_bytes(int dk, int n_max, int n_saves);

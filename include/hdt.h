@@ -70,6 +70,18 @@ typedef enum { HDT_F32 = 0, HDT_BF16 = 1 } hdt_dtype;
  *  attn_scale: softmax scale; <= 0 selects 1/sqrt(attn_d).
  *  max_nodes: largest tree any call will pass (1..HDT_MAX_NODES); sizes the
  *    library's own scratch.
+ *  gdn_conv: width w of the short causal convolution in front of every GDN
+ *    layer (the gdn.conv state section of "Adding a model", "The model layer:
+ *    architecture registry and per-model state"), 1..4; 0 = none, and then a
+ *    GDN layer's q, k, v are taken as already convolved.  With w > 0 a GDN
+ *    layer's q, k, v inputs are the pre-conv channels; per channel the layer
+ *    computes y = SiLU(sum_j W[c][j] x_{w-1-j}), x_r being the input r tokens
+ *    back along the node's root path (the slot's conv tail before the root),
+ *    then divides every q and k head by sqrt(sum of squares + 1e-6).  The
+ *    post-conv values are rounded to io_dtype before the recurrence.
+ *  gdn_conv_weight: device float32 [n_gdn][C][w] taps (tap w-1 multiplies the
+ *    current token), C = 2 gdn_hk gdn_dk + gdn_hv gdn_dv channels ordered q, k,
+ *    v, each head-major; 16-byte aligned.  Unused when gdn_conv = 0.
  */
 typedef struct {
   int32_t n_layers;
@@ -79,6 +91,8 @@ typedef struct {
   int32_t io_dtype;
   float gdn_scale, attn_scale;
   int32_t max_nodes;
+  int32_t gdn_conv;
+  const float *gdn_conv_weight;
 } hdt_model_desc;
 
 /*
@@ -95,6 +109,10 @@ typedef struct {
  *  capacity: rows per head in the caches; a tree of n nodes needs
  *    length + n <= capacity.
  *  length: committed rows at creation.
+ *  gdn_conv_state: io_dtype [n_gdn][w-1][C] (w = gdn_conv > 1): the pre-conv
+ *    inputs of the last w-1 committed tokens, row w-2 the newest; commit_tree
+ *    rolls the accepted path's rows in (bit copies).  16-byte aligned; unused
+ *    (may be NULL) when gdn_conv <= 1.
  */
 typedef struct {
   float *gdn_state;
@@ -102,12 +120,14 @@ typedef struct {
   void *v_cache;
   int64_t capacity;
   int64_t length;
+  void *gdn_conv_state;
 } hdt_slot_desc;
 
 /*
  * Per-layer inputs and output of one tree, all device pointers in io_dtype,
  * n = the tree's node count:
- *  GDN layer:       q, k [n][gdn_hk][gdn_dk]; v [n][gdn_hv][gdn_dv];
+ *  GDN layer:       q, k [n][gdn_hk][gdn_dk]; v [n][gdn_hv][gdn_dv] (pre-conv
+ *                   and 16-byte aligned when gdn_conv > 0);
  *                   alpha, beta [n][gdn_hv] (decay and write strength, values in
  *                   (0,1)); o [n][gdn_hv][gdn_dv] out.
  *  attention layer: q [n][attn_hq][attn_d]; k, v [n][attn_hkv][attn_d] (the
@@ -174,7 +194,9 @@ hdt_status hdt_forward_block(hdt_engine *eng, int32_t slot, int32_t n, const hdt
  * path[0] = 0 and parent[path[d]] = path[d-1].  For every attention layer,
  * cache row L+d takes the pending row of path[d] (a bit copy); for every GDN
  * layer the committed state becomes the state of node path[m-1], with the same
- * bits the pass computed.  Then length += m and the pending round ends.
+ * bits the pass computed, and (gdn_conv > 1) the conv tail becomes the last w-1
+ * rows of (old tail, path's pre-conv rows).  Then length += m and the pending
+ * round ends.
  * Errors: HDT_E_INVALID, HDT_E_PATH, HDT_E_ORDER (no pending round), HDT_E_HIP.
  */
 hdt_status hdt_commit_tree(hdt_engine *eng, int32_t slot, const int32_t *path, int32_t m,
@@ -221,7 +243,7 @@ hdt_status hdt_split_size(const hdt_engine *eng, int32_t slot, int64_t *out);
  * Kernel timing for measurement.  hdt_profile(eng, 1) starts recording a HIP
  * event pair around every launch on the launch stream; hdt_profile_read waits
  * for the recorded events and returns, for kernel class `kind` (0 = GDN tree
- * walk, 1 = attention split pass, 2 = attention fold, 3 = commit), the summed
+ * walk, 1 = attention split pass, 2 = attention fold, 3 = commit, 4 = GDN conv), the summed
  * milliseconds and the launch count since the last read; then clears them.
  */
 hdt_status hdt_profile(hdt_engine *eng, int32_t enable);

@@ -246,6 +246,10 @@ WORKLOADS = {
     # Long context: 262,144 resident tokens, 32-node tree of depth <= 15.
     "stack_262k": Workload("stack_262k", stack_kinds(), 16, 32, 128, 128, 24, 4, 256, "bf16",
                            [262144], 32, "draft"),
+    # stack_65k with the width-4 short causal conv in front of every GDN layer (pre-conv
+    # q, k, v in; the conv tails are part of the committed state).
+    "stack_65k_conv": Workload("stack_65k_conv", stack_kinds(), 16, 32, 128, 128, 24, 4, 256,
+                               "bf16", [65536], 16, "draft", extra={"conv": 4}),
     # Four slots in one pass: 131,072 + 3 x 8,192 resident tokens, 16-node tree each.
     "joint4": Workload("joint4", stack_kinds(), 16, 32, 128, 128, 24, 4, 256, "bf16",
                        [131072, 8192, 8192, 8192], 16, "draft"),

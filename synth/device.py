@@ -47,6 +47,9 @@ class Instance:
     io[s][l] dict of device tensors (q, k, v, alpha, beta for GDN layers; q, k, v for
     attention layers; o for both).  host[s][l] holds the host arrays of each layer's
     tree inputs; h_state / h_kc / h_vc hold the resident data when keep_host.
+    With a conv width (w.extra["conv"]): conv_w float32 [n_gdn][C][width] taps (host:
+    h_conv_w), tail[s] [n_gdn][width-1][C] committed pre-conv rows (host: h_tail[s]),
+    and the GDN layers' q, k, v are pre-conv inputs.
     """
 
     def __init__(self, w: synth.Workload, seed: int, *, device="cuda", lengths=None,
@@ -68,6 +71,22 @@ class Instance:
         dt, tdt = w.dtype, _tdtype(w.dtype)
         self.state, self.kc, self.vc, self.io, self.host = [], [], [], [], []
         self.h_state, self.h_kc, self.h_vc = [], [], []
+        self.conv = synth.conv_width(w)
+        self.tail, self.h_tail, self.conv_w, self.h_conv_w = [], [], None, []
+        if self.conv > 0:
+            C = synth.conv_channels(w)
+            self.h_conv_w = [synth.conv_weight(w, seed, l)
+                             for l, kind in enumerate(w.layer_kind) if kind == 0]
+            self.conv_w = torch.from_numpy(np.stack(self.h_conv_w)).to(device)
+            for s in range(ns):
+                ht = [synth.conv_tail(w, seed, s, l) for l, kind in enumerate(w.layer_kind)
+                      if kind == 0]
+                self.h_tail.append(ht)
+                t = torch.zeros((w.n_gdn, self.conv - 1, C), dtype=tdt, device=device)
+                for gi, a in enumerate(ht):
+                    if self.conv > 1:
+                        t[gi] = to_device(a, dt, device)
+                self.tail.append(t)
         for s in range(ns):
             L, cap = self.lengths[s], self.capacity[s]
             st = torch.empty((w.n_gdn, w.gdn_hv, w.gdn_dv, w.gdn_dk), dtype=torch.float32,
@@ -122,7 +141,8 @@ class Instance:
         ios, hosts = [], []
         for l, kind in enumerate(w.layer_kind):
             if kind == 0:
-                q, k, v, a, b = synth.gdn_inputs(w, self.seed, s, l, n, tag)
+                gen = synth.conv_inputs if self.conv > 0 else synth.gdn_inputs
+                q, k, v, a, b = gen(w, self.seed, s, l, n, tag)
                 host = dict(q=q, k=k, v=v, alpha=a, beta=b)
                 io = {name: to_device(arr, dt, dev) for name, arr in host.items()}
                 io["o"] = torch.zeros((n, w.gdn_hv, w.gdn_dv), dtype=_tdtype(dt), device=dev)
@@ -138,7 +158,8 @@ class Instance:
 
     def slot_descs(self):
         return [dict(gdn_state=self.state[s], k_cache=self.kc[s], v_cache=self.vc[s],
-                     capacity=self.capacity[s], length=self.lengths[s])
+                     capacity=self.capacity[s], length=self.lengths[s],
+                     conv_state=self.tail[s] if self.conv > 1 else None)
                 for s in range(len(self.lengths))]
 
     def engine(self, max_nodes=None):
@@ -148,7 +169,8 @@ class Instance:
         return hdt.Engine(w.layer_kind, gdn_hk=w.gdn_hk, gdn_hv=w.gdn_hv, gdn_dk=w.gdn_dk,
                           gdn_dv=w.gdn_dv, attn_hq=w.attn_hq, attn_hkv=w.attn_hkv,
                           attn_d=w.attn_d, io_dtype=hdt.HDT_BF16 if w.dtype == "bf16" else hdt.HDT_F32,
-                          max_nodes=mn, slots=self.slot_descs())
+                          max_nodes=mn, slots=self.slot_descs(), gdn_conv=self.conv,
+                          gdn_conv_weight=self.conv_w)
 
     def tree_arg(self, s: int):
         return (s, self.trees[s], self.io[s])

@@ -42,6 +42,10 @@ def oracle_layer(inst, s, l, L=None):
     L = inst.lengths[s] if L is None else L
     if w.layer_kind[l] == 0:
         gi = sum(1 for x in w.layer_kind[:l] if x == 0)
+        if inst.conv > 0:
+            return oracle.gdn_conv_layer(parent, inst.h_state[s][gi], inst.h_tail[s][gi], h["q"],
+                                         h["k"], h["v"], h["alpha"], h["beta"],
+                                         inst.h_conv_w[gi])[0]
         return oracle.gdn_tree(parent, inst.h_state[s][gi], h["q"], h["k"], h["v"], h["alpha"],
                                h["beta"])
     ai = sum(1 for x in w.layer_kind[:l] if x == 1)
@@ -66,15 +70,18 @@ def check_layer(inst, s, l, got, tol=None):
 
 
 def snapshot(inst):
-    return [(inst.state[s].clone(), inst.kc[s].clone(), inst.vc[s].clone())
+    return [(inst.state[s].clone(), inst.kc[s].clone(), inst.vc[s].clone(),
+             inst.tail[s].clone() if inst.conv > 0 else None)
             for s in range(len(inst.lengths))]
 
 
 def restore(inst, snap):
-    for s, (st, kc, vc) in enumerate(snap):
+    for s, (st, kc, vc, tl) in enumerate(snap):
         inst.state[s].copy_(st)
         inst.kc[s].copy_(kc)
         inst.vc[s].copy_(vc)
+        if tl is not None:
+            inst.tail[s].copy_(tl)
 
 
 def row_io(inst, s, node):

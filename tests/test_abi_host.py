@@ -76,11 +76,41 @@ def make_engine(**kw):
     (dict(slots=[dict(gdn_state=0, k_cache=FAKE, v_cache=FAKE, capacity=10, length=1)]), -1),
     (dict(slots=[dict(gdn_state=FAKE + 4, k_cache=FAKE, v_cache=FAKE, capacity=10, length=1)]), -1),
     (dict(slots=[]), -1),
+    (dict(gdn_conv=-1, gdn_conv_weight=FAKE), -1),
+    (dict(gdn_conv=5, gdn_conv_weight=FAKE), -7),
+    (dict(gdn_conv=4), -1),                                   # no taps
+    (dict(gdn_conv=4, gdn_conv_weight=FAKE + 8), -1),         # misaligned taps
+    (dict(gdn_conv=4, gdn_conv_weight=FAKE), -1),             # slots without conv tails
+    (dict(gdn_conv=4, gdn_conv_weight=FAKE,
+          slots=[dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=10, length=1,
+                      conv_state=FAKE + 4)]), -1),
 ])
 def test_create_rejects(kw, status):
     with pytest.raises(hdt.HdtError) as e:
         make_engine(**kw)
     assert e.value.status == status
+
+
+def test_create_accepts_conv():
+    conv_slot = dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=10, length=1,
+                     conv_state=FAKE)
+    make_engine(gdn_conv=4, gdn_conv_weight=FAKE, slots=[conv_slot]).close()
+    # width 1 keeps no tail; no GDN layer needs no taps
+    make_engine(gdn_conv=1, gdn_conv_weight=FAKE).close()
+    make_engine(gdn_conv=4, layer_kind=[1]).close()
+
+
+def test_forward_rejects_misaligned_conv_inputs():
+    conv_slot = dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=10, length=1,
+                     conv_state=FAKE)
+    eng = make_engine(gdn_conv=4, gdn_conv_weight=FAKE, slots=[conv_slot])
+    layers = fake_layers()
+    layers[1] = dict(layers[1], k=FAKE + 2)
+    with pytest.raises(hdt.HdtError) as e:
+        eng.forward_tree([(0, [-1, 0], layers)])
+    assert e.value.status == -1 and "conv inputs" in eng.last_error()
+    assert eng.kv_length(0) == 1
+    eng.close()
 
 
 def fake_layers(n_layers=4):

@@ -26,7 +26,7 @@ FIRST4 = [0, 0, 0, 1]
 def _slice(w):
     return synth.Workload(w.name, FIRST4, w.gdn_hk, w.gdn_hv, w.gdn_dk, w.gdn_dv, w.attn_hq,
                           w.attn_hkv, w.attn_d, w.dtype, w.lengths, w.n_nodes, w.tree_kind,
-                          w.max_depth)
+                          w.max_depth, extra=dict(w.extra))
 
 
 def _say(msg):
@@ -68,8 +68,15 @@ def _check_commit(inst, eng, s, path):
     for l, kind in enumerate(w.layer_kind):
         h = inst.host[s][l]
         if kind == 0:
-            ref = oracle.gdn_commit(path, inst.h_state[s][gi], h["k"], h["v"], h["alpha"],
-                                    h["beta"])
+            k, v = h["k"], h["v"]
+            if inst.conv > 0:  # the recurrence ran on the stored post-conv activations
+                _, (_, k, v) = oracle.gdn_conv_layer(inst.trees[s], inst.h_state[s][gi],
+                                                     inst.h_tail[s][gi], h["q"], h["k"], h["v"],
+                                                     h["alpha"], h["beta"], inst.h_conv_w[gi])
+                want = oracle.conv_tail_commit(inst.h_tail[s][gi], h["q"], h["k"], h["v"], path)
+                assert np.array_equal(to_host(inst.tail[s][gi], w.dtype), want), \
+                    f"slot {s} layer {l}: committed conv tail"
+            ref = oracle.gdn_commit(path, inst.h_state[s][gi], k, v, h["alpha"], h["beta"])
             got = inst.state[s][gi].cpu().numpy()
             err = rel_err(got, ref)
             assert err <= gu.TOL_F32, f"slot {s} layer {l}: committed state {err:.3e}"
@@ -115,6 +122,25 @@ def test_stack65k_slice_at_full_size():
     heads = [0, 5, 6, 11, 12, 17, 18, 23]  # first and last q head of every kv head
     _check_attn_sampled(inst, 0, 3, list(range(len(parent))), heads)
     _check_commit(inst, eng, 0, synth.accepted_path(SEED, "full/c2-path", parent))
+    eng.close()
+
+
+def test_stack65k_conv_slice_at_full_size():
+    """The 65,536-token, 16-node workload with the width-4 conv in front of every GDN
+    layer: pre-conv inputs, committed tails, tails rolled by commit."""
+    base = synth.WORKLOADS["stack_65k_conv"]
+    w = _slice(base)
+    parent = base.tree(SEED, 0)
+    cap = _bench_capacity(base, parent)
+    _say(f"stack_65k_conv slice: L={w.lengths[0]} nodes={len(parent)} capacity={cap}")
+    inst = Instance(w, SEED, trees=[parent], capacity=[cap])
+    eng = inst.engine(max_nodes=len(parent))
+    eng.forward_tree([inst.tree_arg(0)], gu.stream())
+    gu.sync()
+    for l in range(3):
+        _check_gdn(inst, 0, l)
+    _check_attn_sampled(inst, 0, 3, _nodes_sample(parent), [0, 11, 23])
+    _check_commit(inst, eng, 0, synth.accepted_path(SEED, "full/conv-path", parent))
     eng.close()
 
 
