@@ -82,7 +82,7 @@ _sigs = {
     "hdt_reset": (_S, [_E, ctypes.c_int32, ctypes.c_int64]),
     "hdt_tree_meta": (_S, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int64,
                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
-    "hdt_split_size": (_S, [_E, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]),
+    "hdt_split_size": (_S, [_E, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
     "hdt_profile": (_S, [_E, ctypes.c_int32]),
     "hdt_profile_read": (_S, [_E, ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
                               ctypes.POINTER(ctypes.c_int64)]),
@@ -208,9 +208,10 @@ class Engine:
     def reset(self, slot, length):
         self._check(hdt_reset(self.h, slot, length))
 
-    def split_size(self, slot) -> int:
+    def split_size(self, slot, position) -> int:
+        """Split size of the row at `position` of `slot` (it sees keys 0..position)."""
         out = ctypes.c_int64()
-        self._check(hdt_split_size(self.h, slot, ctypes.byref(out)))
+        self._check(hdt_split_size(self.h, slot, position, ctypes.byref(out)))
         return out.value
 
     def profile(self, enable: bool):

@@ -72,6 +72,8 @@ struct hdt_engine {
   std::vector<EventPair> ev_live;
   std::vector<EventPair> ev_pool;
   int32_t conv_C = 0;  // channels through the GDN conv: 2 hk dk + hv dv
+  int64_t kv_per_head = 1;        // bf16 attention: most splits a row may have
+  std::vector<int32_t> kv_ladder;  // bf16 attention: split sizes, ascending
   double prof_ms[5] = {0, 0, 0, 0, 0};
   int64_t prof_count[5] = {0, 0, 0, 0, 0};
 };
@@ -98,15 +100,19 @@ int64_t pow2_floor(int64_t x) {
   return p;
 }
 
-// Split size of a slot.  It depends on the capacity (and on the engine's largest
-// tree, for bf16), never on the current length, so a row's fold structure is fixed
-// for the life of the slot.
-//  float32 storage: a power of two between kSplitMin and kSplitMax chosen so that
-//    a full cache gives about kSplitCUs (kv head, split) items;
-//  bf16 storage: the smallest multiple of kKvTile (at least kKvSplitMin) for which
-//    a full cache gives at most kSplitCUs (kv head, split, row group) items, one
-//    wave of workgroups over the chip; row_groups is the number of kKvRowsPerItem-row
-//    groups that the engine's largest tree needs.
+// Split sizes.  A row's fold structure must not depend on how many of its keys are
+// committed, or a verified row would differ from the decoded row.
+//  float32 storage: a slot's split depends on its capacity alone: a power of two
+//    between kSplitMin and kSplitMax chosen so that a full cache gives about
+//    kSplitCUs (kv head, split) items;
+//  bf16 storage: a row's split depends on its own position alone (and on the
+//    engine's shape): the row that sees K keys takes the smallest rung of the
+//    ladder kKvSplitMin, then s + max(kKvTile, s / 32) rounded up to kKvTile, ...
+//    that cuts K keys into at most per_head splits, per_head = kSplitCUs /
+//    (H_kv row_groups).  So at any length a layer is about one wave of
+//    kSplitCUs (kv head, split, row group) workgroups, a slot's capacity does not
+//    matter, and the rungs are close enough (3 %) that a layer rarely holds rows of
+//    two split sizes.
 // Row groups of the split pass for the engine's largest tree (bf16 attention).
 int32_t kv_row_groups(const hdt_model_desc &m) {
   if (m.attn_hkv <= 0) return 1;
@@ -114,16 +120,27 @@ int32_t kv_row_groups(const hdt_model_desc &m) {
   return static_cast<int32_t>(std::max<int64_t>(1, (rows + kKvRowsPerItem - 1) / kKvRowsPerItem));
 }
 
-int32_t split_for(int64_t capacity, int32_t hkv, bool bf16, int32_t row_groups) {
-  if (bf16) {
-    const int64_t per_head = std::max<int64_t>(1, kSplitCUs / (static_cast<int64_t>(hkv) * row_groups));
-    int64_t s = (capacity + per_head - 1) / per_head;
-    s = (s + kKvTile - 1) / kKvTile * kKvTile;
-    return static_cast<int32_t>(std::max(kKvSplitMin, s));
-  }
+int32_t split_for(int64_t capacity, int32_t hkv) {
   int64_t s = pow2_floor(std::max<int64_t>(1, capacity * hkv / kSplitCUs));
   s = std::max(kSplitMin, std::min(kSplitMax, s));
   return static_cast<int32_t>(s);
+}
+
+int64_t kv_per_head(const hdt_model_desc &m) {
+  return std::max<int64_t>(1, kSplitCUs / (static_cast<int64_t>(std::max(1, m.attn_hkv)) * kv_row_groups(m)));
+}
+
+// The rungs up to the first one that serves max_keys.
+std::vector<int32_t> kv_ladder(int64_t max_keys, int64_t per_head) {
+  std::vector<int32_t> r;
+  int64_t s = kKvSplitMin;
+  const int64_t need = (max_keys + per_head - 1) / per_head;
+  while (true) {
+    r.push_back(static_cast<int32_t>(s));
+    if (s >= need) break;
+    s = (s + std::max<int64_t>(kKvTile, s / 32) + kKvTile - 1) / kKvTile * kKvTile;
+  }
+  return r;
 }
 
 // Validates a parent array and fills depth; returns false for a non-tree.
@@ -250,16 +267,49 @@ struct ProfScope {
   }
 };
 
-// One attention layer with bf16 storage: the split pass over the committed rows,
-// then the tree pass (tree tiles, fold, output, pending rows).
-hdt_status launch_kv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
-                           const int8_t (*par)[kMaxNodes], const int8_t (*dep)[kMaxNodes], int l, int ki,
-                           hipStream_t stream) {
+// bf16 attention: split size of a row that sees K keys (K <= the largest capacity).
+int32_t kv_split_of(const hdt_engine *e, int64_t K) {
+  const int64_t need = (K + e->kv_per_head - 1) / e->kv_per_head;
+  const auto it = std::lower_bound(e->kv_ladder.begin(), e->kv_ladder.end(), need);
+  return it == e->kv_ladder.end() ? e->kv_ladder.back() : *it;
+}
+
+// Split sizes of a tree's rows in ascending order, and the nodes of each (ascending
+// tree index).  Usually one size; a tree whose rows straddle a rung has two.
+struct KvGroups {
+  int count = 0;
+  int32_t split[kMaxNodes];
+  int32_t n[kMaxNodes];
+  int8_t nodes[kMaxNodes][kMaxNodes];
+};
+
+void plan_kv_groups(const hdt_engine *e, int64_t L, int32_t n, const int8_t *dep, KvGroups &g) {
+  int32_t sz[kMaxNodes];
+  g.count = 0;
+  for (int i = 0; i < n; ++i) {
+    sz[i] = kv_split_of(e, L + dep[i] + 1);
+    int k = 0;
+    while (k < g.count && g.split[k] != sz[i]) ++k;
+    if (k == g.count) g.split[g.count++] = sz[i];
+  }
+  std::sort(g.split, g.split + g.count);
+  for (int k = 0; k < g.count; ++k) {
+    g.n[k] = 0;
+    for (int i = 0; i < n; ++i)
+      if (sz[i] == g.split[k]) g.nodes[k][g.n[k]++] = static_cast<int8_t>(i);
+  }
+}
+
+// One attention layer with bf16 storage, for group gr of every tree that has one:
+// the split pass over the committed rows, then the tree pass (tree tiles, fold,
+// output, pending rows).
+hdt_status launch_kv_group(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
+                           const int8_t (*par)[kMaxNodes], const int8_t (*dep)[kMaxNodes],
+                           const KvGroups *groups, int gr, int l, int ki, hipStream_t stream) {
   const hdt_model_desc &m = e->desc;
   const int G = m.attn_hq / m.attn_hkv;
   KvLaunch a;
   std::memset(&a, 0, sizeof a);
-  a.n_trees = n_trees;
   a.hq = m.attn_hq;
   a.hkv = m.attn_hkv;
   a.c2 = m.attn_scale * 1.4426950408889634f;
@@ -269,10 +319,14 @@ hdt_status launch_kv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *trees
   // through the same L2.
   int32_t items_a = 0, items_b = 0;
   for (int t = 0; t < n_trees; ++t) {
+    if (gr >= groups[t].count) continue;
     const hdt_tree &tr = trees[t];
     SlotState &s = e->slots[tr.slot];
     const hdt_layer_io &io = tr.io[l];
-    KvTree &x = a.t[t];
+    KvTree &x = a.t[a.n_trees++];
+    const int32_t split = groups[t].split[gr];
+    x.gn = groups[t].n[gr];
+    std::memcpy(x.nodes, groups[t].nodes[gr], kMaxNodes);
     const size_t view = static_cast<size_t>(m.attn_hkv) * s.d.capacity * m.attn_d * 2;
     x.q = io.q;
     x.kt = io.k;
@@ -287,17 +341,17 @@ hdt_status launch_kv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *trees
     x.L = s.d.length;
     x.cap = s.d.capacity;
     x.n = tr.n_nodes;
-    x.split = s.split;
+    x.split = split;
     x.nsplit_cap = s.nsplit_cap;
     x.rows_cap = m.max_nodes * G;
-    x.n_full = static_cast<int32_t>(s.d.length / s.split);
+    x.n_full = static_cast<int32_t>(s.d.length / split);
     const int64_t tb0 = s.d.length / kKvTile * kKvTile;
-    x.carry_tiles = static_cast<int32_t>((tb0 - static_cast<int64_t>(x.n_full) * s.split) / kKvTile);
-    x.row_groups = (tr.n_nodes * G + kKvRowsPerItem - 1) / kKvRowsPerItem;
+    x.carry_tiles = static_cast<int32_t>((tb0 - static_cast<int64_t>(x.n_full) * split) / kKvTile);
+    x.row_groups = (x.gn * G + kKvRowsPerItem - 1) / kKvRowsPerItem;
     x.a_splits = x.n_full + (x.carry_tiles > 0 ? 1 : 0);
     const int pairs = m.attn_hkv * x.a_splits;  // (kv head, split)
     items_a = std::max(items_a, (pairs + 7) / 8 * 8 * x.row_groups);
-    items_b = std::max(items_b, m.attn_hkv * tr.n_nodes * kKvQuarters);
+    items_b = std::max(items_b, m.attn_hkv * x.gn * kKvQuarters);
     std::memcpy(x.parent, par[t], kMaxNodes);
     std::memcpy(x.depth, dep[t], kMaxNodes);
   }
@@ -309,6 +363,20 @@ hdt_status launch_kv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *trees
   }
   ProfScope p(e, 2);
   return check_hip(e, launch_kv_tree(a, m.attn_d, items_b, stream, p.events()), "attention tree launch");
+}
+
+// One attention layer with bf16 storage: one launch pair per group of nodes that
+// share a split size (one group, unless a tree's rows straddle a rung).
+hdt_status launch_kv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
+                           const int8_t (*par)[kMaxNodes], const int8_t (*dep)[kMaxNodes],
+                           const KvGroups *groups, int l, int ki, hipStream_t stream) {
+  int max_groups = 0;
+  for (int t = 0; t < n_trees; ++t) max_groups = std::max(max_groups, groups[t].count);
+  for (int gr = 0; gr < max_groups; ++gr) {
+    hdt_status st = launch_kv_group(e, n_trees, trees, par, dep, groups, gr, l, ki, stream);
+    if (st != HDT_OK) return st;
+  }
+  return HDT_OK;
 }
 
 // The short causal conv in front of GDN layer l (its ki-th GDN layer), every tree at once.
@@ -358,6 +426,11 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
   const int G = m.attn_hkv > 0 ? m.attn_hq / m.attn_hkv : 1;
   int32_t n_max = 0;
   for (int t = 0; t < n_trees; ++t) n_max = std::max(n_max, trees[t].n_nodes);
+  // bf16 attention: every row's split size, the same for all layers of the pass
+  KvGroups groups[kMaxTrees];
+  if (bf && e->n_attn > 0)
+    for (int t = 0; t < n_trees; ++t)
+      plan_kv_groups(e, e->slots[trees[t].slot].d.length, trees[t].n_nodes, dep[t], groups[t]);
 
   for (int l = 0; l < m.n_layers; ++l) {
     const int ki = e->kind_index[l];
@@ -409,7 +482,7 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
           check_hip(e, launch_gdn_tree(a, m.gdn_dk, bf, stream, p.events()), "GDN tree launch");
       if (st != HDT_OK) return st;
     } else if (bf) {
-      hdt_status st = launch_kv_layer(e, n_trees, trees, par, dep, l, ki, stream);
+      hdt_status st = launch_kv_layer(e, n_trees, trees, par, dep, groups, l, ki, stream);
       if (st != HDT_OK) return st;
     } else {
       AttnLaunch a;
@@ -596,11 +669,22 @@ hdt_status hdt_create(const hdt_model_desc *desc, int32_t n_slots, const hdt_slo
   int gi = 0, ai = 0;
   for (int l = 0; l < m.n_layers; ++l) e->kind_index.push_back(m.layer_kind[l] == 0 ? gi++ : ai++);
   e->slots.resize(n_slots);
+  int64_t max_cap = 1;
+  for (int i = 0; i < n_slots; ++i) max_cap = std::max(max_cap, slots[i].capacity);
+  if (m.io_dtype == HDT_BF16) {
+    e->kv_per_head = kv_per_head(m);
+    e->kv_ladder = kv_ladder(max_cap, e->kv_per_head);
+  }
   for (int i = 0; i < n_slots; ++i) {
     SlotState &s = e->slots[i];
     s.d = slots[i];
-    s.split = split_for(s.d.capacity, std::max(1, m.attn_hkv), m.io_dtype == HDT_BF16, kv_row_groups(m));
-    s.nsplit_cap = static_cast<int32_t>((s.d.capacity + s.split - 1) / s.split);
+    if (m.io_dtype == HDT_BF16) {  // splits per row position: at most per_head of them
+      s.split = 0;
+      s.nsplit_cap = static_cast<int32_t>(e->kv_per_head);
+    } else {
+      s.split = split_for(s.d.capacity, std::max(1, m.attn_hkv));
+      s.nsplit_cap = static_cast<int32_t>((s.d.capacity + s.split - 1) / s.split);
+    }
   }
   *out = e;
   return HDT_OK;
@@ -786,9 +870,11 @@ hdt_status hdt_tree_meta(int32_t n, const int32_t *parent, int64_t L, int32_t *d
   return HDT_OK;
 }
 
-hdt_status hdt_split_size(const hdt_engine *e, int32_t slot, int64_t *out) {
+hdt_status hdt_split_size(const hdt_engine *e, int32_t slot, int64_t position, int64_t *out) {
   if (!e || !out || slot < 0 || slot >= static_cast<int32_t>(e->slots.size())) return HDT_E_INVALID;
-  *out = e->slots[slot].split;
+  const SlotState &s = e->slots[slot];
+  if (position < 0 || position >= s.d.capacity) return HDT_E_INVALID;
+  *out = e->desc.io_dtype == HDT_BF16 ? kv_split_of(e, position + 1) : s.split;
   return HDT_OK;
 }
 

@@ -26,9 +26,10 @@
 // A row's result is a function of its query and of the key/value sequence by
 // absolute position only (the verified row equals the decode step's row, "Adding
 // a model", step 4 of "The adapter path in ten steps"):
-//  - tiles and splits are anchored at absolute positions; a tile is processed by
-//    the same instruction sequence in both kernels, and an MFMA output column
-//    depends on its own row only;
+//  - tiles and splits are anchored at absolute positions, and a row's split size is
+//    a function of its own position; a tile is processed by the same instruction
+//    sequence in both kernels, and an MFMA output column depends on its own row
+//    only;
 //  - masked slots hold a finite row (the node's own) and get probability 0;
 //  - the running max moves only when a tile exceeds it by more than kLazyMax, a
 //    rule that depends on the row's scores alone;
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
   const int h = pair / T.a_splits, s = pair % T.a_splits;
   const bool carry = s == T.n_full;  // the tiles of split n_full below tb0
   const int G = P.hq / P.hkv;
-  const int M = T.n * G;
+  const int M = T.gn * G;  // rows of the group: (group node, q head)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, ln = lane & 15;
   const int split_tiles = T.split / kKvTile;
   const int ntiles = carry ? T.carry_tiles : split_tiles;
@@ -380,7 +381,10 @@ __global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       const int r = min(16 * (rblk0 + NB * wave + k) + ln, M - 1);
-      const unsigned char *qr = qb + (static_cast<int64_t>(r / G) * P.hq + h * G + r % G) * C::ROWB;
+      const int gi = r / G;
+      const int node = static_cast<int8_t>(
+          (reinterpret_cast<const uint32_t *>(T.nodes)[gi >> 2] >> (8 * (gi & 3))) & 0xFFu);
+      const unsigned char *qr = qb + (static_cast<int64_t>(node) * P.hq + h * G + r % G) * C::ROWB;
 #pragma unroll
       for (int kk = 0; kk < C::KQ; ++kk) st.q[k][kk] = *reinterpret_cast<const bf16x8 *>(qr + (4 * kk + g) * 16);
     }
@@ -518,13 +522,15 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
   __shared__ float x_ml[16][2];
   __shared__ __align__(16) float f_acc[16][QD];  // the row's last split, float32 state
   __shared__ float f_ml[16][2];
-  // grid: x = (kv head, node, column quarter) of the tree, y = tree
+  // grid: x = (kv head, node of the group, column quarter) of the tree, y = tree
   const KvTree &T = P.t[blockIdx.y];
   scalar_touch(&T, sizeof(KvTree), &P.n_trees);
   const int local = blockIdx.x;
-  if (local >= P.hkv * T.n * kKvQuarters) return;
+  if (local >= P.hkv * T.gn * kKvQuarters) return;
   const int qd = local % kKvQuarters, rest = local / kKvQuarters;
-  const int node = rest % T.n, h = rest / T.n;
+  const int gi = rest % T.gn, h = rest / T.gn;  // gi: the node's index within the group
+  const int node = static_cast<int8_t>(
+      (reinterpret_cast<const uint32_t *>(T.nodes)[gi >> 2] >> (8 * (gi & 3))) & 0xFFu);
   const int G = P.hq / P.hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, ln = lane & 15;
   // depth by a scalar load of the 32-bit word that holds it (the tree arrays are
@@ -567,7 +573,7 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
 #pragma unroll
       for (int kk = 0; kk < C::KQ; ++kk) st.q[0][kk] = *reinterpret_cast<const bf16x8 *>(qrow + (32 * kk + 8 * g) * 2);
     }
-    const int64_t crow = static_cast<int64_t>(h) * T.rows_cap + node * G + jr;
+    const int64_t crow = static_cast<int64_t>(h) * T.rows_cap + gi * G + jr;
     const float2 cml = *reinterpret_cast<const float2 *>(T.carry_ml + crow * 2);
     floatx4 cacc[QDB];
 #pragma unroll
@@ -678,7 +684,7 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
   const int items = G * QO;
   const bool fold_lane = wave > 0 && it < items;
   const int r = min(it / QO, G - 1), co = it % QO;
-  const int R = node * G + r;
+  const int R = gi * G + r;
   const int col = qd * QD + 8 * co;
   const int s_lo = min(sq * per, n_nl), s_hi = min(s_lo + per, n_nl);
   Fold8 acc8;

@@ -114,16 +114,19 @@ struct AttnLaunch {
 };
 
 // ---------------------------------------------------------------- attention, bf16 storage
-// Positions are cut into splits of `split` keys (a multiple of kKvTile fixed by the
-// slot's capacity) and splits into kKvTile-key tiles, both anchored at absolute
-// positions.  The split pass (kv_split_kernel) streams every split wholly below L
-// for all (node, q head) rows of a kv head and writes one normalised fp16 partial
-// per (row, split); it also runs the tiles of split n_full = L / split that lie
-// below tb0 = kKvTile * (L / kKvTile) and leaves their float32 running state (the
-// carry).  The tree pass (kv_tree_kernel) takes one (kv head, node, column
-// quarter): it continues from the carry through the tiles from tb0 to the node's
-// own position, whose rows at or past L are the node's ancestors, and folds every
-// split of the row in ascending order.
+// Positions are cut into splits of `split` keys and splits into kKvTile-key tiles,
+// both anchored at absolute positions.  A row's split size is a function of its own
+// position (the number of keys it sees), so the nodes of one tree can fall on two
+// split sizes; each launch pair then covers one group of nodes that share a split
+// size (`nodes`, `gn`), and a second pair covers the rest.  The split pass
+// (kv_split_kernel) streams every split wholly below L for all (node, q head) rows
+// of the group's nodes of a kv head and writes one normalised fp16 partial per
+// (row, split); it also runs the tiles of split n_full = L / split that lie below
+// tb0 = kKvTile * (L / kKvTile) and leaves their float32 running state (the carry).
+// The tree pass (kv_tree_kernel) takes one (kv head, node, column quarter): it
+// continues from the carry through the tiles from tb0 to the node's own position,
+// whose rows at or past L are the node's ancestors, and folds every split of the
+// row in ascending order.  Partial and carry rows are numbered within the group.
 struct KvTree {
   const void *q;                          // [n][hq][D]
   const void *kt, *vt;                    // tree rows [n][hkv][D]
@@ -134,8 +137,9 @@ struct KvTree {
   float *carry_acc;                       // [hkv][rows_cap][D]
   float *carry_ml;                        // [hkv][rows_cap][2]
   int64_t L, cap;
-  int32_t n;
-  int32_t split;                          // keys per split
+  int32_t n;                              // nodes of the tree
+  int32_t gn;                             // nodes of this launch's group
+  int32_t split;                          // keys per split of the group's rows
   int32_t nsplit_cap, rows_cap;
   int32_t n_full;                         // splits wholly below L
   int32_t carry_tiles;                    // tiles of split n_full below tb0
@@ -143,6 +147,7 @@ struct KvTree {
   int32_t a_splits;                       // split pass: splits per kv head (n_full, + 1 with a carry)
   alignas(4) int8_t parent[kMaxNodes];    // read as 32-bit words
   alignas(4) int8_t depth[kMaxNodes];
+  alignas(4) int8_t nodes[kMaxNodes];     // tree index of the group's i-th node
 };
 
 struct KvLaunch {

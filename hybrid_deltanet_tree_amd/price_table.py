@@ -7,7 +7,7 @@ the device; "Adding a model" ("The adapter path in ten steps", the data-files st
 one such price file per model profile and device.  This module measures those prices and
 writes them as JSON, one entry per (n_nodes, context, slots):
 
-  python -m hybrid_deltanet_tree_amd.price_table --out prices/mi355x.json
+  python -m hybrid_deltanet_tree_amd.price_table --out hybrid_deltanet_tree_amd/prices/hybrid64_bf16.mi355x.json
 
 Timing only: resident K/V rows are unit-norm random vectors, the state random; every slot
 holds the same context, and each tree is a chain of up to 12 nodes with runs of two hung
@@ -17,6 +17,7 @@ commit_ms is the median eager commit_tree of the tree's deepest root path on slo
 """
 import argparse
 import json
+import os
 import statistics
 import time
 
@@ -152,8 +153,12 @@ def make_slots(n_slots, cap, seed):
     return mem
 
 
-def load(path: str) -> dict:
-    with open(path) as f:
+PRICE_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "prices")
+
+
+def load(path: str = None) -> dict:
+    """A price file; by default the one measured on MI355X for the 64-layer bf16 stack."""
+    with open(path or os.path.join(PRICE_DIR, "hybrid64_bf16.mi355x.json")) as f:
         return json.load(f)
 
 
@@ -200,7 +205,9 @@ def main():
                 r = measure(n, L, ns, mem, args.reps, args.warmup)
                 rows.append(r)
                 print(json.dumps(r), flush=True)
-    out = {"device": torch.cuda.get_device_name(0),
+    props = torch.cuda.get_device_properties(0)
+    out = {"device": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", ""),
+           "compute_units": props.multi_processor_count,
            "model": "64 layers, 3:1 (48 Gated DeltaNet: 16 qk / 32 v heads, dk = dv = 128, fp32 state; "
                     "16 attention: 24 q / 4 kv heads, D = 256); bf16 activations and K/V",
            "timing": f"verify_ms: median of {args.reps} HIP graph replays of one joint "

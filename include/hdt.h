@@ -230,14 +230,18 @@ hdt_status hdt_tree_meta(int32_t n, const int32_t *parent, int64_t L, int32_t *d
                          uint64_t *mask, int32_t *anc, int64_t *pos);
 
 /*
- * Attention split size of a slot: the resident keys are cut into splits of this
- * many positions anchored at position 0, each reduced on its own and folded in
- * ascending order.  It depends only on the slot's capacity and, for bf16 storage,
- * on the engine's max_nodes (a tree of more than 96 query rows per kv head takes
- * several row groups per split), all fixed at create, so a row's bits depend only
- * on its inputs.  Errors: HDT_E_INVALID.
+ * Attention split size of the row at `position` (0 <= position < capacity) of a
+ * slot: the keys 0..position are cut into splits of this many positions anchored
+ * at position 0, each reduced on its own and folded in ascending order.  With
+ * bf16 storage it depends only on the position and the engine's shape (attn_hkv
+ * and max_nodes: a tree of more than 96 query rows per kv head takes several row
+ * groups per split): the smallest rung of 128, then s + max(32, s/32) rounded up
+ * to 32, ... that cuts position + 1 keys into at most 256 / (attn_hkv row_groups)
+ * splits.  With float32 storage it depends only on the slot's capacity.  Either
+ * way a row's bits depend only on its inputs, never on how many of its keys were
+ * committed.  Errors: HDT_E_INVALID.
  */
-hdt_status hdt_split_size(const hdt_engine *eng, int32_t slot, int64_t *out);
+hdt_status hdt_split_size(const hdt_engine *eng, int32_t slot, int64_t position, int64_t *out);
 
 /*
  * Kernel timing for measurement.  hdt_profile(eng, 1) starts recording a HIP

@@ -161,37 +161,59 @@ def test_sequencing_rules_without_pending_round():
         e.kv_length(5)
 
 
-def test_split_size_depends_on_capacity_only():
-    # bf16 storage: the smallest multiple of 32 keys (at least 128) for which a full
-    # cache gives at most 256 (kv head, split, row group) items, a row group being 96
-    # query rows of the engine's largest tree; float32: a power of two.
+def _ladder_next(s):
+    return (s + max(32, s // 32) + 31) // 32 * 32
+
+
+def test_split_size_depends_on_position_only():
+    # bf16 storage: a row at position p (p + 1 keys) takes the smallest rung of the
+    # ladder 128, s + max(32, s/32) rounded up to 32, ... that cuts its keys into at most
+    # 256 / (H_kv row_groups) splits, a row group being 96 query rows of the engine's
+    # largest tree.  The slot's capacity and committed length never enter.
     e = make_engine()
-    assert e.split_size(0) == 128 and e.split_size(1) == 128
+    assert e.split_size(0, 0) == 128 and e.split_size(1, 299) == 128
     big = [dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=65536 + 1024, length=65536),
            dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=262144 + 1024, length=0)]
     e2 = make_engine(attn_hkv=4, attn_hq=24, attn_d=256, slots=big)
-    assert e2.split_size(0) == 1056 and e2.split_size(1) == 4128
+    assert e2.split_size(0, 65536) == 1056 and e2.split_size(1, 65536) == 1056
+    assert e2.split_size(0, 65535) == 1024 and e2.split_size(1, 262144) == 4160
+    assert e2.split_size(1, 8192) == 160 and e2.split_size(1, 0) == 128
     e2.reset(0, 5)
-    assert e2.split_size(0) == 1056
-    for cap in (1, 127, 4096, 65536 + 600, 131072, 262144 + 999, 1 << 20):
-        for hkv in (1, 2, 4, 8):
-            slot = [dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=cap, length=0)]
-            s = make_engine(attn_hkv=hkv, attn_hq=hkv * 2, slots=slot).split_size(0)
-            assert s % 32 == 0 and s >= 128
-            assert hkv * -(-cap // s) <= 256 or s == 128
-            assert s == 128 or hkv * -(-cap // (s - 32)) > 256
+    assert e2.split_size(0, 65536) == 1056
+    with pytest.raises(hdt.HdtError):
+        e2.split_size(0, 65536 + 1024)
+    with pytest.raises(hdt.HdtError):
+        e2.split_size(0, -1)
+    # invariants over positions and shapes: a rung of the ladder, at most per_head
+    # splits, the rung below would need more, nondecreasing in the position
+    for hkv, mn in ((1, 8), (2, 8), (4, 16), (4, 17), (4, 33), (8, 64), (4, 64)):
+        rg = -(-(mn * 2) // 96) if hkv != 4 else -(-(mn * 6) // 96)
+        hq = hkv * (6 if hkv == 4 else 2)
+        slot = [dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=1 << 20, length=0)]
+        eng = make_engine(attn_hkv=hkv, attn_hq=hq, attn_d=256 if hkv == 4 else 64, max_nodes=mn,
+                          slots=slot)
+        per_head = max(1, 256 // (hkv * rg))
+        rungs, x = set(), 128
+        while x < (1 << 21):
+            rungs.add(x)
+            x = _ladder_next(x)
+        prev = 0
+        for pos in (0, 1, 127, 128, 4095, 8191, 65535, 65536, 65537, 131071, 262143, 262144,
+                    (1 << 20) - 1):
+            sz = eng.split_size(0, pos)
+            k = pos + 1
+            assert sz in rungs and sz >= prev
+            assert -(-k // sz) <= per_head
+            assert sz == 128 or -(-k // max(r for r in rungs if r < sz)) > per_head
+            prev = sz
     # 32-node trees at 6 q heads per kv head: 192 rows, two row groups per split
     e3 = make_engine(attn_hkv=4, attn_hq=24, attn_d=256, max_nodes=32, slots=big)
-    assert e3.split_size(0) == 2080 and e3.split_size(1) == 8224
-    for mn in (1, 16, 17, 33, 64):
-        rg = -(-(mn * 6) // 96)
-        s = make_engine(attn_hkv=4, attn_hq=24, attn_d=256, max_nodes=mn, slots=big[1:]).split_size(0)
-        assert s % 32 == 0 and 4 * rg * -(-(262144 + 1024) // s) <= 256
-        assert 4 * rg * -(-(262144 + 1024) // (s - 32)) > 256
+    assert e3.split_size(1, 262144) == 8384 and e3.split_size(0, 65536) == 2080
+    # float32 storage: per slot, from the capacity alone (a power of two)
     f32 = make_engine(io_dtype=hdt.HDT_F32, slots=big[:1])
-    assert f32.split_size(0) == 512
+    assert f32.split_size(0, 0) == 512 and f32.split_size(0, 65000) == 512
     f32b = make_engine(io_dtype=hdt.HDT_F32, attn_hkv=4, attn_hq=8, slots=big)
-    assert f32b.split_size(0) == 1024 and f32b.split_size(1) == 4096
+    assert f32b.split_size(0, 7) == 1024 and f32b.split_size(1, 7) == 4096
 
 
 def test_one_hip_runtime_in_process():

@@ -114,7 +114,7 @@ def test_stack65k_slice_at_full_size():
     _say(f"stack_65k slice: L={w.lengths[0]} nodes={len(parent)} capacity={cap}")
     inst = Instance(w, SEED, trees=[parent], capacity=[cap])
     eng = inst.engine(max_nodes=len(parent))
-    assert eng.split_size(0) == 1056
+    assert eng.split_size(0, w.lengths[0]) == 1056
     eng.forward_tree([inst.tree_arg(0)], gu.stream())
     gu.sync()
     for l in range(3):

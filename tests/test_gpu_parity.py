@@ -61,7 +61,7 @@ def test_two_row_groups_match_oracle(L):
     (on one XCD), with the split size scaled to keep one wave of workgroups."""
     inst = Instance(RG2, SEED, lengths=[L])
     eng = inst.engine(max_nodes=20)
-    assert eng.split_size(0) % 32 == 0
+    assert eng.split_size(0, L) % 32 == 0
     run_verify(inst, eng)
     got = gu.outputs(inst, 0)
     for l in range(len(RG2.layer_kind)):
@@ -142,7 +142,7 @@ def decode_rows_along(inst, eng, node, s=0):
 
 @pytest.mark.parametrize("wname,L,tree", [("tiny", 256, "chain"), ("tiny", 250, "random"),
                                           ("mini", 1000, "draft"), ("mini", 1275, "draft"),
-                                          ("rg2", 1300, "draft")])
+                                          ("rg2", 1300, "draft"), ("mini", 8185, "draft")])
 def test_verify_row_equals_decode_row(wname, L, tree):
     w = {"mini": MINI, "rg2": RG2}.get(wname) or W[wname]
     parent = synth.chain_tree(8) if tree == "chain" else w.tree(SEED + L)
@@ -178,6 +178,56 @@ def test_committed_state_equals_decoded_state():
     assert torch.equal(inst.state[0], committed[0])
     assert torch.equal(inst.kc[0][:, :, :1000 + len(path)], committed[1][:, :, :1000 + len(path)])
     assert torch.equal(inst.vc[0][:, :, :1000 + len(path)], committed[2][:, :, :1000 + len(path)])
+
+
+@pytest.mark.parametrize("L", [8185, 8190])
+def test_rows_straddling_a_split_rung(L):
+    """A tree whose rows straddle a rung of the split ladder: at 64 splits per kv head,
+    rows that see up to 8,192 keys take 128-key splits and deeper rows 160-key splits, so
+    the layer runs two launch pairs, one per node group.  Both groups match the oracle."""
+    inst = Instance(MINI, SEED, lengths=[L])
+    eng = inst.engine()
+    d = synth.depths(inst.trees[0])
+    assert {eng.split_size(0, L + x) for x in d} == {128, 160}
+    run_verify(inst, eng)
+    got = gu.outputs(inst, 0)
+    for l in range(len(MINI.layer_kind)):
+        gu.check_layer(inst, 0, l, got[l])
+    eng.close()
+
+
+def test_capacity_does_not_change_bits():
+    """The same tree at the same length in slots of very different capacity: the split
+    size follows each row's position, so every output bit is the same."""
+    outs = []
+    for cap in (1000 + 64, 1 << 17):
+        inst = Instance(MINI, SEED, lengths=[1000], capacity=[cap])
+        eng = inst.engine()
+        run_verify(inst, eng)
+        outs.append(gu.raw_outputs(inst, 0))
+        eng.close()
+    for l in range(len(MINI.layer_kind)):
+        assert np.array_equal(outs[0][l], outs[1][l]), f"layer {l}"
+
+
+def test_joint_with_a_straddling_tree_equals_lone():
+    w = synth.Workload("joint_straddle", [0, 1, 0, 1], 16, 32, 128, 128, 24, 4, 256, "bf16",
+                       [8185, 1000], 16, "draft")
+    inst = Instance(w, SEED)
+    eng = inst.engine()
+    snap = gu.snapshot(inst)
+    run_verify(inst, eng)
+    joint = [gu.raw_outputs(inst, s) for s in range(2)]
+    for s in range(2):
+        eng.rollback_to(s, inst.lengths[s])
+    for s in range(2):
+        gu.restore(inst, snap)
+        run_verify(inst, eng, slots=[s])
+        lone = gu.raw_outputs(inst, s)
+        eng.rollback_to(s, inst.lengths[s])
+        for l in range(len(w.layer_kind)):
+            assert np.array_equal(lone[l], joint[s][l]), f"slot {s} layer {l}"
+    eng.close()
 
 
 def test_joint_equals_lone():

@@ -56,3 +56,23 @@ def test_lookup_rounds_up_and_clamps():
         pt.lookup(t, 33, 3000, 1)
     with pytest.raises(KeyError):
         pt.lookup(t, 4, 3000, 5)
+
+
+def test_shipped_price_file():
+    # the MI355X price file of the 64-layer bf16 stack: a full grid, positive prices that
+    # grow with the context (measurement noise aside)
+    t = pt.load()
+    rows = t["entries"]
+    grid = {(r["n_nodes"], r["context"], r["slots"]) for r in rows}
+    ns = sorted({r["n_nodes"] for r in rows})
+    Ls = sorted({r["context"] for r in rows})
+    ss = sorted({r["slots"] for r in rows})
+    assert len(grid) == len(rows) == len(ns) * len(Ls) * len(ss)
+    assert ns[0] == 1 and ns[-1] >= 32 and Ls[-1] >= 262144 and ss == [1, 2, 4]
+    for r in rows:
+        assert 0 < r["verify_p10_ms"] <= r["verify_ms"] <= r["verify_p90_ms"]
+        assert 0 < r["commit_ms"] < r["verify_ms"]
+    for n in ns:
+        for s in ss:
+            v = [pt.lookup(t, n, L, s) for L in Ls]
+            assert all(b >= 0.98 * a for a, b in zip(v, v[1:])), (n, s, v)
