@@ -278,3 +278,31 @@ def gdn_conv_layer(parent, S_base, tail, q, k, v, alpha, beta, W, scale=None, wa
     qc, kc, vc = (to_storage(x, q) for x in gdn_conv(parent, tail, q, k, v, W))
     out = gdn_tree(parent, S_base, qc, kc, vc, alpha, beta, scale=scale, want_states=want_states)
     return out, (qc, kc, vc)
+
+
+def greedy_walk(parent, draft, target):
+    """The round's accept rule ("One request, end to end", 2.6: walk the verified tree with
+    the model's own tokens, keep the longest agreeing path plus one token of the model's
+    own).  draft[i] is node i's token (the root's is the model's own token from the last
+    round and is not compared); target[i] is the model's own next token after node i.
+    The root agrees; node i > 0 agrees when its parent agrees and draft[i] equals
+    target[parent[i]].  The accepted node is the deepest agreeing node, the lowest index
+    among equals; returns (its root path, target of that node = the bonus token)."""
+    n = len(parent)
+    depth = [0] * n
+    agree = [False] * n
+    agree[0] = True
+    for i in range(1, n):
+        p = parent[i]
+        depth[i] = depth[p] + 1
+        agree[i] = agree[p] and int(draft[i]) == int(target[p])
+    best = 0
+    for i in range(n):
+        if agree[i] and depth[i] > depth[best]:
+            best = i
+    path = []
+    x = best
+    while x >= 0:
+        path.append(x)
+        x = parent[x]
+    return path[::-1], int(target[best])

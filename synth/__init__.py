@@ -343,3 +343,40 @@ def conv_tail(w: Workload, seed: int, slot: int, layer: int) -> np.ndarray:
     width = conv_width(w)
     return fill(seed, f"{w.name}/s{slot}/l{layer}/conv_tail", NORMAL,
                 (max(width - 1, 1), conv_channels(w)), dtype=w.dtype)[:width - 1]
+
+
+# --------------------------------------------------------------------------------------------
+# Tokens of a round: each node's draft token and the model's own next token after it
+# --------------------------------------------------------------------------------------------
+
+def round_tokens(seed: int, name: str, parent, vocab: int = 151_936, agree: float = 0.7,
+                 distinct: bool = True):
+    """(draft[n], target[n]) int32.  Draft tokens are uniform over the vocabulary (distinct
+    among siblings unless distinct=False); the model's own token after node x is, with
+    probability `agree`, the draft token of one of x's children (uniform among them), else
+    a uniform token."""
+    s = _Stream(seed, name)
+    n = len(parent)
+    if distinct and n > vocab:
+        raise ValueError("distinct sibling tokens need a vocabulary of at least n tokens")
+    draft = np.zeros(n, np.int32)
+    children = [[] for _ in range(n)]
+    for i in range(1, n):
+        children[parent[i]].append(i)
+    draft[0] = s.uint(0, vocab - 1)
+    for x in range(n):
+        used = set()
+        for c in children[x]:
+            t = s.uint(0, vocab - 1)
+            while distinct and t in used:
+                t = s.uint(0, vocab - 1)
+            used.add(t)
+            draft[c] = t
+    target = np.zeros(n, np.int32)
+    thresh = int(agree * 1_000_000)
+    for x in range(n):
+        if children[x] and s.uint(0, 999_999) < thresh:
+            target[x] = draft[children[x][s.uint(0, len(children[x]) - 1)]]
+        else:
+            target[x] = s.uint(0, vocab - 1)
+    return draft, target

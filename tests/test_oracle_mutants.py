@@ -76,3 +76,34 @@ def test_mutant_is_caught(name, tmp_path, monkeypatch):
         except (AssertionError, ValueError):
             failed.append(pin)
     assert failed, f"no pin catches the mutant {name}"
+
+
+# The accept walk lives in oracle/__init__.py (plain Python): its mutants are the function's
+# source with one edit, executed in the oracle module's namespace.
+WALK_MUTANTS = {
+    "walk_tie_to_highest_index": ("if agree[i] and depth[i] > depth[best]:",
+                                  "if agree[i] and depth[i] >= depth[best]:"),
+    "walk_compares_own_target": ("int(draft[i]) == int(target[p])", "int(draft[i]) == int(target[i])"),
+    "walk_ignores_parent": ("agree[i] = agree[p] and int(draft[i])", "agree[i] = int(draft[i])"),
+    "walk_bonus_is_draft": ("return path[::-1], int(target[best])", "return path[::-1], int(draft[best])"),
+    "walk_path_unreversed": ("return path[::-1], int(target[best])", "return path, int(target[best])"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WALK_MUTANTS))
+def test_walk_mutant_is_caught(name, monkeypatch):
+    import inspect
+    import textwrap
+    old, new = WALK_MUTANTS[name]
+    src = textwrap.dedent(inspect.getsource(oracle.greedy_walk))
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    ns = dict(vars(oracle))
+    exec(src.replace(old, new), ns)
+    monkeypatch.setattr(oracle, "greedy_walk", ns["greedy_walk"])
+    failed = []
+    for pin in ("walk_hand_examples", "walk_brute_and_greedy_descent"):
+        try:
+            pins.PINS[pin]()
+        except (AssertionError, ValueError, IndexError):
+            failed.append(pin)
+    assert failed, f"no pin catches the mutant {name}"

@@ -368,6 +368,52 @@ def pin_storage_rounding():
     assert oracle.to_storage(x, x) is not None and np.array_equal(oracle.to_storage(x, x), x)
 
 
+# ---------------------------------------------------------------------------------------------
+# The accept walk
+# ---------------------------------------------------------------------------------------------
+
+def pin_walk_hand_examples():
+    g = json.load(open(os.path.join(GOLDEN, "walk_hand_example.json")))
+    for c in g["cases"]:
+        path, bonus = oracle.greedy_walk(c["parent"], c["draft"], c["target"])
+        assert path == c["path"] and bonus == c["bonus"], c["name"]
+
+
+def _walk_brute(parent, draft, target):
+    """Every root path, kept when each of its edges agrees; the longest wins, then the
+    lowest last node."""
+    best = None
+    for x in range(len(parent)):
+        path = synth.root_path(parent, x)
+        if all(int(draft[c]) == int(target[p]) for p, c in zip(path, path[1:])):
+            if best is None or len(path) > len(best):
+                best = path
+    return best, int(target[best[-1]])
+
+
+def pin_walk_brute_and_greedy_descent():
+    for seed in range(40):
+        n = 1 + seed % 33
+        parent = synth.random_tree(seed, "pin/walk", n, 1 + seed % 9)
+        draft, target = synth.round_tokens(seed, "pin/walk/tokens", parent, vocab=4 + seed % 5,
+                                           agree=0.8, distinct=False)
+        got = oracle.greedy_walk(parent, draft, target)
+        assert got == _walk_brute(parent, draft, target), seed
+    # distinct sibling tokens: the walk is the plain greedy descent
+    for seed in range(20):
+        parent = synth.draft_tree(seed, "pin/walk/draft", 16)
+        draft, target = synth.round_tokens(seed, "pin/walk/draft/tokens", parent)
+        x = 0
+        while True:
+            nxt = [c for c in range(len(parent)) if parent[c] == x and draft[c] == target[x]]
+            assert len(nxt) <= 1
+            if not nxt:
+                break
+            x = nxt[0]
+        assert oracle.greedy_walk(parent, draft, target) == (synth.root_path(parent, x),
+                                                             int(target[x]))
+
+
 PINS = {name[4:]: fn for name, fn in list(globals().items()) if name.startswith("pin_")}
 
 
