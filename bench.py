@@ -165,6 +165,9 @@ def main():
     ap.add_argument("--seed", type=int, default=20261202)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time the eager pass only")
+    ap.add_argument("--walk", action="store_true",
+                    help="close each round with the on-device accept walk + commit (walk_commit) "
+                         "on seeded tokens that accept the same path, instead of commit_tree")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     args = ap.parse_args()
@@ -207,10 +210,23 @@ def main():
     def lens():
         return [eng.kv_length(s) for s in range(ns)]
 
+    walk = []
+    if args.walk:
+        for s in range(ns):
+            d, t = synth.tokens_for_path(args.seed, f"{w.name}/bench-tokens/{s}", parents[s], paths[s])
+            walk.append([torch.from_numpy(d).cuda(), torch.from_numpy(t).cuda(),
+                         torch.zeros(2 + len(parents[s]), dtype=torch.int32, device="cuda")])
+
+    def close_round():
+        for s in range(ns):
+            if walk:
+                eng.walk_commit(s, walk[s][0], walk[s][1], walk[s][2], sp)
+            else:
+                eng.commit_tree(s, paths[s], sp)
+
     def step():
         eng.forward_tree(tree, sp)
-        for s in range(ns):
-            eng.commit_tree(s, paths[s], sp)
+        close_round()
 
     for _ in range(args.warmup):
         step()
@@ -227,8 +243,7 @@ def main():
         ev[i][0].record(stream)
         eng.forward_tree(tree, sp)
         ev[i][1].record(stream)
-        for s in range(ns):
-            eng.commit_tree(s, paths[s], sp)
+        close_round()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     verify_ms = [a.elapsed_time(b) for a, b in ev]
@@ -263,7 +278,7 @@ def main():
     for i in range(args.steps):
         lengths.append(lens())
         step()
-    prof = {k: eng.profile_read(k) for k in (0, 1, 2, 3, 4)}
+    prof = {k: eng.profile_read(k) for k in (0, 1, 2, 3, 4, 5)}
     eng.profile(False)
 
     import statistics
@@ -288,7 +303,7 @@ def main():
     kernels = {name: {"avg_us": round(1e3 * prof[k][0] / max(1, prof[k][1]), 2),
                       "launches_per_step": prof[k][1] // args.steps}
                for k, name in ((0, "gdn_tree"), (1, "attn_split"), (2, "attn_tree"), (3, "commit"),
-                               (4, "gdn_conv")) if prof[k][1] > 0}
+                               (4, "gdn_conv"), (5, "walk")) if prof[k][1] > 0}
 
     traffic = None   # measured bytes are stale once the kernels change
     if args.workload == "stack_65k" and os.path.exists(TRAFFIC_FILE):
@@ -312,7 +327,9 @@ def main():
                 "and weights excluded" + ("; conv taps synthetic N(0, 1/width)"
                                           if synth.conv_width(w) else ""),
         "config": {"workload": (f"{w.name}: {w.n_gdn} GDN + {w.n_attn} attention layers (3:1), "
-                                f"{L0} resident tokens, {n}-node draft tree, commit of {len(path)}"
+                                f"{L0} resident tokens, {n}-node draft tree, "
+                                + ("on-device accept walk + commit" if args.walk else "commit")
+                                + f" of {len(path)}"
                                 + (f"; width-{synth.conv_width(w)} causal conv in front of every "
                                    "GDN layer" if synth.conv_width(w) else ""))
                    if ns == 1 else

@@ -23,7 +23,7 @@ HDT_MAX_TREES = 8
 HDT_F32, HDT_BF16 = 0, 1
 STATUS = {0: "HDT_OK", -1: "HDT_E_INVALID", -2: "HDT_E_TREE", -3: "HDT_E_PATH",
           -4: "HDT_E_CAPACITY", -5: "HDT_E_ORDER", -6: "HDT_E_HIP", -7: "HDT_E_UNSUPPORTED"}
-KIND_GDN, KIND_ATTN_SPLIT, KIND_ATTN_FOLD, KIND_COMMIT, KIND_CONV = 0, 1, 2, 3, 4
+KIND_GDN, KIND_ATTN_SPLIT, KIND_ATTN_FOLD, KIND_COMMIT, KIND_CONV, KIND_WALK = 0, 1, 2, 3, 4, 5
 
 # PyTorch owns the device memory and the streams, so libhdt must run on the same
 # HIP runtime instance.  PyTorch ships its own libamdhip64 under the same soname;
@@ -78,6 +78,8 @@ _sigs = {
     "hdt_commit_tree": (_S, [_E, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
                              ctypes.c_void_p]),
     "hdt_rollback_to": (_S, [_E, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p]),
+    "hdt_walk_commit": (_S, [_E, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                             ctypes.c_void_p]),
     "hdt_kv_length": (_S, [_E, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]),
     "hdt_reset": (_S, [_E, ctypes.c_int32, ctypes.c_int64]),
     "hdt_tree_meta": (_S, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int64,
@@ -199,6 +201,11 @@ class Engine:
 
     def rollback_to(self, slot, n, stream=0):
         self._check(hdt_rollback_to(self.h, slot, n, stream))
+
+    def walk_commit(self, slot, draft, target, out, stream=0):
+        """Accept walk + commit on the device: draft, target int32 [n], out int32 [2 + n]
+        (m, bonus token, path)."""
+        self._check(hdt_walk_commit(self.h, slot, _ptr(draft), _ptr(target), _ptr(out), stream))
 
     def kv_length(self, slot) -> int:
         out = ctypes.c_int64()

@@ -45,6 +45,8 @@ struct SlotState {
   void *conv_out = nullptr;   // GDN conv: post-conv q | k | v of one layer [max_nodes][..] each
   void *x_pend = nullptr;     // GDN conv: pre-conv rows of the tree [n_gdn][max_nodes][C]
   bool pending = false;
+  bool walk_pending = false;  // an accept walk's commit is in flight: length not yet known
+  hipEvent_t walk_ev = nullptr;
   int32_t n = 0;
   int32_t chain = 0;
   int8_t parent[kMaxNodes]{};
@@ -72,10 +74,11 @@ struct hdt_engine {
   std::vector<EventPair> ev_live;
   std::vector<EventPair> ev_pool;
   int32_t conv_C = 0;  // channels through the GDN conv: 2 hk dk + hv dv
+  int32_t *walk_m = nullptr;      // pinned host copy of each slot's last accept-walk length
   int64_t kv_per_head = 1;        // bf16 attention: most splits a row may have
   std::vector<int32_t> kv_ladder;  // bf16 attention: split sizes, ascending
-  double prof_ms[5] = {0, 0, 0, 0, 0};
-  int64_t prof_count[5] = {0, 0, 0, 0, 0};
+  double prof_ms[6] = {0, 0, 0, 0, 0, 0};
+  int64_t prof_count[6] = {0, 0, 0, 0, 0, 0};
 };
 
 namespace {
@@ -214,6 +217,11 @@ hdt_status ensure_alloc(hdt_engine *e) {
       }
     }
   }
+  if (hipHostMalloc(reinterpret_cast<void **>(&e->walk_m), e->slots.size() * sizeof(int32_t)) != hipSuccess)
+    return fail(e, HDT_E_HIP, "hipHostMalloc of the walk results failed");
+  for (auto &s : e->slots)
+    if (hipEventCreateWithFlags(&s.walk_ev, hipEventDisableTiming) != hipSuccess)
+      return fail(e, HDT_E_HIP, "hipEventCreate failed");
   e->allocated = true;
   return HDT_OK;
 }
@@ -230,10 +238,14 @@ void free_scratch(hdt_engine *e) {
     (void)hipFree(s.carry_ml);
     (void)hipFree(s.conv_out);
     (void)hipFree(s.x_pend);
+    if (s.walk_ev) (void)hipEventDestroy(s.walk_ev);
+    s.walk_ev = nullptr;
     s.u_pend = nullptr;
     s.k_pend = s.a_pend = s.part_o = s.conv_out = s.x_pend = nullptr;
     s.part_acc = s.part_ml = s.carry_acc = s.carry_ml = nullptr;
   }
+  if (e->walk_m) (void)hipHostFree(e->walk_m);
+  e->walk_m = nullptr;
   e->allocated = false;
 }
 
@@ -557,8 +569,11 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
   return HDT_OK;
 }
 
+// Commits a root path of the pending tree: from the host (path, m_len), or, with
+// dev_out set, from the accept walk's output in device memory (m_len is then the
+// tree's node count, the most the path can hold); the caller updates the length.
 hdt_status do_commit(hdt_engine *e, int32_t slot, const int32_t *path, int32_t m_len,
-                     hipStream_t stream) {
+                     const int32_t *dev_out, hipStream_t stream) {
   const hdt_model_desc &m = e->desc;
   SlotState &s = e->slots[slot];
   CommitLaunch c;
@@ -592,7 +607,9 @@ hdt_status do_commit(hdt_engine *e, int32_t slot, const int32_t *path, int32_t m
     conv_blocks = e->n_gdn * c.conv_blocks_per_layer;
   }
   c.m = m_len;
-  for (int d = 0; d < m_len; ++d) c.path[d] = static_cast<int8_t>(path[d]);
+  c.dev_out = dev_out;
+  if (!dev_out)
+    for (int d = 0; d < m_len; ++d) c.path[d] = static_cast<int8_t>(path[d]);
   const int blocks = c.gdn_blocks + c.kv_blocks + conv_blocks;
   if (blocks > 0) {
     ProfScope p(e, 3);
@@ -601,8 +618,19 @@ hdt_status do_commit(hdt_engine *e, int32_t slot, const int32_t *path, int32_t m
                               "commit launch");
     if (st != HDT_OK) return st;
   }
-  s.d.length += m_len;
   s.pending = false;
+  return HDT_OK;
+}
+
+// After an accept walk, the slot's new length is known once the device has run the
+// walk: wait for it and take m from the pinned copy.
+hdt_status settle(hdt_engine *e, int32_t slot) {
+  SlotState &s = e->slots[slot];
+  if (!s.walk_pending) return HDT_OK;
+  if (hipEventSynchronize(s.walk_ev) != hipSuccess)
+    return fail(e, HDT_E_HIP, "waiting for the accept walk of slot %d failed", slot);
+  s.d.length += e->walk_m[slot];
+  s.walk_pending = false;
   return HDT_OK;
 }
 
@@ -719,6 +747,7 @@ hdt_status hdt_forward_tree(hdt_engine *e, int32_t n_trees, const hdt_tree *tree
       return fail(e, HDT_E_INVALID, "tree %d: slot %d out of range", t, tr.slot);
     for (int u = 0; u < t; ++u)
       if (trees[u].slot == tr.slot) return fail(e, HDT_E_INVALID, "slot %d appears twice", tr.slot);
+    if (settle(e, tr.slot) != HDT_OK) return HDT_E_HIP;
     const SlotState &s = e->slots[tr.slot];
     if (s.pending) return fail(e, HDT_E_ORDER, "slot %d has a pending round", tr.slot);
     if (tr.n_nodes < 1 || tr.n_nodes > m.max_nodes)
@@ -792,6 +821,7 @@ hdt_status hdt_commit_tree(hdt_engine *e, int32_t slot, const int32_t *path, int
   if (!e) return HDT_E_INVALID;
   if (slot < 0 || slot >= static_cast<int32_t>(e->slots.size()))
     return fail(e, HDT_E_INVALID, "slot %d out of range", slot);
+  if (settle(e, slot) != HDT_OK) return HDT_E_HIP;
   SlotState &s = e->slots[slot];
   if (!s.pending) return fail(e, HDT_E_ORDER, "slot %d has no pending round", slot);
   if (!path || m < 1 || m > s.n) return fail(e, HDT_E_PATH, "path length %d (tree of %d)", m, s.n);
@@ -801,15 +831,18 @@ hdt_status hdt_commit_tree(hdt_engine *e, int32_t slot, const int32_t *path, int
       return fail(e, HDT_E_PATH, "path[%d] = %d is not a child of %d", d, path[d], path[d - 1]);
   if (commit_lds_bytes(e->desc.attn_d, e->desc.io_dtype == HDT_BF16, m) > static_cast<size_t>(e->max_lds))
     return fail(e, HDT_E_UNSUPPORTED, "commit of %d rows needs more LDS than the device allows", m);
-  hdt_status st = do_commit(e, slot, path, m, static_cast<hipStream_t>(stream));
-  if (st == HDT_OK) e->err.clear();
-  return st;
+  hdt_status st = do_commit(e, slot, path, m, nullptr, static_cast<hipStream_t>(stream));
+  if (st != HDT_OK) return st;
+  s.d.length += m;
+  e->err.clear();
+  return HDT_OK;
 }
 
 hdt_status hdt_rollback_to(hdt_engine *e, int32_t slot, int64_t n, void *stream) {
   if (!e) return HDT_E_INVALID;
   if (slot < 0 || slot >= static_cast<int32_t>(e->slots.size()))
     return fail(e, HDT_E_INVALID, "slot %d out of range", slot);
+  if (settle(e, slot) != HDT_OK) return HDT_E_HIP;
   SlotState &s = e->slots[slot];
   const int64_t L = s.d.length;
   if (n < L) return fail(e, HDT_E_UNSUPPORTED, "rollback below the committed length needs state anchors");
@@ -826,13 +859,54 @@ hdt_status hdt_rollback_to(hdt_engine *e, int32_t slot, int64_t n, void *stream)
   int32_t path[HDT_MAX_NODES];
   const int32_t m = static_cast<int32_t>(n - L);
   for (int d = 0; d < m; ++d) path[d] = d;
-  hdt_status st = do_commit(e, slot, path, m, static_cast<hipStream_t>(stream));
-  if (st == HDT_OK) e->err.clear();
-  return st;
+  hdt_status st = do_commit(e, slot, path, m, nullptr, static_cast<hipStream_t>(stream));
+  if (st != HDT_OK) return st;
+  s.d.length += m;
+  e->err.clear();
+  return HDT_OK;
+}
+
+hdt_status hdt_walk_commit(hdt_engine *e, int32_t slot, const int32_t *draft, const int32_t *target,
+                           int32_t *out, void *stream) {
+  if (!e) return HDT_E_INVALID;
+  if (slot < 0 || slot >= static_cast<int32_t>(e->slots.size()))
+    return fail(e, HDT_E_INVALID, "slot %d out of range", slot);
+  if (!draft || !target || !out) return fail(e, HDT_E_INVALID, "NULL draft, target or out");
+  if ((reinterpret_cast<uintptr_t>(draft) | reinterpret_cast<uintptr_t>(target) |
+       reinterpret_cast<uintptr_t>(out)) & 3u)
+    return fail(e, HDT_E_INVALID, "token buffers must be 4-byte aligned");
+  if (settle(e, slot) != HDT_OK) return HDT_E_HIP;
+  SlotState &s = e->slots[slot];
+  if (!s.pending) return fail(e, HDT_E_ORDER, "slot %d has no pending round", slot);
+  if (commit_lds_bytes(e->desc.attn_d, e->desc.io_dtype == HDT_BF16, s.n) > static_cast<size_t>(e->max_lds))
+    return fail(e, HDT_E_UNSUPPORTED, "commit of %d rows needs more LDS than the device allows", s.n);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  WalkLaunch w;
+  std::memset(&w, 0, sizeof w);
+  w.draft = draft;
+  w.target = target;
+  w.out = out;
+  w.n = s.n;
+  for (int i = 0; i < s.n; ++i) w.anc[i] = (i == 0 ? 0 : w.anc[s.parent[i]]) | (uint64_t(1) << i);
+  {
+    ProfScope p(e, 5);
+    hdt_status r = check_hip(e, launch_walk(w, st, p.events()), "accept walk launch");
+    if (r != HDT_OK) return r;
+  }
+  hdt_status r = do_commit(e, slot, nullptr, s.n, out, st);
+  if (r != HDT_OK) return r;
+  if (hipMemcpyAsync(&e->walk_m[slot], out, sizeof(int32_t), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipEventRecord(s.walk_ev, st) != hipSuccess)
+    return fail(e, HDT_E_HIP, "recording the accept walk's length failed");
+  s.walk_pending = true;
+  e->err.clear();
+  return HDT_OK;
 }
 
 hdt_status hdt_kv_length(const hdt_engine *e, int32_t slot, int64_t *out) {
   if (!e || !out || slot < 0 || slot >= static_cast<int32_t>(e->slots.size())) return HDT_E_INVALID;
+  // waiting for an accept walk only resolves a length that is already determined
+  if (settle(const_cast<hdt_engine *>(e), slot) != HDT_OK) return HDT_E_HIP;
   *out = e->slots[slot].d.length;
   return HDT_OK;
 }
@@ -841,6 +915,7 @@ hdt_status hdt_reset(hdt_engine *e, int32_t slot, int64_t length) {
   if (!e) return HDT_E_INVALID;
   if (slot < 0 || slot >= static_cast<int32_t>(e->slots.size()))
     return fail(e, HDT_E_INVALID, "slot %d out of range", slot);
+  if (settle(e, slot) != HDT_OK) return HDT_E_HIP;
   SlotState &s = e->slots[slot];
   if (length < 0 || length > s.d.capacity)
     return fail(e, HDT_E_INVALID, "length %lld outside [0, %lld]", (long long)length,
@@ -885,7 +960,7 @@ hdt_status hdt_profile(hdt_engine *e, int32_t enable) {
 }
 
 hdt_status hdt_profile_read(hdt_engine *e, int32_t kind, double *ms, int64_t *launches) {
-  if (!e || kind < 0 || kind > 4 || !ms || !launches) return HDT_E_INVALID;
+  if (!e || kind < 0 || kind > 5 || !ms || !launches) return HDT_E_INVALID;
   for (auto &p : e->ev_live) {
     if (hipEventSynchronize(p.b) != hipSuccess) return fail(e, HDT_E_HIP, "event wait failed");
     float t = 0.0f;

@@ -976,6 +976,28 @@ __global__ __launch_bounds__(kFoldThreads) void attn_fold_kernel(const FoldLaunc
 
 // ============================================================================ commit
 
+// The accepted path: from the launch block, or (after the accept walk) from the
+// walk's output in device memory, {m, bonus token, path[m]}.
+// A device path is read in one round trip: m by every lane, and lane j's copy of
+// path[j] (j < the tree's node count, P.m); entry d is then read from lane d.
+struct CommitPath {
+  const int8_t *host;
+  int m;
+  int pv;
+  bool dev;
+  // d is uniform over the wave
+  __device__ __forceinline__ int operator[](int d) const {
+    return dev ? __builtin_amdgcn_readlane(pv, d) : host[d];
+  }
+};
+
+__device__ __forceinline__ CommitPath load_path(const CommitLaunch &P, int lane) {
+  if (!P.dev_out) return CommitPath{P.path, P.m, 0, false};
+  const int mv = P.dev_out[0];
+  const int pv = P.dev_out[2 + min(lane, P.m - 1)];
+  return CommitPath{P.path, __builtin_amdgcn_readfirstlane(mv), pv, true};
+}
+
 template <bool BF, int DK>
 __global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch P) {
   constexpr int R = DK / 16;
@@ -997,16 +1019,17 @@ __global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch 
     const int g = lane & 15;
     float *sp = P.state + ((static_cast<int64_t>(lg) * P.hv + h) * P.dv + col) * DK + g * R;
     float cur[R];
-    lds_row<R>(sp, cur);
+    lds_row<R>(sp, cur);  // the state slice is in flight before the path is known
+    const CommitPath path = load_path(P, lane);
     const int64_t lbase = static_cast<int64_t>(lg) * P.max_nodes;
-    for (int d0 = 0; d0 < P.m; d0 += B) {
+    for (int d0 = 0; d0 < path.m; d0 += B) {
       uint32_t kw[B][KW];
       float u[B];
       io_t<BF> araw[B];
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        if (d0 + b < P.m) {
-          const int64_t nb = lbase + P.path[d0 + b];
+        if (d0 + b < path.m) {
+          const int64_t nb = lbase + path[d0 + b];
           const unsigned char *kp = static_cast<const unsigned char *>(P.k_pend) +
                                     ((nb * P.hk + qh) * DK + g * R) * ESZ;
           if constexpr (KW % 4 == 0) {
@@ -1029,7 +1052,7 @@ __global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch 
       }
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        if (d0 + b < P.m) {
+        if (d0 + b < path.m) {
           float kj[R];
 #pragma unroll
           for (int a = 0; a < R; ++a) {
@@ -1057,6 +1080,7 @@ __global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch 
     // Conv tail of one GDN layer, 16 bytes of channels per thread: the new tail is
     // the last width-1 rows of (old tail, the path's pre-conv rows), bit copies.
     // A thread reads every source of its channels before it writes any row.
+    const CommitPath path = load_path(P, tid & 63);  // every lane, before any returns
     const int cb = bid - P.gdn_blocks - P.kv_blocks;
     const int lg = cb / P.conv_blocks_per_layer;
     const int64_t row_bytes = static_cast<int64_t>(P.conv_C) * (BF ? 2 : 4);
@@ -1070,9 +1094,9 @@ __global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch 
 #pragma unroll
     for (int r = 0; r < kConvMaxWidth - 1; ++r) {
       if (r < keep) {
-        const int src = P.m + r;  // index into (old tail rows, path rows)
+        const int src = path.m + r;  // index into (old tail rows, path rows)
         rows[r] = src < keep ? *reinterpret_cast<const uint4 *>(tail + src * row_bytes)
-                             : *reinterpret_cast<const uint4 *>(xp + P.path[src - keep] * row_bytes);
+                             : *reinterpret_cast<const uint4 *>(xp + static_cast<int64_t>(path[src - keep]) * row_bytes);
       }
     }
 #pragma unroll
@@ -1084,6 +1108,10 @@ __global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch 
   // Rows are staged through LDS because a destination row may be another
   // destination's source.
   extern __shared__ __align__(16) uint4 c_lds[];
+  __shared__ int path_s[kMaxNodes];  // the path, for lanes that index it per lane
+  const CommitPath path = load_path(P, tid & 63);
+  if (tid < kMaxNodes) path_s[tid] = tid < path.m ? (path.dev ? path.pv : P.path[tid]) : 0;
+  __syncthreads();
   const int kb = bid - P.gdn_blocks;
   const int la = kb / P.hkv, hh = kb % P.hkv;
   const int esz = BF ? 2 : 4;
@@ -1091,13 +1119,13 @@ __global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch 
   for (int which = 0; which < 2; ++which) {
     unsigned char *base = static_cast<unsigned char *>(which == 0 ? P.kc : P.vc) +
                           ((static_cast<int64_t>(la) * P.hkv + hh) * P.cap + P.L) * P.D * esz;
-    for (int c = tid; c < P.m * cpr; c += kGdnThreads) {
+    for (int c = tid; c < path.m * cpr; c += kGdnThreads) {
       const int d = c / cpr, cc = c % cpr;
-      c_lds[c] = *reinterpret_cast<const uint4 *>(base + static_cast<int64_t>(P.path[d]) * P.D * esz +
+      c_lds[c] = *reinterpret_cast<const uint4 *>(base + static_cast<int64_t>(path_s[d]) * P.D * esz +
                                                   cc * 16);
     }
     __syncthreads();
-    for (int c = tid; c < P.m * cpr; c += kGdnThreads) {
+    for (int c = tid; c < path.m * cpr; c += kGdnThreads) {
       const int d = c / cpr, cc = c % cpr;
       *reinterpret_cast<uint4 *>(base + static_cast<int64_t>(d) * P.D * esz + cc * 16) = c_lds[c];
     }
@@ -1105,14 +1133,49 @@ __global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch 
   }
 }
 
+// ============================================================================ accept walk
+
+// One wave: lane i is node i.  Node i > 0 agrees when draft[i] equals the model's own
+// token after its parent and every ancestor agrees (its ancestor mask holds no
+// disagreeing node).  The deepest agreeing node, the lowest index among equals,
+// ends the path; its ancestors-or-self in index order are the path (parents have
+// lower indices); the bonus token is the model's own token after it.
+__global__ __launch_bounds__(64) void walk_kernel(const WalkLaunch W) {
+  const int lane = threadIdx.x;
+  const bool real = lane < W.n;
+  const int me = real ? lane : 0;
+  const uint64_t anc = W.anc[me];
+  const int par = lane > 0 && real ? 63 - __builtin_clzll(anc & ~(1ull << lane)) : 0;
+  const bool match = real && (lane == 0 || W.draft[lane] == W.target[par]);
+  const uint64_t ok = __ballot(match);
+  const bool agrees = real && (anc & ~ok) == 0;
+  const int depth = __popcll(anc) - 1;
+  int key = agrees ? depth * 64 + (63 - lane) : -1;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) key = max(key, __shfl_xor(key, m));
+  const int x = 63 - (key & 63);  // key >= 0: the root always agrees
+  const uint64_t path = W.anc[x];
+  const int m = __popcll(path);
+  if (lane < 64 && ((path >> lane) & 1)) W.out[2 + __popcll(path & ((1ull << lane) - 1))] = lane;
+  if (lane == 0) {
+    W.out[0] = m;
+    W.out[1] = W.target[x];
+  }
+}
+
 template <typename K>
 hipError_t set_lds(K kernel, size_t bytes) {
-  // Raised once per kernel to the largest dynamic LDS any launch asks for (the whole
-  // 160 KiB), at the first launch: later launches, graph capture included, then make
-  // no attribute call.
-  static const hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     kMaxDynamicLds);
+  // Raised once per kernel to the largest dynamic LDS any launch asks for (the 160 KiB
+  // of a workgroup less the kernel's static LDS), at the first launch: later launches,
+  // graph capture included, then make no attribute call.
+  static const hipError_t once = [kernel] {
+    hipFuncAttributes attr{};
+    hipError_t r = hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(kernel));
+    if (r != hipSuccess) return r;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               kMaxDynamicLds - static_cast<int>(attr.sharedSizeBytes));
+  }();
   (void)bytes;
   return once;
 }
@@ -1170,6 +1233,11 @@ hipError_t launch_attn_fold(const FoldLaunch &a, int D, int bf16, int n_blocks, 
   if (bf16 || D != 64) return hipErrorInvalidValue;
   hipExtLaunchKernelGGL((attn_fold_kernel<false, 64>), dim3(n_blocks), dim3(kFoldThreads), 0, s,
                         ev.start, ev.stop, 0, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_walk(const WalkLaunch &a, hipStream_t s, KernelEvents ev) {
+  hipExtLaunchKernelGGL(walk_kernel, dim3(1), dim3(64), 0, s, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 

@@ -192,6 +192,16 @@ struct CommitLaunch {
   int32_t conv_width, conv_C, conv_blocks_per_layer;
   int32_t m;
   int8_t path[kMaxNodes];
+  const int32_t *dev_out;                 // non-null: m and the path come from the accept
+                                          // walk's output {m, bonus, path[m]} instead
+};
+
+// ---------------------------------------------------------------- accept walk
+struct WalkLaunch {
+  const int32_t *draft, *target;          // [n]: each node's token; the model's own next token
+  int32_t *out;                           // [2 + n]: m, bonus token, path[m]
+  uint64_t anc[kMaxNodes];                // ancestor-or-self bits of each node
+  int32_t n;
 };
 
 // ---------------------------------------------------------------- host entry points
@@ -214,6 +224,7 @@ hipError_t launch_kv_tree(const KvLaunch &a, int D, int max_items, hipStream_t s
 hipError_t launch_commit(const CommitLaunch &a, int dk, int bf16, int n_blocks, hipStream_t s,
                          KernelEvents ev);
 hipError_t launch_gdn_conv(const ConvLaunch &a, int bf16, hipStream_t s, KernelEvents ev);
+hipError_t launch_walk(const WalkLaunch &a, hipStream_t s, KernelEvents ev);
 // Channels one conv thread handles (16 bytes of io dtype).
 constexpr int conv_channels_per_thread(int bf16) { return bf16 ? 8 : 4; }
 

@@ -212,7 +212,30 @@ hdt_status hdt_commit_tree(hdt_engine *eng, int32_t slot, const int32_t *path, i
  */
 hdt_status hdt_rollback_to(hdt_engine *eng, int32_t slot, int64_t n, void *stream);
 
-/* kv.length: committed rows of a slot (host value, no device access). */
+/*
+ * Accept walk + commit on the device, with no host wait ("One request, end to end",
+ * 2.6: the verified tree is walked with the model's own tokens, the longest agreeing
+ * path plus one token of the model's own is kept, and that path is committed).
+ *  draft: device int32 [n] token of each node of the slot's pending tree (draft[0],
+ *    the root, is the model's own token from the last round and is not compared);
+ *  target: device int32 [n], the model's own next token after each node (the argmax
+ *    of its logits, computed by the caller);
+ *  out: device int32 [2 + n] written by the walk: out[0] = m, out[1] = the bonus
+ *    token, out[2 .. 2+m) = the accepted path.
+ * Node i > 0 agrees when its parent agrees and draft[i] == target[parent[i]]; the
+ * root agrees.  The path ends at the deepest agreeing node (the lowest index among
+ * equals) and the bonus token is target[that node].  The path is then committed as
+ * hdt_commit_tree would, reading it from `out` on the device.  The slot's new
+ * length (length + m) is known to the host once the device has finished the walk:
+ * every later call on the slot (hdt_kv_length included) first waits for that.
+ * Buffers 4-byte aligned.  Not for graph capture.
+ * Errors: HDT_E_INVALID, HDT_E_ORDER (no pending round), HDT_E_HIP.
+ */
+hdt_status hdt_walk_commit(hdt_engine *eng, int32_t slot, const int32_t *draft, const int32_t *target,
+                           int32_t *out, void *stream);
+
+/* kv.length: committed rows of a slot (host value; after hdt_walk_commit it waits for
+ * the device to finish that walk). */
 hdt_status hdt_kv_length(const hdt_engine *eng, int32_t slot, int64_t *out);
 
 /* reset: set a slot's committed length (0..capacity) and drop any pending
@@ -247,7 +270,8 @@ hdt_status hdt_split_size(const hdt_engine *eng, int32_t slot, int64_t position,
  * Kernel timing for measurement.  hdt_profile(eng, 1) starts recording a HIP
  * event pair around every launch on the launch stream; hdt_profile_read waits
  * for the recorded events and returns, for kernel class `kind` (0 = GDN tree
- * walk, 1 = attention split pass, 2 = attention fold, 3 = commit, 4 = GDN conv), the summed
+ * walk, 1 = attention split pass, 2 = attention fold, 3 = commit, 4 = GDN conv,
+ * 5 = accept walk), the summed
  * milliseconds and the launch count since the last read; then clears them.
  */
 hdt_status hdt_profile(hdt_engine *eng, int32_t enable);

@@ -380,3 +380,19 @@ def round_tokens(seed: int, name: str, parent, vocab: int = 151_936, agree: floa
         else:
             target[x] = s.uint(0, vocab - 1)
     return draft, target
+
+
+def tokens_for_path(seed: int, name: str, parent, path, vocab: int = 151_936):
+    """(draft, target) whose accept walk keeps exactly `path`: round_tokens, then the
+    model's token after each path node but the last set to the next path node's draft
+    token, and after the last to a token none of its children carries."""
+    draft, target = round_tokens(seed, name, parent, vocab=vocab)
+    for a, b in zip(path, path[1:]):
+        target[a] = draft[b]
+    last = path[-1]
+    kids = {int(draft[c]) for c in range(len(parent)) if parent[c] == last}
+    t = int(target[last])
+    while t in kids:
+        t = (t + 1) % vocab
+    target[last] = t
+    return draft, target

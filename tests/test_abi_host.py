@@ -113,6 +113,20 @@ def test_forward_rejects_misaligned_conv_inputs():
     eng.close()
 
 
+def test_walk_commit_rejects_without_touching_the_device():
+    e = make_engine()
+    with pytest.raises(hdt.HdtError) as err:
+        e.walk_commit(0, FAKE, FAKE, FAKE)
+    assert err.value.status == -5  # no pending round
+    for args, status in (((5, FAKE, FAKE, FAKE), -1), ((0, 0, FAKE, FAKE), -1),
+                         ((0, FAKE, FAKE, None), -1), ((0, FAKE + 2, FAKE, FAKE), -1)):
+        with pytest.raises(hdt.HdtError) as err:
+            e.walk_commit(*args)
+        assert err.value.status == status
+    assert e.kv_length(0) == 100
+    e.close()
+
+
 def fake_layers(n_layers=4):
     return [dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, o=FAKE) for _ in range(n_layers)]
 

@@ -412,6 +412,9 @@ def pin_walk_brute_and_greedy_descent():
             x = nxt[0]
         assert oracle.greedy_walk(parent, draft, target) == (synth.root_path(parent, x),
                                                              int(target[x]))
+        path = synth.accepted_path(seed, "pin/walk/path", parent)
+        draft, target = synth.tokens_for_path(seed, "pin/walk/path/tokens", parent, path)
+        assert oracle.greedy_walk(parent, draft, target)[0] == path
 
 
 PINS = {name[4:]: fn for name, fn in list(globals().items()) if name.startswith("pin_")}
