@@ -232,7 +232,7 @@ def gdn_conv(parent, tail, q, k, v, W, eps=CONV_EPS):
     W = _c(np.asarray(W, dtype=np.float32))
     w = W.shape[1]
     C = 2 * hk * dk + hv * dv
-    assert W.shape == (C, w)
+    assert W.shape == (C, w) and 1 <= w <= 8
     if tail is None or w == 1:
         tail = np.zeros((max(w - 1, 1), C), q.dtype)
     assert tail.shape[1] == C

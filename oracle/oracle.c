@@ -281,19 +281,19 @@ void orc_gdn_conv(int hk, int dk, int hv, int dv, int w, int n, const int32_t *p
                   const void *tail, const void *q, const void *k, const void *v,
                   const float *W, int dtype, float eps, float *qo, float *ko, float *vo) {
   const int64_t CQ = (int64_t)hk * dk, C = 2 * CQ + (int64_t)hv * dv;
-  int32_t path[ORC_MAX_NODES];
+  int32_t up[8];  /* up[r]: the ancestor r steps above node i (w <= 8) */
   for (int i = 0; i < n; ++i) {
     int d = 0;
-    for (int x = i; x >= 0; x = parent[x]) ++d;
-    for (int x = i, p = d - 1; x >= 0; x = parent[x], --p) path[p] = x;  /* root..i */
-    d -= 1;                                                               /* depth of i */
+    for (int x = parent[i]; x >= 0; x = parent[x]) ++d;  /* depth of i */
+    up[0] = i;
+    for (int r = 1; r < w && r <= d; ++r) up[r] = parent[up[r - 1]];
     for (int64_t c = 0; c < C; ++c) {
       float acc = 0.0f;
       for (int j = 0; j < w; ++j) {
         const int r = w - 1 - j;  /* steps above node i */
         float xin;
         if (r <= d) {
-          const int node = path[d - r];
+          const int node = up[r];
           if (c < CQ)
             xin = ld(q, dtype, (int64_t)node * CQ + c);
           else if (c < 2 * CQ)

@@ -43,7 +43,7 @@ MUTANTS = {
                            "acc = acc + W[c * w + (w - 1 - j)] * xin;"),
     "conv_tail_rows_reversed": ("xin = ld(tail, dtype, (int64_t)((w - 1) - (r - d)) * C + c);",
                                 "xin = ld(tail, dtype, (int64_t)((r - d) - 1) * C + c);"),
-    "conv_path_from_root": ("const int node = path[d - r];", "const int node = path[r];"),
+    "conv_ancestor_off_by_one": ("const int node = up[r];", "const int node = up[r > 0 ? r - 1 : 0];"),
     "conv_silu_sign": ("const float y = acc / (1.0f + expf(-acc));",
                        "const float y = acc / (1.0f + expf(acc));"),
     "conv_no_activation": ("const float y = acc / (1.0f + expf(-acc));",
