@@ -156,6 +156,66 @@ def cpu_baseline(w, seed, L, parent, gdn_layers=3, attn_heads=4):
                        f"scaled to the 64-layer verify; measured {t_gdn + t_att:.1f} s")}
 
 
+def prefill_bench(args):
+    """forward_span of T tokens through the whole stack, K times back to back from the
+    workload's context (each span appends T tokens).  Timing only: every layer of a kind
+    reads the same seeded span inputs."""
+    import statistics
+    import torch
+    import synth
+    from synth.device import Instance, to_device
+    w = synth.WORKLOADS[args.workload]
+    T, K = args.prefill, args.steps
+    L0 = w.lengths[0]
+    cap = L0 + T * (K + args.warmup) + 64
+    inst = Instance(w, args.seed, lengths=[L0], trees=[[-1]], capacity=[cap], keep_host=False)
+    eng = inst.engine(max_nodes=64)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    shared = {}
+    for kind in (0, 1):
+        l = w.layer_kind.index(kind)
+        if kind == 0:
+            gen = synth.conv_inputs if synth.conv_width(w) else synth.gdn_inputs
+            names, arrs = ("q", "k", "v", "alpha", "beta"), gen(w, args.seed, 0, l, T, "prefill")
+            oshape = (T, w.gdn_hv, w.gdn_dv)
+        else:
+            names, arrs = ("q", "k", "v"), synth.attn_inputs(w, args.seed, 0, l, T, "prefill")
+            oshape = (T, w.attn_hq, w.attn_d)
+        d = {nm: to_device(a, w.dtype, "cuda") for nm, a in zip(names, arrs)}
+        d["o"] = torch.empty(oshape, dtype=tdt, device="cuda")
+        shared[kind] = d
+    layers = [shared[k] for k in w.layer_kind]
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        eng.forward_span(0, T, layers, stream.cuda_stream)
+    torch.cuda.synchronize()
+    L_start = eng.kv_length(0)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    eng.profile(True)
+    for a, b in ev:
+        a.record(stream)
+        eng.forward_span(0, T, layers, stream.cuda_stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    prof = {k: eng.profile_read(k) for k in (0, 1, 2, 3, 4)}
+    eng.profile(False)
+    ms = [a.elapsed_time(b) for a, b in ev]
+    med = statistics.median(ms)
+    kernels = {name: {"avg_us": round(1e3 * prof[k][0] / max(1, prof[k][1]), 2),
+                      "ms_per_span": round(prof[k][0] / K, 3)}
+               for k, name in ((0, "gdn_tree"), (1, "attn_split"), (2, "attn_tree"), (3, "commit"),
+                               (4, "gdn_conv")) if prof[k][1] > 0}
+    out = {"metric": f"prefill tokens/s, {T}-token spans appended to a {L0}-token context",
+           "value": round(T / (med * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+           "warmup": args.warmup, "ms_per_span": round(med, 3), "higher_is_better": True,
+           "dtype": w.dtype, "data": "synthetic; every layer of a kind reads the same span inputs",
+           "config": {"workload": f"{w.name}: {w.n_gdn} GDN + {w.n_attn} attention layers, spans of "
+                                  f"{T} tokens in chains of 64 from {L_start} to {eng.kv_length(0)} tokens"},
+           "kernels": kernels}
+    eng.close()
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +225,9 @@ def main():
     ap.add_argument("--seed", type=int, default=20261202)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time the eager pass only")
+    ap.add_argument("--prefill", type=int, default=0, metavar="T",
+                    help="instead of the verify, time forward_span prefills of T tokens (chains "
+                         "of 64) appended to the workload's context, and print prefill tokens/s")
     ap.add_argument("--walk", action="store_true",
                     help="close each round with the on-device accept walk + commit (walk_commit) "
                          "on seeded tokens that accept the same path, instead of commit_tree")
@@ -181,6 +244,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.prefill:
+        prefill_bench(args)
         return
     import torch
     import synth

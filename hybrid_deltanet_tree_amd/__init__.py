@@ -80,6 +80,11 @@ _sigs = {
     "hdt_rollback_to": (_S, [_E, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p]),
     "hdt_walk_commit": (_S, [_E, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                              ctypes.c_void_p]),
+    "hdt_forward_span": (_S, [_E, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(hdt_layer_io),
+                              ctypes.c_void_p]),
+    "hdt_set_anchors": (_S, [_E, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                             ctypes.c_void_p]),
+    "hdt_anchor_below": (_S, [_E, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
     "hdt_kv_length": (_S, [_E, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]),
     "hdt_reset": (_S, [_E, ctypes.c_int32, ctypes.c_int64]),
     "hdt_tree_meta": (_S, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int64,
@@ -201,6 +206,18 @@ class Engine:
 
     def rollback_to(self, slot, n, stream=0):
         self._check(hdt_rollback_to(self.h, slot, n, stream))
+
+    def forward_span(self, slot, T, layers, stream=0):
+        """Prefill of T tokens: layers as for forward_tree, each array holding T rows."""
+        self._check(hdt_forward_span(self.h, slot, T, self._io_array(layers), stream))
+
+    def set_anchors(self, slot, every, n_max=0, state=None, conv=None):
+        self._check(hdt_set_anchors(self.h, slot, every, n_max, _ptr(state), _ptr(conv)))
+
+    def anchor_below(self, slot, n) -> int:
+        out = ctypes.c_int64()
+        self._check(hdt_anchor_below(self.h, slot, n, ctypes.byref(out)))
+        return out.value
 
     def walk_commit(self, slot, draft, target, out, stream=0):
         """Accept walk + commit on the device: draft, target int32 [n], out int32 [2 + n]

@@ -46,6 +46,11 @@ struct SlotState {
   void *x_pend = nullptr;     // GDN conv: pre-conv rows of the tree [n_gdn][max_nodes][C]
   bool pending = false;
   bool walk_pending = false;  // an accept walk's commit is in flight: length not yet known
+  int64_t anchor_every = 0;   // state anchors: anchor k holds position (k + 1) * every
+  int32_t anchor_n = 0;
+  float *anchor_state = nullptr;
+  void *anchor_conv = nullptr;
+  std::vector<bool> anchor_ok;
   hipEvent_t walk_ev = nullptr;
   int32_t n = 0;
   int32_t chain = 0;
@@ -622,6 +627,32 @@ hdt_status do_commit(hdt_engine *e, int32_t slot, const int32_t *path, int32_t m
   return HDT_OK;
 }
 
+size_t gdn_state_bytes(const hdt_engine *e) {
+  return static_cast<size_t>(e->n_gdn) * e->desc.gdn_hv * e->desc.gdn_dv * e->desc.gdn_dk * sizeof(float);
+}
+
+size_t conv_tail_bytes(const hdt_engine *e) {
+  return e->desc.gdn_conv > 1 ? static_cast<size_t>(e->n_gdn) * (e->desc.gdn_conv - 1) * e->conv_C * e->esz : 0;
+}
+
+// Copies the slot's recurrent state (and conv tails) to or from anchor k.
+hdt_status anchor_copy(hdt_engine *e, int32_t slot, int32_t k, bool save, hipStream_t stream) {
+  SlotState &s = e->slots[slot];
+  const size_t sb = gdn_state_bytes(e), cb = conv_tail_bytes(e);
+  char *as = reinterpret_cast<char *>(s.anchor_state) + static_cast<size_t>(k) * sb;
+  if (sb > 0 && hipMemcpyAsync(save ? as : static_cast<void *>(s.d.gdn_state), save ? s.d.gdn_state : static_cast<void *>(as),
+                               sb, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return fail(e, HDT_E_HIP, "anchor copy of the state failed");
+  if (cb > 0) {
+    char *ac = static_cast<char *>(s.anchor_conv) + static_cast<size_t>(k) * cb;
+    if (hipMemcpyAsync(save ? ac : s.d.gdn_conv_state, save ? s.d.gdn_conv_state : static_cast<void *>(ac), cb,
+                       hipMemcpyDeviceToDevice, stream) != hipSuccess)
+      return fail(e, HDT_E_HIP, "anchor copy of the conv tails failed");
+  }
+  if (save) s.anchor_ok[k] = true;
+  return HDT_OK;
+}
+
 // After an accept walk, the slot's new length is known once the device has run the
 // walk: wait for it and take m from the pinned copy.
 hdt_status settle(hdt_engine *e, int32_t slot) {
@@ -845,7 +876,19 @@ hdt_status hdt_rollback_to(hdt_engine *e, int32_t slot, int64_t n, void *stream)
   if (settle(e, slot) != HDT_OK) return HDT_E_HIP;
   SlotState &s = e->slots[slot];
   const int64_t L = s.d.length;
-  if (n < L) return fail(e, HDT_E_UNSUPPORTED, "rollback below the committed length needs state anchors");
+  if (n < L) {
+    const int64_t k = s.anchor_every > 0 && n % s.anchor_every == 0 ? n / s.anchor_every - 1 : -1;
+    if (k < 0 || k >= s.anchor_n || !s.anchor_ok[k])
+      return fail(e, HDT_E_UNSUPPORTED, "rollback to %lld below the committed length needs an anchor there",
+                  (long long)n);
+    hdt_status st = anchor_copy(e, slot, static_cast<int32_t>(k), false, static_cast<hipStream_t>(stream));
+    if (st != HDT_OK) return st;
+    for (int32_t j = static_cast<int32_t>(k) + 1; j < s.anchor_n; ++j) s.anchor_ok[j] = false;
+    s.d.length = n;
+    s.pending = false;
+    e->err.clear();
+    return HDT_OK;
+  }
   if (n == L) {
     s.pending = false;
     e->err.clear();
@@ -863,6 +906,130 @@ hdt_status hdt_rollback_to(hdt_engine *e, int32_t slot, int64_t n, void *stream)
   if (st != HDT_OK) return st;
   s.d.length += m;
   e->err.clear();
+  return HDT_OK;
+}
+
+hdt_status hdt_forward_span(hdt_engine *e, int32_t slot, int32_t T, const hdt_layer_io *io, void *stream) {
+  if (!e) return HDT_E_INVALID;
+  if (slot < 0 || slot >= static_cast<int32_t>(e->slots.size()))
+    return fail(e, HDT_E_INVALID, "slot %d out of range", slot);
+  if (T < 1 || !io) return fail(e, HDT_E_INVALID, "span of %d tokens", T);
+  if (settle(e, slot) != HDT_OK) return HDT_E_HIP;
+  SlotState &s = e->slots[slot];
+  const hdt_model_desc &m = e->desc;
+  if (s.pending) return fail(e, HDT_E_ORDER, "slot %d has a pending round", slot);
+  if (s.d.length + T > s.d.capacity)
+    return fail(e, HDT_E_CAPACITY, "slot %d: length %lld + %d tokens exceeds capacity %lld", slot,
+                (long long)s.d.length, T, (long long)s.d.capacity);
+  for (int l = 0; l < m.n_layers; ++l) {
+    const hdt_layer_io &x = io[l];
+    if (!x.q || !x.k || !x.v || !x.o) return fail(e, HDT_E_INVALID, "layer %d: NULL q/k/v/o", l);
+    if (e->kind[l] == 0 && (!x.alpha || !x.beta)) return fail(e, HDT_E_INVALID, "layer %d: NULL alpha/beta", l);
+    if (e->kind[l] == 1 && (!aligned16(x.q) || !aligned16(x.k) || !aligned16(x.v) || !aligned16(x.o)))
+      return fail(e, HDT_E_INVALID, "layer %d: attention buffers must be 16-byte aligned", l);
+    if (e->kind[l] == 0 && m.gdn_conv > 0 && (!aligned16(x.q) || !aligned16(x.k) || !aligned16(x.v)))
+      return fail(e, HDT_E_INVALID, "layer %d: conv inputs must be 16-byte aligned", l);
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!e->allocated) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+      return fail(e, HDT_E_ORDER, "the first forward allocates scratch: run it outside graph capture");
+  }
+  hdt_status r = ensure_alloc(e);
+  if (r != HDT_OK) return r;
+  if (gdn_lds_bytes(m.gdn_dk, m.max_nodes, kGdnSaves) > static_cast<size_t>(e->max_lds) && e->n_gdn > 0)
+    return fail(e, HDT_E_UNSUPPORTED, "a chain of %d needs more LDS than the device allows", m.max_nodes);
+  // bytes per row of each io array, by layer kind
+  const size_t z = e->esz;
+  int32_t chain[kMaxNodes], path[kMaxNodes];
+  for (int i = 0; i < kMaxNodes; ++i) {
+    chain[i] = i - 1;
+    path[i] = i;
+  }
+  std::vector<hdt_layer_io> cio(m.n_layers);
+  for (int32_t t0 = 0; t0 < T;) {
+    int32_t c = std::min<int32_t>(m.max_nodes, T - t0);
+    if (s.anchor_every > 0) {  // end a chain at every anchor position
+      const int64_t next = (s.d.length / s.anchor_every + 1) * s.anchor_every;
+      c = static_cast<int32_t>(std::min<int64_t>(c, next - s.d.length));
+    }
+    for (int l = 0; l < m.n_layers; ++l) {
+      const hdt_layer_io &x = io[l];
+      const size_t t = static_cast<size_t>(t0);
+      size_t bq, bk, bv, bo, bg = 0;
+      if (e->kind[l] == 0) {
+        bq = bk = static_cast<size_t>(m.gdn_hk) * m.gdn_dk * z;
+        bv = bo = static_cast<size_t>(m.gdn_hv) * m.gdn_dv * z;
+        bg = static_cast<size_t>(m.gdn_hv) * z;
+      } else {
+        bq = bo = static_cast<size_t>(m.attn_hq) * m.attn_d * z;
+        bk = bv = static_cast<size_t>(m.attn_hkv) * m.attn_d * z;
+      }
+      cio[l].q = static_cast<const char *>(x.q) + t * bq;
+      cio[l].k = static_cast<const char *>(x.k) + t * bk;
+      cio[l].v = static_cast<const char *>(x.v) + t * bv;
+      cio[l].o = static_cast<char *>(x.o) + t * bo;
+      cio[l].alpha = x.alpha ? static_cast<const char *>(x.alpha) + t * bg : nullptr;
+      cio[l].beta = x.beta ? static_cast<const char *>(x.beta) + t * bg : nullptr;
+    }
+    int8_t par[1][kMaxNodes], dep[1][kMaxNodes];
+    int32_t cl;
+    std::memset(par, 0, sizeof par);
+    std::memset(dep, 0, sizeof dep);
+    plan_tree(c, chain, par[0], dep[0], &cl);
+    const hdt_tree tr{slot, c, chain, cio.data()};
+    r = launch_forward(e, 1, &tr, par, dep, st);
+    if (r != HDT_OK) return r;
+    s.n = c;
+    std::memcpy(s.parent, par[0], kMaxNodes);
+    std::memcpy(s.depth, dep[0], kMaxNodes);
+    r = do_commit(e, slot, path, c, nullptr, st);
+    if (r != HDT_OK) return r;
+    s.d.length += c;
+    if (s.anchor_every > 0 && s.d.length % s.anchor_every == 0) {
+      const int64_t k = s.d.length / s.anchor_every - 1;
+      if (k < s.anchor_n) {
+        r = anchor_copy(e, slot, static_cast<int32_t>(k), true, st);
+        if (r != HDT_OK) return r;
+      }
+    }
+    t0 += c;
+  }
+  e->err.clear();
+  return HDT_OK;
+}
+
+hdt_status hdt_set_anchors(hdt_engine *e, int32_t slot, int64_t every, int32_t n_max, float *state,
+                           void *conv) {
+  if (!e) return HDT_E_INVALID;
+  if (slot < 0 || slot >= static_cast<int32_t>(e->slots.size()))
+    return fail(e, HDT_E_INVALID, "slot %d out of range", slot);
+  SlotState &s = e->slots[slot];
+  if (every < 0 || (every > 0 && n_max < 1)) return fail(e, HDT_E_INVALID, "anchors every %lld, %d of them",
+                                                         (long long)every, n_max);
+  if (every > 0 && e->n_gdn > 0 && (!state || !aligned16(state)))
+    return fail(e, HDT_E_INVALID, "anchor state buffer missing or not 16-byte aligned");
+  if (every > 0 && conv_tail_bytes(e) > 0 && (!conv || !aligned16(conv)))
+    return fail(e, HDT_E_INVALID, "anchor conv buffer missing or not 16-byte aligned");
+  s.anchor_every = every;
+  s.anchor_n = every > 0 ? n_max : 0;
+  s.anchor_state = state;
+  s.anchor_conv = conv;
+  s.anchor_ok.assign(static_cast<size_t>(s.anchor_n), false);
+  e->err.clear();
+  return HDT_OK;
+}
+
+hdt_status hdt_anchor_below(const hdt_engine *e, int32_t slot, int64_t n, int64_t *out) {
+  if (!e || !out || slot < 0 || slot >= static_cast<int32_t>(e->slots.size())) return HDT_E_INVALID;
+  const SlotState &s = e->slots[slot];
+  *out = -1;
+  for (int32_t k = s.anchor_n - 1; k >= 0; --k)
+    if (s.anchor_ok[k] && (k + 1) * s.anchor_every <= n) {
+      *out = (k + 1) * s.anchor_every;
+      break;
+    }
   return HDT_OK;
 }
 
@@ -922,6 +1089,8 @@ hdt_status hdt_reset(hdt_engine *e, int32_t slot, int64_t length) {
                 (long long)s.d.capacity);
   s.d.length = length;
   s.pending = false;
+  for (int32_t j = 0; j < s.anchor_n; ++j)
+    if ((j + 1) * s.anchor_every > length) s.anchor_ok[j] = false;
   e->err.clear();
   return HDT_OK;
 }

@@ -189,6 +189,37 @@ hdt_status hdt_forward_block(hdt_engine *eng, int32_t slot, int32_t n, const hdt
                              void *stream);
 
 /*
+ * forward_span: a prefill of T tokens ("One request, end to end", 2.5: the prompt
+ * tokens past the resident prefix go through the model once), committed as it goes.
+ * io has n_layers entries whose arrays hold T rows (the hdt_layer_io layouts with
+ * n = T).  The span runs as consecutive chains of up to max_nodes tokens through the
+ * tree kernels, each chain committed before the next, so every row and the final
+ * state equal a token-by-token decode bit for bit.  With anchors set
+ * (hdt_set_anchors), a chain also ends at every multiple of `every`, and the
+ * recurrent state (and conv tails) at that position is copied to its anchor.
+ * Needs no pending round; length + T <= capacity.  length += T.
+ * Errors: HDT_E_INVALID, HDT_E_ORDER, HDT_E_CAPACITY, HDT_E_HIP.
+ */
+hdt_status hdt_forward_span(hdt_engine *eng, int32_t slot, int32_t T, const hdt_layer_io *io,
+                            void *stream);
+
+/*
+ * State anchors of a slot ("One request, end to end", 2.5: recurrent-state anchors
+ * every 1,024 tokens let a later turn resume inside the resident prefix).  Device
+ * buffers owned by the caller: state float32 [n_max][n_gdn][gdn_hv][gdn_dv][gdn_dk]
+ * (anchor k holds the state at position (k + 1) * every) and, when gdn_conv > 1,
+ * conv in io_dtype [n_max][n_gdn][gdn_conv - 1][C] (else NULL).  every >= 1.
+ * forward_span fills them; commit_tree and the accept walk do not.  A call replaces
+ * the previous anchors of the slot (all marked empty); every = 0 removes them.
+ * Errors: HDT_E_INVALID.
+ */
+hdt_status hdt_set_anchors(hdt_engine *eng, int32_t slot, int64_t every, int32_t n_max,
+                           float *state, void *conv);
+
+/* The highest position p <= n whose anchor holds a state, or -1 (none). */
+hdt_status hdt_anchor_below(const hdt_engine *eng, int32_t slot, int64_t n, int64_t *out);
+
+/*
  * commit_tree ("One request, end to end", 2.6: commit the accepted path's KV
  * rows and recurrent state): path is a HOST array of m >= 1 node indices with
  * path[0] = 0 and parent[path[d]] = path[d-1].  For every attention layer,
@@ -207,8 +238,10 @@ hdt_status hdt_commit_tree(hdt_engine *eng, int32_t slot, const int32_t *path, i
  * (or does nothing when none is pending).  length < n <= length + c, c being
  * the pending tree's leading chain (nodes 0..c-1 with parent[i] = i-1), keeps
  * that chain prefix: the same as hdt_commit_tree with path 0..n-length-1.
- * n < length needs state anchors this library does not keep: HDT_E_UNSUPPORTED.
- * Other n: HDT_E_INVALID.
+ * n < length: when n is the position of a filled anchor (hdt_set_anchors,
+ * hdt_anchor_below), the state and conv tails are copied back from it, the pending
+ * round is dropped, length = n, and the anchors above n are emptied (the rows past
+ * n will be written again); otherwise HDT_E_UNSUPPORTED.  Other n: HDT_E_INVALID.
  */
 hdt_status hdt_rollback_to(hdt_engine *eng, int32_t slot, int64_t n, void *stream);
 

@@ -127,6 +127,32 @@ def test_walk_commit_rejects_without_touching_the_device():
     e.close()
 
 
+def test_span_and_anchor_rejections_on_the_host():
+    e = make_engine()
+    layers = [dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, o=FAKE) for _ in range(4)]
+    for args, status in (((0, 0, layers), -1), ((7, 4, layers), -1), ((1, 6, layers), -4)):
+        with pytest.raises(hdt.HdtError) as err:
+            e.forward_span(*args)
+        assert err.value.status == status
+    bad = [dict(l) for l in layers]
+    bad[3]["q"] = FAKE + 8  # attention buffers must be 16-byte aligned
+    with pytest.raises(hdt.HdtError) as err:
+        e.forward_span(0, 4, bad)
+    assert err.value.status == -1
+    assert e.kv_length(0) == 100 and e.kv_length(1) == 295
+    assert e.anchor_below(0, 10 ** 6) == -1
+    for args in ((0, -1, 4, FAKE), (0, 64, 0, FAKE), (0, 64, 4, None), (0, 64, 4, FAKE + 4)):
+        with pytest.raises(hdt.HdtError):
+            e.set_anchors(*args)
+    e.set_anchors(0, 64, 4, FAKE)
+    assert e.anchor_below(0, 10 ** 6) == -1  # nothing filled yet
+    with pytest.raises(hdt.HdtError) as err:
+        e.rollback_to(0, 64)  # below the length, no filled anchor there
+    assert err.value.status == -7
+    e.set_anchors(0, 0)
+    e.close()
+
+
 def fake_layers(n_layers=4):
     return [dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, o=FAKE) for _ in range(n_layers)]
 
