@@ -599,7 +599,7 @@ hdt_status do_commit(hdt_engine *e, int32_t slot, const int32_t *path, int32_t m
   c.dv = m.gdn_dv;
   c.hkv = m.attn_hkv;
   c.D = m.attn_d;
-  c.gdn_blocks = e->n_gdn > 0 ? e->n_gdn * m.gdn_hv * (m.gdn_dv / kGdnCols) : 0;
+  c.gdn_blocks = e->n_gdn > 0 ? e->n_gdn * m.gdn_hv * (m.gdn_dv / (kGdnCols * kCommitCols)) : 0;
   c.kv_blocks = e->n_attn > 0 ? e->n_attn * m.attn_hkv : 0;
   int conv_blocks = 0;
   if (e->n_gdn > 0 && m.gdn_conv > 1) {

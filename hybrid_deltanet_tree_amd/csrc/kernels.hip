@@ -1006,25 +1006,29 @@ __global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch 
   constexpr int B = 8;               // path steps whose operands are in flight together
   const int bid = blockIdx.x, tid = threadIdx.x;
   if (bid < P.gdn_blocks) {
-    // Committed state of one (GDN layer, value head, 16 columns): replay the
-    // accepted path's rank-1 steps fmaf(k, u, alpha * S) with the bits the pass
-    // used, so the result equals the pass's state of the path's last node.
-    const int cgroups = P.dv / kGdnCols;
+    // Committed state of one (GDN layer, value head, NC groups of 16 columns): replay
+    // the accepted path's rank-1 steps fmaf(k, u, alpha * S) with the bits the pass
+    // used, so the result equals the pass's state of the path's last node.  A lane
+    // holds the same 8 key rows of NC columns 16 apart, which share its k and alpha
+    // loads, so every lane keeps NC state slices in flight.
+    constexpr int NC = kCommitCols;
+    const int cgroups = P.dv / (kGdnCols * NC);
     const int per_layer = P.hv * cgroups;
     const int lg = bid / per_layer, local = bid % per_layer;
     const int h = local / cgroups, cg = local % cgroups;
     const int qh = h / (P.hv / P.hk);
     const int wave = tid >> 6, lane = tid & 63;
-    const int col = cg * kGdnCols + wave * 4 + (lane >> 4);
+    const int col0 = cg * kGdnCols * NC + wave * 4 + (lane >> 4);
     const int g = lane & 15;
-    float *sp = P.state + ((static_cast<int64_t>(lg) * P.hv + h) * P.dv + col) * DK + g * R;
-    float cur[R];
-    lds_row<R>(sp, cur);  // the state slice is in flight before the path is known
+    float *sp0 = P.state + ((static_cast<int64_t>(lg) * P.hv + h) * P.dv + col0) * DK + g * R;
+    float cur[NC][R];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) lds_row<R>(sp0 + j * kGdnCols * DK, cur[j]);  // in flight first
     const CommitPath path = load_path(P, lane);
     const int64_t lbase = static_cast<int64_t>(lg) * P.max_nodes;
     for (int d0 = 0; d0 < path.m; d0 += B) {
       uint32_t kw[B][KW];
-      float u[B];
+      float u[B][NC];
       io_t<BF> araw[B];
 #pragma unroll
       for (int b = 0; b < B; ++b) {
@@ -1046,7 +1050,8 @@ __global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch 
             kw[b][0] = x.x;
             kw[b][1] = x.y;
           }
-          u[b] = P.u_pend[(nb * P.hv + h) * P.dv + col];
+#pragma unroll
+          for (int j = 0; j < NC; ++j) u[b][j] = P.u_pend[(nb * P.hv + h) * P.dv + col0 + j * kGdnCols];
           araw[b] = static_cast<const io_t<BF> *>(P.a_pend)[nb * P.hv + h];
         }
       }
@@ -1067,13 +1072,18 @@ __global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch 
           else
             al = araw[b];
 #pragma unroll
-          for (int a = 0; a < R; ++a) cur[a] = fmaf(kj[a], u[b], al * cur[a]);
+          for (int j = 0; j < NC; ++j)
+#pragma unroll
+            for (int a = 0; a < R; ++a) cur[j][a] = fmaf(kj[a], u[b][j], al * cur[j][a]);
         }
       }
     }
 #pragma unroll
-    for (int a = 0; a < R; a += 4)
-      *reinterpret_cast<float4 *>(sp + a) = make_float4(cur[a], cur[a + 1], cur[a + 2], cur[a + 3]);
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+      for (int a = 0; a < R; a += 4)
+        *reinterpret_cast<float4 *>(sp0 + j * kGdnCols * DK + a) =
+            make_float4(cur[j][a], cur[j][a + 1], cur[j][a + 2], cur[j][a + 3]);
     return;
   }
   if (bid >= P.gdn_blocks + P.kv_blocks) {
@@ -1090,18 +1100,18 @@ __global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch 
     unsigned char *tail = static_cast<unsigned char *>(P.conv_state) + lg * keep * row_bytes + byte;
     const unsigned char *xp = static_cast<const unsigned char *>(P.x_pend) +
                               static_cast<int64_t>(lg) * P.max_nodes * row_bytes + byte;
-    uint4 rows[kConvMaxWidth - 1];
-#pragma unroll
-    for (int r = 0; r < kConvMaxWidth - 1; ++r) {
-      if (r < keep) {
-        const int src = path.m + r;  // index into (old tail rows, path rows)
-        rows[r] = src < keep ? *reinterpret_cast<const uint4 *>(tail + src * row_bytes)
-                             : *reinterpret_cast<const uint4 *>(xp + static_cast<int64_t>(path[src - keep]) * row_bytes);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kConvMaxWidth - 1; ++r)
-      if (r < keep) *reinterpret_cast<uint4 *>(tail + r * row_bytes) = rows[r];
+    static_assert(kConvMaxWidth - 1 == 3, "three tail rows at most");
+    auto source = [&](int r) {  // row r of the new tail: (old tail rows, path rows)[m + r]
+      const int src = path.m + r;
+      return src < keep ? *reinterpret_cast<const uint4 *>(tail + src * row_bytes)
+                        : *reinterpret_cast<const uint4 *>(xp + static_cast<int64_t>(path[src - keep]) * row_bytes);
+    };
+    const uint4 r0 = source(0);
+    const uint4 r1 = keep > 1 ? source(1) : r0;
+    const uint4 r2 = keep > 2 ? source(2) : r0;
+    *reinterpret_cast<uint4 *>(tail) = r0;
+    if (keep > 1) *reinterpret_cast<uint4 *>(tail + row_bytes) = r1;
+    if (keep > 2) *reinterpret_cast<uint4 *>(tail + 2 * row_bytes) = r2;
     return;
   }
   // K/V gather: row L+d <- row L+path[d] of one (attention layer, kv head).
