@@ -32,7 +32,7 @@ constexpr int64_t kKvSplitMin = 128;  // bf16 attention: smallest split (> kKvTi
 
 struct SlotState {
   hdt_slot_desc d{};
-  int32_t split = 0;
+  int32_t split = 0;          // float32 attention: keys per split (bf16 splits follow each row's position)
   int32_t nsplit_cap = 0;
   float *u_pend = nullptr;
   void *k_pend = nullptr;
@@ -119,8 +119,9 @@ int64_t pow2_floor(int64_t x) {
 //    that cuts K keys into at most per_head splits, per_head = kSplitCUs /
 //    (H_kv row_groups).  So at any length a layer is about one wave of
 //    kSplitCUs (kv head, split, row group) workgroups, a slot's capacity does not
-//    matter, and the rungs are close enough (3 %) that a layer rarely holds rows of
-//    two split sizes.
+//    matter, and the rungs are close enough (3-6 %) that a layer rarely holds rows
+//    of two split sizes.
+
 // Row groups of the split pass for the engine's largest tree (bf16 attention).
 int32_t kv_row_groups(const hdt_model_desc &m) {
   if (m.attn_hkv <= 0) return 1;

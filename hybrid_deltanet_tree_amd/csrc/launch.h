@@ -1,10 +1,11 @@
 // launch.h - argument blocks passed by value from the host engine to the kernels.
 //
 // Every launch covers one layer (or, for commit, every layer) of up to
-// kMaxTrees trees; a workgroup finds its tree from its block index and the
-// per-tree *_begin offsets.  All sizes were validated on the host before a
-// block is filled in, so the kernels index without further checks beyond
-// what the tree itself bounds.
+// kMaxTrees trees; in the tree kernels a workgroup's tree is its grid row
+// (blockIdx.y), except in the float32 attention path, which places trees by
+// per-tree *_begin offsets along x.  All sizes were validated on the host
+// before a block is filled in, so the kernels index without further checks
+// beyond what the tree itself bounds.
 #pragma once
 
 #include <hip/hip_runtime.h>
