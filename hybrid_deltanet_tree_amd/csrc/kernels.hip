@@ -222,7 +222,7 @@ __global__ __launch_bounds__(gdn_threads(DK)) void gdn_tree_kernel(const GdnLaun
     savel[tid] = static_cast<int8_t>(save_i);
   }
   lds_barrier();
-  if (tid < n) {
+  if (T.need_anc && tid < n) {
     int x = tid;
     for (int k = dep_i; k >= 0; --k) {
       anc[tid * kMaxNodes + k] = static_cast<int8_t>(x);

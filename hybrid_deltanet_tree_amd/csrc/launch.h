@@ -44,6 +44,8 @@ struct GdnTree {
   void *k_pend;                          // [max_nodes][hk][dk]: copy of k (io dtype)
   void *a_pend;                          // [max_nodes][hv]:     copy of alpha (io dtype)
   int32_t n;
+  int32_t need_anc;                      // some restore replays a root path (a branch point
+                                         // beyond the kept states): build the ancestor table
   int8_t parent[kMaxNodes];
   int8_t depth[kMaxNodes];
   int8_t save[kMaxNodes];                // LDS slot that keeps node i's state, or -1

@@ -282,6 +282,34 @@ def test_deep_chain_of_64_across_splits(L):
         gu.check_layer(inst, 0, l, got[l])
 
 
+def test_many_branch_points_replay_from_committed_state():
+    """A bushy 64-node tree: more branch points than the walk keeps in LDS, so some parents
+    are restored by replaying their root path from the committed state (the ancestor
+    table is built).  Outputs against the oracle; verified rows equal decoded rows."""
+    w = synth.Workload("bushy", [0, 1], 4, 8, 128, 128, 12, 2, 256, "bf16", [700], 64, "random4")
+    parent = synth.random_tree(SEED, "bushy", 64, 5)
+    branch = {parent[c] for c in range(1, 64) if parent[c] != c - 1}
+    assert len(branch) > 8  # beyond the 8 kept states
+    inst = Instance(w, SEED, trees=[parent])
+    eng = inst.engine(max_nodes=64)
+    snap = gu.snapshot(inst)
+    run_verify(inst, eng)
+    got = gu.outputs(inst, 0)
+    for l in range(2):
+        gu.check_layer(inst, 0, l, got[l])
+    verified = gu.raw_outputs(inst, 0)
+    eng.rollback_to(0, 700)
+    leaves = [i for i in range(64) if i not in parent]
+    for leaf in leaves[-3:]:
+        gu.restore(inst, snap)
+        eng.reset(0, 700)
+        outs = decode_rows_along(inst, eng, leaf)
+        for step, j in enumerate(synth.root_path(parent, leaf)):
+            for l in range(2):
+                assert np.array_equal(outs[step][l][0], verified[l][j]), f"leaf {leaf} node {j} layer {l}"
+    eng.close()
+
+
 def test_single_node_and_nan_past_length():
     inst = Instance(MINI, SEED, lengths=[1000], trees=[[-1]], poison=True)
     eng = inst.engine()
