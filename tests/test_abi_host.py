@@ -23,6 +23,15 @@ def declared_functions():
                                  re.M)))
 
 
+def test_header_is_plain_c():
+    # include/hdt.h compiles as C11 in a C program that uses every part of it it needs
+    import subprocess
+    src = os.path.join(os.path.dirname(__file__), "c_abi", "verify_round.c")
+    subprocess.check_call(["gcc", "-fsyntax-only", "-std=c11", "-Wall", "-Werror",
+                           "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                           "-I" + os.path.dirname(HEADER), src])
+
+
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert len(names) >= 12
