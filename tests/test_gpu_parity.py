@@ -259,6 +259,42 @@ def test_joint_equals_lone():
             assert torch.equal(a, b)
 
 
+def test_joint_of_eight_trees_mixed_sizes():
+    """The most trees one call takes (8): lengths 0 .. 2,100 with one slot filled to its
+    capacity exactly, trees of 1 to 64 nodes (so the split pass mixes row groups); every
+    slot's rows equal its lone verify bit for bit, and two slots match the oracle."""
+    lengths = [0, 1, 31, 257, 1000, 1300, 2047, 2100]
+    trees = [[-1], synth.chain_tree(2), synth.draft_tree(SEED, "j8/16", 16),
+             synth.random_tree(SEED, "j8/64", 64, 6), synth.chain_tree(5),
+             synth.draft_tree(SEED, "j8/20", 20), synth.random_tree(SEED, "j8/9", 9, 3),
+             synth.draft_tree(SEED, "j8/16b", 16)]
+    w = synth.Workload("joint8", [0, 1, 0, 1], 4, 8, 128, 128, 12, 2, 256, "bf16", lengths, 64,
+                       "draft")
+    caps = [L + len(t) + 64 for L, t in zip(lengths, trees)]
+    caps[6] = lengths[6] + len(trees[6])  # filled exactly
+    inst = Instance(w, SEED, trees=trees, capacity=caps)
+    eng = inst.engine(max_nodes=64)
+    snap = gu.snapshot(inst)
+    run_verify(inst, eng, list(range(8)))
+    joint = [gu.raw_outputs(inst, s) for s in range(8)]
+    for s in (3, 6):
+        got = gu.outputs(inst, s)
+        for l in range(4):
+            gu.check_layer(inst, s, l, got[l])
+    for s in range(8):
+        eng.rollback_to(s, lengths[s])
+    for s in range(8):
+        gu.restore(inst, snap)
+        for io in inst.io[s]:
+            io["o"].zero_()
+        run_verify(inst, eng, [s])
+        lone = gu.raw_outputs(inst, s)
+        eng.rollback_to(s, lengths[s])
+        for l in range(4):
+            assert np.array_equal(lone[l], joint[s][l]), f"slot {s} layer {l}"
+    eng.close()
+
+
 # ------------------------------------------------------------------------------ edge cases
 
 def test_empty_context_root_returns_its_value():
