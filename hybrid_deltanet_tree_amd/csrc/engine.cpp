@@ -437,8 +437,10 @@ hdt_status launch_conv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *tre
   return check_hip(e, launch_gdn_conv(c, m.io_dtype == HDT_BF16, stream, p.events()), "GDN conv launch");
 }
 
+// chain_commit: every tree is a chain that will be committed whole (a prefill span):
+// the GDN walk writes each layer's final state straight to the committed state.
 hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, const int8_t (*par)[kMaxNodes],
-                          const int8_t (*dep)[kMaxNodes], hipStream_t stream) {
+                          const int8_t (*dep)[kMaxNodes], hipStream_t stream, bool chain_commit = false) {
   const hdt_model_desc &m = e->desc;
   const int bf = m.io_dtype == HDT_BF16;
   const int G = m.attn_hkv > 0 ? m.attn_hq / m.attn_hkv : 1;
@@ -485,6 +487,7 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
         g.o = io.o;
         const size_t hs = static_cast<size_t>(m.gdn_hv) * m.gdn_dv * m.gdn_dk;
         g.state = s.d.gdn_state + static_cast<size_t>(ki) * hs;
+        g.commit_state = chain_commit ? s.d.gdn_state + static_cast<size_t>(ki) * hs : nullptr;
         const size_t nm = static_cast<size_t>(m.max_nodes);
         g.u_pend = s.u_pend + static_cast<size_t>(ki) * nm * m.gdn_hv * m.gdn_dv;
         g.k_pend = static_cast<char *>(s.k_pend) +
@@ -581,8 +584,10 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
 // Commits a root path of the pending tree: from the host (path, m_len), or, with
 // dev_out set, from the accept walk's output in device memory (m_len is then the
 // tree's node count, the most the path can hold); the caller updates the length.
+// tails_only: a prefill chain whose states and cache rows are already in place; only
+// the conv tails roll.
 hdt_status do_commit(hdt_engine *e, int32_t slot, const int32_t *path, int32_t m_len,
-                     const int32_t *dev_out, hipStream_t stream) {
+                     const int32_t *dev_out, hipStream_t stream, bool tails_only = false) {
   const hdt_model_desc &m = e->desc;
   SlotState &s = e->slots[slot];
   CommitLaunch c;
@@ -603,8 +608,8 @@ hdt_status do_commit(hdt_engine *e, int32_t slot, const int32_t *path, int32_t m
   c.dv = m.gdn_dv;
   c.hkv = m.attn_hkv;
   c.D = m.attn_d;
-  c.gdn_blocks = e->n_gdn > 0 ? e->n_gdn * m.gdn_hv * (m.gdn_dv / (kGdnCols * kCommitCols)) : 0;
-  c.kv_blocks = e->n_attn > 0 ? e->n_attn * m.attn_hkv : 0;
+  c.gdn_blocks = e->n_gdn > 0 && !tails_only ? e->n_gdn * m.gdn_hv * (m.gdn_dv / (kGdnCols * kCommitCols)) : 0;
+  c.kv_blocks = e->n_attn > 0 && !tails_only ? e->n_attn * m.attn_hkv : 0;
   int conv_blocks = 0;
   if (e->n_gdn > 0 && m.gdn_conv > 1) {
     c.conv_state = s.d.gdn_conv_state;
@@ -983,12 +988,14 @@ hdt_status hdt_forward_span(hdt_engine *e, int32_t slot, int32_t T, const hdt_la
     std::memset(dep, 0, sizeof dep);
     plan_tree(c, chain, par[0], dep[0], &cl);
     const hdt_tree tr{slot, c, chain, cio.data()};
-    r = launch_forward(e, 1, &tr, par, dep, st);
+    r = launch_forward(e, 1, &tr, par, dep, st, /*chain_commit=*/true);
     if (r != HDT_OK) return r;
     s.n = c;
     std::memcpy(s.parent, par[0], kMaxNodes);
     std::memcpy(s.depth, dep[0], kMaxNodes);
-    r = do_commit(e, slot, path, c, nullptr, st);
+    // the walk wrote each GDN layer's final state and the tree pass wrote the rows in
+    // chain order at L..L+c-1: only the conv tails remain to be rolled
+    r = do_commit(e, slot, path, c, nullptr, st, /*tails_only=*/true);
     if (r != HDT_OK) return r;
     s.d.length += c;
     if (s.anchor_every > 0 && s.d.length % s.anchor_every == 0) {

@@ -391,6 +391,14 @@ __global__ __launch_bounds__(gdn_threads(DK)) void gdn_tree_kernel(const GdnLaun
     st_io<BF>(T.o, idx, ol[e]);
     T.u_pend[idx] = ul[e];
   }
+  if (T.commit_state) {
+    // a chain committed whole (a prefill span): `cur` is the last node's state, the
+    // same bits a commit replay of the chain would write; each lane owns its slice
+    float *dst = T.commit_state + (static_cast<int64_t>(h) * P.dv + col) * DK + g * R;
+#pragma unroll
+    for (int a = 0; a < R; a += 4)
+      *reinterpret_cast<float4 *>(dst + a) = make_float4(cur[a], cur[a + 1], cur[a + 2], cur[a + 3]);
+  }
 }
 
 // ============================================================================ attention

@@ -40,6 +40,8 @@ struct GdnTree {
   const void *q, *k, *v, *alpha, *beta;  // tree inputs of this layer (io dtype)
   void *o;                               // [n][hv][dv] out
   const float *state;                    // committed state of this layer [hv][dv][dk]
+  float *commit_state;                   // non-null (a chain committed whole): the last node's
+                                         // state is written here, the same address as `state`
   float *u_pend;                         // [max_nodes][hv][dv]: delta-rule corrections u_i
   void *k_pend;                          // [max_nodes][hk][dk]: copy of k (io dtype)
   void *a_pend;                          // [max_nodes][hv]:     copy of alpha (io dtype)
