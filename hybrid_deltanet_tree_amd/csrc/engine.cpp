@@ -498,8 +498,14 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
         std::memcpy(g.depth, dep[t], kMaxNodes);
         a.n_saves = std::max(a.n_saves, plan_saves(tr.n_nodes, par[t], g.save));
         g.need_anc = 0;  // a restore without a kept state replays the parent's root path
-        for (int c = 1; c < tr.n_nodes; ++c)
-          if (par[t][c] != c - 1 && g.save[par[t][c]] < 0) g.need_anc = 1;
+        for (int c = 1; c < tr.n_nodes; ++c) {
+          if (par[t][c] != c - 1) {
+            g.restore_mask |= uint64_t{1} << c;
+            if (g.save[par[t][c]] < 0) g.need_anc = 1;
+          }
+        }
+        for (int c = 0; c < tr.n_nodes; ++c)
+          if (g.save[c] >= 0) g.keep_mask |= uint64_t{1} << c;
       }
       ProfScope p(e, 0);
       hdt_status st =

@@ -47,12 +47,14 @@ __device__ __forceinline__ float rowsum16(float x) {
 
 // ============================================================================ GDN
 
-// LDS layout of the GDN walk: k[n][dk] and s*q[n][dk] (float); per node
-// {alpha, beta, k . s q, parent} (float4); v[n][16], u[n][16], o[n][16] (float);
-// depth[n] and parent[n] (int); then the kept states [n_saves][16][dk] (float);
-// then anc[n][64] and save[n] (int8).
+// LDS layout of the GDN walk: k[n+1][dk] and s*q[n+1][dk] (float); per node
+// {alpha, beta, k . s q, parent} (float4) [n+1]; v[n+1][16], u[n][16], o[n][16]
+// (float); depth[n] and parent[n] (int); then the kept states [n_saves][16][dk]
+// (float); then anc[n][64] and save[n] (int8).  Row n of the operand arrays is never
+// written: the walk's operand load after the last node reads it and drops it.
 __host__ __device__ constexpr size_t gdn_lds_floats(int dk, int n) {
-  return static_cast<size_t>(n) * (2 * dk + 4 + 3 * kGdnCols) + ((2 * n + 3) & ~3);
+  return static_cast<size_t>(n + 1) * (2 * dk + 4 + kGdnCols) + static_cast<size_t>(n) * 2 * kGdnCols +
+         ((2 * n + 3) & ~3);
 }
 
 // Sum of x[a] * y[a] over a lane's R elements in a fixed order: even and odd
@@ -157,13 +159,18 @@ __global__ __launch_bounds__(gdn_threads(DK)) void gdn_tree_kernel(const GdnLaun
   // grid: x = (v head, column group), y = tree
   const GdnTree &T = P.t[blockIdx.y];
   scalar_touch(&T, sizeof(GdnTree), &P.n_trees);
+  // which nodes restore their parent's state first (the parent is not the node just
+  // finished) and which keep theirs for later siblings, tested per node as scalar
+  // bits; the opaque copies keep their loads here, waited on once, out of the walk
+  uint64_t restore_mask = T.restore_mask, keep_mask = T.keep_mask;
+  asm volatile("" : "+s"(restore_mask), "+s"(keep_mask));
   const int n = T.n;
   const int nm = P.n_max;
   float *kf = g_lds;
-  float *qs = kf + nm * DK;
-  float4 *nsc = reinterpret_cast<float4 *>(qs + nm * DK);
-  float *vl = reinterpret_cast<float *>(nsc + nm);
-  float *ul = vl + nm * kGdnCols;
+  float *qs = kf + (nm + 1) * DK;
+  float4 *nsc = reinterpret_cast<float4 *>(qs + (nm + 1) * DK);
+  float *vl = reinterpret_cast<float *>(nsc + nm + 1);
+  float *ul = vl + (nm + 1) * kGdnCols;
   float *ol = ul + nm * kGdnCols;
   int *dep = reinterpret_cast<int *>(ol + nm * kGdnCols);  // depth[n], then parent[n]
   float *kept = reinterpret_cast<float *>(dep + ((2 * nm + 3) & ~3));  // 16-byte aligned
@@ -289,12 +296,21 @@ __global__ __launch_bounds__(gdn_threads(DK)) void gdn_tree_kernel(const GdnLaun
   float cur[R];
 #pragma unroll
   for (int a = 0; a < R; ++a) cur[a] = base[a];
-  int cur_node = -1;
-  auto load_node = [&](int i, GdnNode<R> &x) {
-    lds_row<R>(kf + i * DK + g * R, x.k);
-    lds_row<R>(qs + i * DK + g * R, x.q);
-    x.sc = nsc[i];
-    x.v = vl[i * kGdnCols + lc];
+  // this lane's operands of the next node to load, one node further per load (the
+  // load after the last node reads the spare row n); its u and o slots, one node
+  // further per step
+  const float *k_at = kf + g * R, *q_at = qs + g * R, *v_at = vl + lc;
+  const float4 *sc_at = nsc;
+  float *u_at = ul + lc, *o_at = ol + lc;
+  auto load_node = [&](GdnNode<R> &x) {
+    lds_row<R>(k_at, x.k);
+    lds_row<R>(q_at, x.q);
+    x.sc = *sc_at;
+    x.v = *v_at;
+    k_at += DK;
+    q_at += DK;
+    sc_at += 1;
+    v_at += kGdnCols;
   };
   auto restore = [&](int p) {
     // the parent's state: kept in LDS, or replayed from the committed state along
@@ -331,14 +347,13 @@ __global__ __launch_bounds__(gdn_threads(DK)) void gdn_tree_kernel(const GdnLaun
     }
   };
   // the parent's state into `cur` when it is not the node just finished
-  auto prepare = [&](const GdnNode<R> &x) {
-    const int w = __builtin_amdgcn_readfirstlane(__float_as_int(x.sc.w));
-    const int p = static_cast<int8_t>(w & 0xFF);
-    if (p != cur_node) restore(p);
+  auto prepare = [&](int i, const GdnNode<R> &x) {
+    if ((restore_mask >> i) & 1) {
+      const int w = __builtin_amdgcn_readfirstlane(__float_as_int(x.sc.w));
+      restore(static_cast<int8_t>(w & 0xFF));
+    }
   };
   auto step = [&](int i, const GdnNode<R> &x) {
-    const int w = __builtin_amdgcn_readfirstlane(__float_as_int(x.sc.w));
-    const int keep = static_cast<int8_t>((w >> 8) & 0xFF);
     float A[R];
 #pragma unroll
     for (int a = 0; a < R; ++a) A[a] = x.sc.x * cur[a];
@@ -349,38 +364,40 @@ __global__ __launch_bounds__(gdn_threads(DK)) void gdn_tree_kernel(const GdnLaun
 #pragma unroll
     for (int a = 0; a < R; ++a) cur[a] = fmaf(x.k[a], u, A[a]);
     // every lane of the column stores the same bits (no branch)
-    ul[i * kGdnCols + lc] = u;
-    ol[i * kGdnCols + lc] = fmaf(u, x.sc.z, oa);
-    if (keep >= 0) {
+    *u_at = u;
+    *o_at = fmaf(u, x.sc.z, oa);
+    u_at += kGdnCols;
+    o_at += kGdnCols;
+    if ((keep_mask >> i) & 1) {
+      const int keep = static_cast<int8_t>((__builtin_amdgcn_readfirstlane(__float_as_int(x.sc.w)) >> 8) & 0xFF);
 #pragma unroll
       for (int a = 0; a < R; a += 4)
         *reinterpret_cast<float4 *>(kept + (keep * kGdnCols + lc) * DK + g * R + a) =
             make_float4(cur[a], cur[a + 1], cur[a + 2], cur[a + 3]);
     }
-    cur_node = i;
   };
   // Per node: wait for its operands (loaded during the previous node), restore
   // the parent's state if needed, issue the next node's loads into the other
   // register set, then compute with no LDS read outstanding that the node needs.
-  // The next node's index is clamped so the loads are unconditional.  LDS
+  // The load after the last node reads the spare row, so the loads are unconditional.  LDS
   // operations of a wave complete in order, so the operands are in once at most
   // the previous node's two u / o stores are outstanding (its state copy, when
   // kept, only makes the wait longer).
   GdnNode<R> na, nb;
-  load_node(0, na);
+  load_node(na);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   for (int i = 0; i < n; i += 2) {
     __builtin_amdgcn_s_waitcnt(0xC27F);  // lgkmcnt(2)
-    prepare(na);
+    prepare(i, na);
     __builtin_amdgcn_sched_barrier(0);
-    load_node(min(i + 1, n - 1), nb);
+    load_node(nb);
     __builtin_amdgcn_sched_barrier(0);
     step(i, na);
     if (i + 1 >= n) break;
     __builtin_amdgcn_s_waitcnt(0xC27F);
-    prepare(nb);
+    prepare(i + 1, nb);
     __builtin_amdgcn_sched_barrier(0);
-    load_node(min(i + 2, n - 1), na);
+    load_node(na);
     __builtin_amdgcn_sched_barrier(0);
     step(i + 1, nb);
   }

@@ -51,7 +51,11 @@ struct GdnTree {
   int8_t parent[kMaxNodes];
   int8_t depth[kMaxNodes];
   int8_t save[kMaxNodes];                // LDS slot that keeps node i's state, or -1
+  uint64_t restore_mask;                 // bit i: node i's parent is not node i - 1 (the walk
+                                         // restores the parent's state before node i)
+  uint64_t keep_mask;                    // bit i: save[i] >= 0
 };
+static_assert(sizeof(GdnTree) <= 384, "a tree descriptor is pulled into the scalar cache whole");
 
 struct GdnLaunch {
   GdnTree t[kMaxTrees];
