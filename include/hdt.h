@@ -48,7 +48,7 @@ typedef enum {
   HDT_E_CAPACITY = -4,    /* the slot's buffers cannot hold the rows      */
   HDT_E_ORDER = -5,       /* verb out of sequence (pending round rules)   */
   HDT_E_HIP = -6,         /* a HIP runtime call failed                    */
-  HDT_E_UNSUPPORTED = -7  /* valid request this build does not implement  */
+  HDT_E_UNSUPPORTED = -7  /* valid request the library does not implement */
 } hdt_status;
 
 typedef enum { HDT_F32 = 0, HDT_BF16 = 1 } hdt_dtype;
