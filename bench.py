@@ -9,7 +9,7 @@ after the eager steps); the eager median is reported beside it.  The default wor
 16-node draft tree; inputs are seeded synthetic data resident in HBM before the
 timed region.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload stack_65k] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload stack_65k] [--nodes N] [--no-cpu-baseline]
 
 HBM traffic of the split kernel comes from two rocprofv3 counter passes over the
 bench (FETCH_SIZE, then WRITE_SIZE), scaled by what the same counters read for a
@@ -18,6 +18,7 @@ plain device-to-device copy of known size:
   python bench.py --copy-calibration            # run under rocprofv3 --pmc, twice
   python bench.py --traffic-from F W CF CW      # the four counter CSVs -> profiles/
 """
+import dataclasses
 import argparse
 import json
 import os
@@ -260,6 +261,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="stack_65k")
+    ap.add_argument("--nodes", type=int, default=0, metavar="N",
+                    help="draft trees of N nodes instead of the workload's own size (1 to 64)")
     ap.add_argument("--seed", type=int, default=20261202)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time the eager pass only")
@@ -292,6 +295,10 @@ def main():
     import hybrid_deltanet_tree_amd as hdt
 
     w = synth.WORKLOADS[args.workload]
+    if args.nodes:
+        if not 1 <= args.nodes <= 64:
+            sys.exit("--nodes takes 1 to 64")
+        w = dataclasses.replace(w, n_nodes=args.nodes)
     ns = w.n_slots  # several slots: one joint pass over every slot's tree
     L0 = w.lengths[0]
     parents = [w.tree(args.seed, s) for s in range(ns)]
