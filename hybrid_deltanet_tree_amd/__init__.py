@@ -93,6 +93,9 @@ _sigs = {
     "hdt_profile": (_S, [_E, ctypes.c_int32]),
     "hdt_profile_read": (_S, [_E, ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
                               ctypes.POINTER(ctypes.c_int64)]),
+    "hdt_state_bytes": (_S, [_E, ctypes.POINTER(ctypes.c_int64)]),
+    "hdt_state_copy": (_S, [_E, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                            ctypes.c_void_p]),
     "hdt_last_error": (ctypes.c_char_p, [_E]),
 }
 for _name, (_res, _args) in _sigs.items():
@@ -179,8 +182,10 @@ class Engine:
         if st != 0:
             raise HdtError(st, hdt_last_error(self.h).decode())
 
-    @staticmethod
-    def _io_array(layers):
+    def _io_array(self, layers):
+        if len(layers) != len(self.layer_kind):
+            raise ValueError(f"{len(layers)} per-layer io entries for a model of "
+                             f"{len(self.layer_kind)} layers")
         arr = (hdt_layer_io * len(layers))()
         for l, io in enumerate(layers):
             arr[l] = hdt_layer_io(_ptr(io.get("q")), _ptr(io.get("k")), _ptr(io.get("v")),
@@ -245,6 +250,18 @@ class Engine:
         ms, n = ctypes.c_double(), ctypes.c_int64()
         self._check(hdt_profile_read(self.h, kind, ctypes.byref(ms), ctypes.byref(n)))
         return ms.value, n.value
+
+    def state_bytes(self) -> int:
+        """Size of a state snapshot of this engine's shape."""
+        out = ctypes.c_int64()
+        self._check(hdt_state_bytes(self.h, ctypes.byref(out)))
+        return out.value
+
+    def state_copy(self, slot, buf, restore=False, stream=0):
+        """Save (restore=False) or restore slot's state sections and length through `buf`
+        (a device tensor of at least state_bytes() bytes, 256-byte aligned)."""
+        nbytes = buf.numel() * buf.element_size() if hasattr(buf, "numel") else 0
+        self._check(hdt_state_copy(self.h, slot, _ptr(buf), nbytes, 1 if restore else 0, stream))
 
     def last_error(self) -> str:
         return hdt_last_error(self.h).decode()

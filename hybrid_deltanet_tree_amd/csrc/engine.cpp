@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -84,6 +85,13 @@ struct hdt_engine {
   std::vector<int32_t> kv_ladder;  // bf16 attention: split sizes, ascending
   double prof_ms[6] = {0, 0, 0, 0, 0, 0};
   int64_t prof_count[6] = {0, 0, 0, 0, 0, 0};
+  // committed K/V read-ahead on a stream of the engine's own, forked from and joined to
+  // the caller's stream by events
+  float pf_frac = 0.0f;
+  int pf_mode = 0;
+  hipStream_t pf_stream = nullptr;
+  std::vector<hipEvent_t> pf_ev;
+  uint32_t *pf_sink = nullptr;
 };
 
 namespace {
@@ -223,6 +231,15 @@ hdt_status ensure_alloc(hdt_engine *e) {
       }
     }
   }
+  if (e->pf_frac > 0.0f && e->n_attn > 0 && m.io_dtype == HDT_BF16) {
+    if (hipStreamCreateWithFlags(&e->pf_stream, hipStreamNonBlocking) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void **>(&e->pf_sink), 256) != hipSuccess)
+      return fail(e, HDT_E_HIP, "read-ahead stream or sink allocation failed");
+    e->pf_ev.assign(static_cast<size_t>(e->n_attn) + 2, nullptr);
+    for (auto &ev : e->pf_ev)
+      if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess)
+        return fail(e, HDT_E_HIP, "hipEventCreate failed");
+  }
   if (hipHostMalloc(reinterpret_cast<void **>(&e->walk_m), e->slots.size() * sizeof(int32_t)) != hipSuccess)
     return fail(e, HDT_E_HIP, "hipHostMalloc of the walk results failed");
   for (auto &s : e->slots)
@@ -252,6 +269,13 @@ void free_scratch(hdt_engine *e) {
   }
   if (e->walk_m) (void)hipHostFree(e->walk_m);
   e->walk_m = nullptr;
+  for (auto &ev : e->pf_ev)
+    if (ev) (void)hipEventDestroy(ev);
+  e->pf_ev.clear();
+  if (e->pf_stream) (void)hipStreamDestroy(e->pf_stream);
+  e->pf_stream = nullptr;
+  (void)hipFree(e->pf_sink);
+  e->pf_sink = nullptr;
   e->allocated = false;
 }
 
@@ -321,9 +345,11 @@ void plan_kv_groups(const hdt_engine *e, int64_t L, int32_t n, const int8_t *dep
 // One attention layer with bf16 storage, for group gr of every tree that has one:
 // the split pass over the committed rows, then the tree pass (tree tiles, fold,
 // output, pending rows).
+template <typename AfterSplit>
 hdt_status launch_kv_group(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
                            const int8_t (*par)[kMaxNodes], const int8_t (*dep)[kMaxNodes],
-                           const KvGroups *groups, int gr, int l, int ki, hipStream_t stream) {
+                           const KvGroups *groups, int gr, int l, int ki, hipStream_t stream,
+                           AfterSplit *after_split, int ev_index) {
   const hdt_model_desc &m = e->desc;
   const int G = m.attn_hq / m.attn_hkv;
   KvLaunch a;
@@ -379,19 +405,26 @@ hdt_status launch_kv_group(hdt_engine *e, int32_t n_trees, const hdt_tree *trees
                               "attention split launch");
     if (st != HDT_OK) return st;
   }
+  if (after_split && gr == 0) {
+    hdt_status st = (*after_split)(ev_index);
+    if (st != HDT_OK) return st;
+  }
   ProfScope p(e, 2);
   return check_hip(e, launch_kv_tree(a, m.attn_d, items_b, stream, p.events()), "attention tree launch");
 }
 
 // One attention layer with bf16 storage: one launch pair per group of nodes that
 // share a split size (one group, unless a tree's rows straddle a rung).
+template <typename AfterSplit>
 hdt_status launch_kv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
                            const int8_t (*par)[kMaxNodes], const int8_t (*dep)[kMaxNodes],
-                           const KvGroups *groups, int l, int ki, hipStream_t stream) {
+                           const KvGroups *groups, int l, int ki, hipStream_t stream,
+                           AfterSplit *after_split, int ev_index) {
   int max_groups = 0;
   for (int t = 0; t < n_trees; ++t) max_groups = std::max(max_groups, groups[t].count);
   for (int gr = 0; gr < max_groups; ++gr) {
-    hdt_status st = launch_kv_group(e, n_trees, trees, par, dep, groups, gr, l, ki, stream);
+    hdt_status st = launch_kv_group(e, n_trees, trees, par, dep, groups, gr, l, ki, stream, after_split,
+                                    ev_index);
     if (st != HDT_OK) return st;
   }
   return HDT_OK;
@@ -437,6 +470,36 @@ hdt_status launch_conv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *tre
   return check_hip(e, launch_gdn_conv(c, m.io_dtype == HDT_BF16, stream, p.events()), "GDN conv launch");
 }
 
+// Read-ahead of attention layer ki's committed K/V for every tree, on the engine's
+// read-ahead stream (group 0's split size; a second group reads the same rows).
+hdt_status launch_prefetch(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, const KvGroups *groups,
+                           int ki) {
+  const hdt_model_desc &m = e->desc;
+  PrefetchLaunch a;
+  std::memset(&a, 0, sizeof a);
+  a.hkv = m.attn_hkv;
+  a.row_bytes = m.attn_d * 2;
+  a.mode = e->pf_mode;
+  a.frac = e->pf_frac;
+  a.sink = e->pf_sink;
+  int32_t items = 0;
+  for (int t = 0; t < n_trees; ++t) {
+    const SlotState &s = e->slots[trees[t].slot];
+    PrefetchTree &x = a.t[a.n_trees++];
+    const size_t view = static_cast<size_t>(m.attn_hkv) * s.d.capacity * m.attn_d * 2;
+    x.kc = static_cast<const char *>(s.d.k_cache) + static_cast<size_t>(ki) * view;
+    x.vc = static_cast<const char *>(s.d.v_cache) + static_cast<size_t>(ki) * view;
+    x.cap = s.d.capacity;
+    x.tb0 = s.d.length / kKvTile * kKvTile;
+    x.split = groups[t].split[0];
+    x.n_splits = static_cast<int32_t>((x.tb0 + x.split - 1) / x.split);
+    x.item_begin = items;
+    items += 2 * m.attn_hkv * x.n_splits;
+  }
+  if (items == 0) return HDT_OK;
+  return check_hip(e, launch_kv_prefetch(a, items, e->pf_stream), "read-ahead launch");
+}
+
 // chain_commit: every tree is a chain that will be committed whole (a prefill span):
 // the GDN walk writes each layer's final state straight to the committed state.
 hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, const int8_t (*par)[kMaxNodes],
@@ -451,6 +514,21 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
   if (bf && e->n_attn > 0)
     for (int t = 0; t < n_trees; ++t)
       plan_kv_groups(e, e->slots[trees[t].slot].d.length, trees[t].n_nodes, dep[t], groups[t]);
+  // read-ahead: the first attention layer's rows from the start of the pass; each later
+  // one's once the split pass before it has been enqueued
+  const bool pf = bf && e->pf_stream && e->n_attn > 0 && !chain_commit;
+  int pf_next = 0;  // attention layer (by kind index) read ahead next
+  auto pf_issue = [&](int ev_index) -> hdt_status {
+    if (!pf || pf_next >= e->n_attn) return HDT_OK;
+    if (hipEventRecord(e->pf_ev[ev_index], stream) != hipSuccess ||
+        hipStreamWaitEvent(e->pf_stream, e->pf_ev[ev_index], 0) != hipSuccess)
+      return fail(e, HDT_E_HIP, "read-ahead fork failed");
+    return launch_prefetch(e, n_trees, trees, groups, pf_next++);
+  };
+  {
+    hdt_status st = pf_issue(0);
+    if (st != HDT_OK) return st;
+  }
 
   for (int l = 0; l < m.n_layers; ++l) {
     const int ki = e->kind_index[l];
@@ -512,7 +590,8 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
           check_hip(e, launch_gdn_tree(a, m.gdn_dk, bf, stream, p.events()), "GDN tree launch");
       if (st != HDT_OK) return st;
     } else if (bf) {
-      hdt_status st = launch_kv_layer(e, n_trees, trees, par, dep, groups, l, ki, stream);
+      hdt_status st = launch_kv_layer(e, n_trees, trees, par, dep, groups, l, ki, stream, pf ? &pf_issue : nullptr,
+                                      ki + 1);
       if (st != HDT_OK) return st;
     } else {
       AttnLaunch a;
@@ -583,6 +662,11 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
         if (st != HDT_OK) return st;
       }
     }
+  }
+  if (pf) {  // join: the caller's stream waits for the last read-ahead
+    const size_t j = e->pf_ev.size() - 1;
+    if (hipEventRecord(e->pf_ev[j], e->pf_stream) != hipSuccess || hipStreamWaitEvent(stream, e->pf_ev[j], 0) != hipSuccess)
+      return fail(e, HDT_E_HIP, "read-ahead join failed");
   }
   return HDT_OK;
 }
@@ -668,6 +752,34 @@ hdt_status anchor_copy(hdt_engine *e, int32_t slot, int32_t k, bool save, hipStr
   return HDT_OK;
 }
 
+// Shape signature of a state snapshot: FNV-1a over every field that fixes the layout of
+// the state sections (layer kinds in order, GDN heads and dims, conv width, io dtype) and
+// the attention shape the length is measured against.
+uint64_t shape_signature(const hdt_engine *e) {
+  const hdt_model_desc &m = e->desc;
+  uint64_t h = 0xcbf29ce484222325ull;
+  auto mix = [&h](int64_t x) {
+    for (int b = 0; b < 8; ++b) {
+      h ^= static_cast<uint64_t>(x >> (8 * b)) & 0xFFu;
+      h *= 0x100000001b3ull;
+    }
+  };
+  mix(m.n_layers);
+  for (int l = 0; l < m.n_layers; ++l) mix(e->kind[l]);
+  for (int64_t x : {int64_t(m.gdn_hk), int64_t(m.gdn_hv), int64_t(m.gdn_dk), int64_t(m.gdn_dv),
+                    int64_t(m.gdn_conv), int64_t(m.attn_hq), int64_t(m.attn_hkv), int64_t(m.attn_d),
+                    int64_t(m.io_dtype)})
+    mix(x);
+  return h;
+}
+
+int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+
+int64_t snapshot_bytes(const hdt_engine *e) {
+  return kSnapshotHeaderBytes + round256(static_cast<int64_t>(gdn_state_bytes(e))) +
+         static_cast<int64_t>(conv_tail_bytes(e));
+}
+
 // After an accept walk, the slot's new length is known once the device has run the
 // walk: wait for it and take m from the pinned copy.
 hdt_status settle(hdt_engine *e, int32_t slot) {
@@ -737,6 +849,8 @@ hdt_status hdt_create(const hdt_model_desc *desc, int32_t n_slots, const hdt_slo
   if (e->desc.attn_scale <= 0.0f && n_attn > 0) e->desc.attn_scale = 1.0f / std::sqrt(float(m.attn_d));
   e->n_gdn = n_gdn;
   e->n_attn = n_attn;
+  if (const char *f = std::getenv("HDT_PF_FRAC")) e->pf_frac = static_cast<float>(std::atof(f));
+  if (const char *f = std::getenv("HDT_PF_MODE")) e->pf_mode = std::atoi(f);
   e->esz = m.io_dtype == HDT_BF16 ? 2 : 4;
   if (n_gdn == 0) e->desc.gdn_conv = 0;
   e->conv_C = n_gdn > 0 ? 2 * m.gdn_hk * m.gdn_dk + m.gdn_hv * m.gdn_dv : 0;
@@ -1108,6 +1222,66 @@ hdt_status hdt_reset(hdt_engine *e, int32_t slot, int64_t length) {
   s.pending = false;
   for (int32_t j = 0; j < s.anchor_n; ++j)
     if ((j + 1) * s.anchor_every > length) s.anchor_ok[j] = false;
+  e->err.clear();
+  return HDT_OK;
+}
+
+hdt_status hdt_state_bytes(const hdt_engine *e, int64_t *out) {
+  if (!e || !out) return HDT_E_INVALID;
+  *out = snapshot_bytes(e);
+  return HDT_OK;
+}
+
+hdt_status hdt_state_copy(hdt_engine *e, int32_t slot, void *buf, int64_t buf_bytes, int32_t restore,
+                          void *stream) {
+  if (!e) return HDT_E_INVALID;
+  if (slot < 0 || slot >= static_cast<int32_t>(e->slots.size()))
+    return fail(e, HDT_E_INVALID, "slot %d out of range", slot);
+  if (!buf || (reinterpret_cast<uintptr_t>(buf) & 255u))
+    return fail(e, HDT_E_INVALID, "snapshot buffer missing or not 256-byte aligned");
+  const int64_t need = snapshot_bytes(e);
+  if (buf_bytes < need)
+    return fail(e, HDT_E_INVALID, "snapshot buffer of %lld bytes; the state needs %lld", (long long)buf_bytes,
+                (long long)need);
+  if (settle(e, slot) != HDT_OK) return HDT_E_HIP;
+  SlotState &s = e->slots[slot];
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t sb = static_cast<int64_t>(gdn_state_bytes(e)), cb = static_cast<int64_t>(conv_tail_bytes(e));
+  char *state_sec = static_cast<char *>(buf) + kSnapshotHeaderBytes;
+  char *conv_sec = state_sec + round256(sb);
+  if (!restore) {
+    SnapshotHeader h{};
+    h.magic = kSnapshotMagic;
+    h.signature = shape_signature(e);
+    h.length = s.d.length;
+    h.state_bytes = sb;
+    h.conv_bytes = cb;
+    if (check_hip(e, launch_snapshot_header(h, buf, st), "snapshot header launch") != HDT_OK) return HDT_E_HIP;
+    if (sb > 0 && hipMemcpyAsync(state_sec, s.d.gdn_state, sb, hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return fail(e, HDT_E_HIP, "copy of the state section failed");
+    if (cb > 0 && hipMemcpyAsync(conv_sec, s.d.gdn_conv_state, cb, hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return fail(e, HDT_E_HIP, "copy of the conv tail section failed");
+    e->err.clear();
+    return HDT_OK;
+  }
+  SnapshotHeader h{};
+  if (hipStreamSynchronize(st) != hipSuccess ||
+      hipMemcpy(&h, buf, sizeof h, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(e, HDT_E_HIP, "reading the snapshot header failed");
+  if (h.magic != kSnapshotMagic) return fail(e, HDT_E_INVALID, "the buffer holds no state snapshot");
+  if (h.signature != shape_signature(e) || h.state_bytes != sb || h.conv_bytes != cb)
+    return fail(e, HDT_E_INVALID, "the snapshot was taken from a model of another shape");
+  if (h.length < 0 || h.length > s.d.length)
+    return fail(e, HDT_E_INVALID, "the snapshot holds %lld rows; the slot has %lld committed (a restore keeps "
+                "rows the cache still holds)", (long long)h.length, (long long)s.d.length);
+  if (sb > 0 && hipMemcpyAsync(s.d.gdn_state, state_sec, sb, hipMemcpyDeviceToDevice, st) != hipSuccess)
+    return fail(e, HDT_E_HIP, "restore of the state section failed");
+  if (cb > 0 && hipMemcpyAsync(s.d.gdn_conv_state, conv_sec, cb, hipMemcpyDeviceToDevice, st) != hipSuccess)
+    return fail(e, HDT_E_HIP, "restore of the conv tail section failed");
+  s.d.length = h.length;
+  s.pending = false;
+  for (int32_t j = 0; j < s.anchor_n; ++j)
+    if ((j + 1) * s.anchor_every > s.d.length) s.anchor_ok[j] = false;
   e->err.clear();
   return HDT_OK;
 }

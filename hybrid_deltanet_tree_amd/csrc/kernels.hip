@@ -1198,6 +1198,14 @@ __global__ __launch_bounds__(64) void walk_kernel(const WalkLaunch W) {
   }
 }
 
+// The header of a state snapshot, from the kernel arguments: eight 64-bit words.
+__global__ __launch_bounds__(64) void snapshot_header_kernel(const SnapshotHeader H, uint64_t *dst) {
+  const uint64_t w[8] = {H.magic, H.signature, static_cast<uint64_t>(H.length), static_cast<uint64_t>(H.state_bytes),
+                         static_cast<uint64_t>(H.conv_bytes), 0, 0, 0};
+  const int t = threadIdx.x;
+  if (t < 8) dst[t] = w[t];
+}
+
 template <typename K>
 hipError_t set_lds(K kernel, size_t bytes) {
   // Raised once per kernel to the largest dynamic LDS any launch asks for (the 160 KiB
@@ -1273,6 +1281,11 @@ hipError_t launch_attn_fold(const FoldLaunch &a, int D, int bf16, int n_blocks, 
 
 hipError_t launch_walk(const WalkLaunch &a, hipStream_t s, KernelEvents ev) {
   hipExtLaunchKernelGGL(walk_kernel, dim3(1), dim3(64), 0, s, ev.start, ev.stop, 0, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_snapshot_header(const SnapshotHeader &h, void *dst, hipStream_t s) {
+  hipLaunchKernelGGL(snapshot_header_kernel, dim3(1), dim3(64), 0, s, h, static_cast<uint64_t *>(dst));
   return hipGetLastError();
 }
 

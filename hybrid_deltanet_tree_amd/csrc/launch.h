@@ -167,6 +167,31 @@ struct KvLaunch {
   float c2;                               // softmax scale times log2(e)
 };
 
+// ---------------------------------------------------------------- committed K/V read-ahead
+// Reads part of every split of one attention layer's committed K/V rows and discards it,
+// while the Gated DeltaNet layers before that attention layer keep the HBM idle, so that
+// the split pass finds those lines in the memory-side cache.  Only committed rows (below
+// the split pass's last tile boundary) are read; nothing is written.  One workgroup per
+// (tree, kv head, split, K or V).
+struct PrefetchTree {
+  const void *kc, *vc;                    // the layer's cache [hkv][cap][D]
+  int64_t cap;
+  int64_t tb0;                            // rows below this are read by the split pass
+  int32_t split;                          // keys per split
+  int32_t n_splits;                       // splits with rows below tb0
+  int32_t item_begin;                     // first workgroup of this tree
+};
+
+struct PrefetchLaunch {
+  PrefetchTree t[kMaxTrees];
+  int32_t n_trees;
+  int32_t hkv, row_bytes;
+  int32_t mode;                           // 0: leading tiles of a split, 1: spread, 2: trailing
+  float frac;                             // share of each split's tiles read
+  uint32_t *sink;                         // a word written only if the discarded data hashes
+                                          // to a fixed value (keeps the loads)
+};
+
 // ---------------------------------------------------------------- attention fold
 struct FoldTree {
   const float *part_acc, *part_ml;
@@ -214,6 +239,21 @@ struct WalkLaunch {
   int32_t n;
 };
 
+// ---------------------------------------------------------------- state snapshot header
+// The first bytes of a state snapshot (hdt_state_copy): written by a one-wave kernel from
+// its arguments, read back by the host before a restore.
+struct SnapshotHeader {
+  uint64_t magic;       // kSnapshotMagic
+  uint64_t signature;   // shape of the engine that wrote it
+  int64_t length;       // committed rows when it was taken
+  int64_t state_bytes;  // GDN state section
+  int64_t conv_bytes;   // conv tail section
+  int64_t reserved[3];
+};
+constexpr uint64_t kSnapshotMagic = 0x3150414E53544448ull;  // "HDTSNAP1" little-endian
+constexpr int64_t kSnapshotHeaderBytes = 256;                // sections start 256-byte aligned
+static_assert(sizeof(SnapshotHeader) == 64, "eight 64-bit words");
+
 // ---------------------------------------------------------------- host entry points
 // Each returns the result of hipGetLastError() after enqueueing.  With ev0 / ev1
 // set, the dispatch itself records its start and end time into them (the
@@ -231,10 +271,12 @@ hipError_t launch_attn_fold(const FoldLaunch &a, int D, int bf16, int n_blocks, 
 hipError_t launch_kv_split(const KvLaunch &a, int D, int max_items, hipStream_t s,
                            KernelEvents ev);
 hipError_t launch_kv_tree(const KvLaunch &a, int D, int max_items, hipStream_t s, KernelEvents ev);
+hipError_t launch_kv_prefetch(const PrefetchLaunch &a, int n_blocks, hipStream_t s);
 hipError_t launch_commit(const CommitLaunch &a, int dk, int bf16, int n_blocks, hipStream_t s,
                          KernelEvents ev);
 hipError_t launch_gdn_conv(const ConvLaunch &a, int bf16, hipStream_t s, KernelEvents ev);
 hipError_t launch_walk(const WalkLaunch &a, hipStream_t s, KernelEvents ev);
+hipError_t launch_snapshot_header(const SnapshotHeader &h, void *dst, hipStream_t s);
 // Channels one conv thread handles (16 bytes of io dtype).
 constexpr int conv_channels_per_thread(int bf16) { return bf16 ? 8 : 4; }
 

@@ -152,15 +152,21 @@ typedef struct {
 typedef struct hdt_engine hdt_engine;
 
 /*
- * Create an engine over n_slots caller-owned slots.  Validates every field;
- * allocates nothing on the device (scratch is allocated on the current HIP
- * device at the first call that launches work).  *out is NULL on failure.
+ * Create an engine over n_slots caller-owned slots: the one call per model load of
+ * the flat C ABI in "How ignis serves a request" ("The shape of the process"), with
+ * the model described by its layer kinds and head shapes ("Adding a model", "The
+ * model layer: architecture registry and per-model state").  Validates every field;
+ * allocates nothing on the device (scratch is allocated on the current HIP device at
+ * the first call that launches work).  *out is NULL on failure.
+ * Errors: HDT_E_INVALID (a field out of range), HDT_E_UNSUPPORTED (a shape the kernels
+ * do not implement).
  */
 hdt_status hdt_create(const hdt_model_desc *desc, int32_t n_slots, const hdt_slot_desc *slots,
                       hdt_engine **out);
 
-/* Free the engine and its scratch (not the caller's buffers).  Waits for the
- * device first.  NULL is a no-op. */
+/* Free the engine and its scratch (not the caller's buffers): the model-unload end of
+ * the lifecycle in "How ignis serves a request" ("The shape of the process").  Waits
+ * for the device first.  NULL is a no-op. */
 void hdt_destroy(hdt_engine *eng);
 
 /*
@@ -184,7 +190,9 @@ void hdt_destroy(hdt_engine *eng);
 hdt_status hdt_forward_tree(hdt_engine *eng, int32_t n_trees, const hdt_tree *trees,
                             void *stream);
 
-/* forward_block: forward_tree of one chain of n nodes (parent[i] = i - 1). */
+/* forward_block ("Adding a model", step 4 of "The adapter path in ten steps": the hot
+ * verb that verifies a block of drafted tokens): forward_tree of one chain of n nodes
+ * (parent[i] = i - 1), 1 <= n <= HDT_MAX_NODES.  Same errors as forward_tree. */
 hdt_status hdt_forward_block(hdt_engine *eng, int32_t slot, int32_t n, const hdt_layer_io *io,
                              void *stream);
 
@@ -216,7 +224,9 @@ hdt_status hdt_forward_span(hdt_engine *eng, int32_t slot, int32_t T, const hdt_
 hdt_status hdt_set_anchors(hdt_engine *eng, int32_t slot, int64_t every, int32_t n_max,
                            float *state, void *conv);
 
-/* The highest position p <= n whose anchor holds a state, or -1 (none). */
+/* The highest position p <= n whose anchor holds a state, or -1 (none): where a later
+ * turn can resume ("One request, end to end", 2.5: a prefix is reused up to its last
+ * recurrent-state anchor).  Host only.  Errors: HDT_E_INVALID. */
 hdt_status hdt_anchor_below(const hdt_engine *eng, int32_t slot, int64_t n, int64_t *out);
 
 /*
@@ -234,7 +244,9 @@ hdt_status hdt_commit_tree(hdt_engine *eng, int32_t slot, const int32_t *path, i
                            void *stream);
 
 /*
- * rollback_to(n): keep exactly n tokens.  n = length drops the pending round
+ * rollback_to(n) ("Adding a model", step 4 of "The adapter path in ten steps", a hot
+ * verb; "The tests a new model must pass": a block verify followed by a rollback):
+ * keep exactly n tokens.  n = length drops the pending round
  * (or does nothing when none is pending).  length < n <= length + c, c being
  * the pending tree's leading chain (nodes 0..c-1 with parent[i] = i-1), keeps
  * that chain prefix: the same as hdt_commit_tree with path 0..n-length-1.
@@ -267,16 +279,21 @@ hdt_status hdt_rollback_to(hdt_engine *eng, int32_t slot, int64_t n, void *strea
 hdt_status hdt_walk_commit(hdt_engine *eng, int32_t slot, const int32_t *draft, const int32_t *target,
                            int32_t *out, void *stream);
 
-/* kv.length: committed rows of a slot (host value; after hdt_walk_commit it waits for
- * the device to finish that walk). */
+/* kv.length ("Adding a model", step 4 of "The adapter path in ten steps"): committed
+ * rows of a slot (host value; after hdt_walk_commit it waits for the device to finish
+ * that walk).  Errors: HDT_E_INVALID, HDT_E_HIP. */
 hdt_status hdt_kv_length(const hdt_engine *eng, int32_t slot, int64_t *out);
 
-/* reset: set a slot's committed length (0..capacity) and drop any pending
- * round.  The caller owns the state and cache contents. */
+/* reset ("Adding a model", step 4 of "The adapter path in ten steps"): set a slot's
+ * committed length (0..capacity) and drop any pending round; anchors above the new
+ * length are emptied.  The caller owns the state and cache contents.
+ * Errors: HDT_E_INVALID, HDT_E_HIP. */
 hdt_status hdt_reset(hdt_engine *eng, int32_t slot, int64_t length);
 
 /*
- * Tree metadata on the host, as the kernels use it: depth[n]; mask[n] with bit
+ * Tree metadata of one merged draft tree ("One request, end to end", 2.6: the drafts
+ * are merged into one tree verified in one pass) on the host, as the kernels use it:
+ * depth[n]; mask[n] with bit
  * j set when node j is an ancestor-or-self of node i; anc[n][HDT_MAX_NODES]
  * with anc[i][d] the ancestor of i at depth d (-1 beyond depth(i));
  * pos[n] = L + depth.  Any output may be NULL.  No engine, no device.
@@ -298,9 +315,14 @@ hdt_status hdt_tree_meta(int32_t n, const int32_t *parent, int64_t L, int32_t *d
  * committed.  Errors: HDT_E_INVALID.
  */
 hdt_status hdt_split_size(const hdt_engine *eng, int32_t slot, int64_t position, int64_t *out);
+/* (The split rule is how the kernels keep the rule of "Adding a model", step 4 of "The
+ * adapter path in ten steps", that a verified row equals the decode step's row: a row's
+ * reduction order follows from its own position.)  Host only. */
 
 /*
- * Kernel timing for measurement.  hdt_profile(eng, 1) starts recording a HIP
+ * Kernel timing for measurement (the per-device verify cost that StairCut prices its
+ * cuts with, "One request, end to end", 2.6, is built from such timings).
+ * hdt_profile(eng, 1) starts recording a HIP
  * event pair around every launch on the launch stream; hdt_profile_read waits
  * for the recorded events and returns, for kernel class `kind` (0 = GDN tree
  * walk, 1 = attention split pass, 2 = attention fold, 3 = commit, 4 = GDN conv,
@@ -310,7 +332,37 @@ hdt_status hdt_split_size(const hdt_engine *eng, int32_t slot, int64_t position,
 hdt_status hdt_profile(hdt_engine *eng, int32_t enable);
 hdt_status hdt_profile_read(hdt_engine *eng, int32_t kind, double *ms, int64_t *launches);
 
-/* Text of the last error on this engine ("" when none); never NULL. */
+/*
+ * State snapshot ("Adding a model", "The model layer: architecture registry and
+ * per-model state": a model's cache state has sections copied whole and views sliced
+ * by length, with nbytes, clone, restore and a signature that refuses a restore across
+ * shapes).  The sections here are the recurrent state (gdn.S) and the conv tails
+ * (gdn.conv); the views are the slot's K/V cache rows, which stay where they are.
+ *
+ * hdt_state_bytes: the size of a snapshot of this engine's shape (nbytes).
+ *
+ * hdt_state_copy(restore = 0) (clone): writes into `buf` (device memory owned by the
+ * caller, 256-byte aligned, buf_bytes >= hdt_state_bytes) a 256-byte header holding the
+ * engine's shape signature and the slot's committed length, then the state and conv
+ * sections, enqueued on `stream`.  A pending round is left as it is (its rows are not
+ * committed and are not part of the snapshot).
+ *
+ * hdt_state_copy(restore = 1): waits for `stream`, reads the header, and refuses
+ * (HDT_E_INVALID, nothing changed) a buffer that holds no snapshot, a snapshot of an
+ * engine of another shape, or one taken at more committed rows than the slot now holds
+ * (the cache must still hold the rows below the snapshot's length).  Otherwise it copies
+ * the sections back on `stream`, sets the slot's length to the snapshot's, drops any
+ * pending round and empties the anchors above that length.  Not for graph capture.
+ * Errors: HDT_E_INVALID, HDT_E_HIP.
+ */
+hdt_status hdt_state_bytes(const hdt_engine *eng, int64_t *out);
+hdt_status hdt_state_copy(hdt_engine *eng, int32_t slot, void *buf, int64_t buf_bytes, int32_t restore,
+                          void *stream);
+
+/* Text of the last error on this engine ("" when none); never NULL.  The flat C ABI of
+ * "How ignis serves a request" ("The shape of the process") lets no exception cross;
+ * each call returns a status and this names the failed check.  Owned by the engine,
+ * valid until its next call. */
 const char *hdt_last_error(const hdt_engine *eng);
 
 #ifdef __cplusplus

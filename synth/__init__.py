@@ -280,15 +280,17 @@ def gdn_state(w: Workload, seed: int, slot: int, layer: int) -> np.ndarray:
 
 
 def attn_inputs(w: Workload, seed: int, slot: int, layer: int, n: int, tag: str = "verify",
-                sharp: bool = False):
+                sharp: bool = False, q_scale: float = 1.0, v_scale: float = 1.0):
     """q [n][hq][D]; tree k, v [n][hkv][D].  sharp=True draws q, k without normalisation
-    (a parity-only variant whose softmax is far from flat)."""
+    (a parity-only variant whose softmax is far from flat), q as q_scale N(0,1).  v_scale
+    multiplies the tree's value rows (parity-only: a power of two makes every tree row's
+    share of an output visible even under a flat softmax over a long context)."""
     base = f"{w.name}/s{slot}/l{layer}/{tag}/attn"
     dt = w.dtype
     kq = NORMAL if sharp else NORMAL_L2
-    q = fill(seed, base + "/q", kq, (n, w.attn_hq, w.attn_d), dtype=dt)
+    q = fill(seed, base + "/q", kq, (n, w.attn_hq, w.attn_d), dtype=dt, scale=q_scale)
     k = fill(seed, base + "/k", kq, (n, w.attn_hkv, w.attn_d), dtype=dt)
-    v = fill(seed, base + "/v", NORMAL, (n, w.attn_hkv, w.attn_d), dtype=dt)
+    v = fill(seed, base + "/v", NORMAL, (n, w.attn_hkv, w.attn_d), dtype=dt, scale=v_scale)
     return q, k, v
 
 

@@ -54,9 +54,12 @@ class Instance:
 
     def __init__(self, w: synth.Workload, seed: int, *, device="cuda", lengths=None,
                  trees=None, n_nodes=None, capacity=None, sharp=False, poison=False,
-                 keep_host=True, tag="verify"):
+                 keep_host=True, tag="verify", q_scale=1.0, v_scale=1.0, host_layers=None):
         torch = _torch()
         self.w, self.seed, self.device, self.sharp = w, seed, device, sharp
+        self.q_scale, self.v_scale = q_scale, v_scale
+        # layers whose resident data stays on the host (keep_host=False: none unless listed)
+        self.host_layers = set(range(len(w.layer_kind))) if keep_host else set(host_layers or ())
         self.lengths = list(lengths if lengths is not None else w.lengths)
         ns = len(self.lengths)
         if trees is None:
@@ -97,8 +100,7 @@ class Instance:
                 if kind == 0:
                     a = synth.gdn_state(w, seed, s, l)
                     st[gi] = torch.from_numpy(a).to(device)
-                    if keep_host:
-                        hs.append(a)
+                    hs.append(a if l in self.host_layers else None)
                     gi += 1
             self.state.append(st)
             self.h_state.append(hs)
@@ -110,18 +112,19 @@ class Instance:
             for l, kind in enumerate(w.layer_kind):
                 if kind != 1:
                     continue
-                hK = np.zeros((w.attn_hkv, cap, w.attn_d), np.uint16 if dt == "bf16" else np.float32)
-                hV = np.zeros_like(hK)
+                keep = l in self.host_layers
+                if keep:
+                    hK = np.zeros((w.attn_hkv, cap, w.attn_d), np.uint16 if dt == "bf16" else np.float32)
+                    hV = np.zeros_like(hK)
                 for h in range(w.attn_hkv):
                     K, V = synth.kv_rows(w, seed, s, l, h, 0, L, sharp=sharp)
                     if L > 0:
                         kc[ai, h, :L] = to_device(K, dt, device)
                         vc[ai, h, :L] = to_device(V, dt, device)
-                    if keep_host:
+                    if keep:
                         hK[h, :L], hV[h, :L] = K, V
-                if keep_host:
-                    hk.append(hK)
-                    hv.append(hV)
+                hk.append(hK if keep else None)
+                hv.append(hV if keep else None)
                 ai += 1
             self.kc.append(kc)
             self.vc.append(vc)
@@ -147,7 +150,8 @@ class Instance:
                 io = {name: to_device(arr, dt, dev) for name, arr in host.items()}
                 io["o"] = torch.zeros((n, w.gdn_hv, w.gdn_dv), dtype=_tdtype(dt), device=dev)
             else:
-                q, k, v = synth.attn_inputs(w, self.seed, s, l, n, tag, sharp=self.sharp)
+                q, k, v = synth.attn_inputs(w, self.seed, s, l, n, tag, sharp=self.sharp,
+                                            q_scale=self.q_scale, v_scale=self.v_scale)
                 host = dict(q=q, k=k, v=v)
                 io = {name: to_device(arr, dt, dev) for name, arr in host.items()}
                 io["o"] = torch.zeros((n, w.attn_hq, w.attn_d), dtype=_tdtype(dt), device=dev)

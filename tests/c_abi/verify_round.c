@@ -155,6 +155,13 @@ int main(void) {
   orc_attn_tree(HQ, HKV, D, N, parent, L, CAP, Kc, Vc, aq, ak, av, 1, 1.0f / 16.0f, ref);
   const double e_att = rel_err(go, 1, ref, (size_t)N * HQ * D);
 
+  /* a state snapshot before the commit (restored at the end) */
+  int64_t snap_bytes = 0;
+  CHECK_HDT(eng, hdt_state_bytes(eng, &snap_bytes));
+  void *snap = NULL;
+  CHECK_HIP(hipMalloc(&snap, (size_t)snap_bytes));
+  CHECK_HDT(eng, hdt_state_copy(eng, 0, snap, snap_bytes, 0, NULL));
+
   /* commit a root path: the state against the oracle's sequential recurrence, the cache
      rows bit for bit */
   CHECK_HDT(eng, hdt_commit_tree(eng, 0, path, 4, NULL));
@@ -172,11 +179,21 @@ int main(void) {
       rows_ok &= memcmp(rows + ((size_t)h * CAP + L + d) * D, ak + ((size_t)path[d] * HKV + h) * D, D * 2) == 0;
   int64_t len = 0;
   CHECK_HDT(eng, hdt_kv_length(eng, 0, &len));
+
+  /* restore the snapshot: the committed state before the round, bit for bit, at length L */
+  CHECK_HDT(eng, hdt_state_copy(eng, 0, snap, snap_bytes, 1, NULL));
+  CHECK_HIP(hipDeviceSynchronize());
+  CHECK_HIP(hipMemcpy(gS, dS, sizeof(float) * HV * DK * DK, hipMemcpyDeviceToHost));
+  int64_t len_back = 0;
+  CHECK_HDT(eng, hdt_kv_length(eng, 0, &len_back));
+  const int restored = memcmp(gS, S, sizeof(float) * HV * DK * DK) == 0 && len_back == L;
+  CHECK_HIP(hipFree(snap));
   hdt_destroy(eng);
 
-  printf("gdn output %.3e, attention output %.3e, committed state %.3e, rows %s, length %lld\n",
-         e_gdn, e_att, e_state, rows_ok ? "equal" : "DIFFER", (long long)len);
-  const int ok = e_gdn <= 2e-2 && e_att <= 2e-2 && e_state <= 2e-3 && rows_ok && len == L + 4;
+  printf("gdn output %.3e, attention output %.3e, committed state %.3e, rows %s, length %lld, "
+         "snapshot restore %s\n",
+         e_gdn, e_att, e_state, rows_ok ? "equal" : "DIFFER", (long long)len, restored ? "exact" : "WRONG");
+  const int ok = e_gdn <= 2e-2 && e_att <= 2e-2 && e_state <= 2e-3 && rows_ok && len == L + 4 && restored;
   printf("%s\n", ok ? "PASS" : "FAIL");
   return ok ? 0 : 1;
 }

@@ -60,11 +60,27 @@ def max_rel_per_head(got, ref):
     return worst
 
 
+def elementwise_worst(got, ref, floor=1e-2):
+    """P17's elementwise worst case, reported beside the per-head figure: the largest
+    |a - b| / |b| over elements whose reference is at least `floor` times the largest
+    reference magnitude of its head (smaller elements have no stable relative error)."""
+    worst = 0.0
+    for hh in range(ref.shape[1]):
+        r = ref[:, hh].astype(np.float64)
+        g = got[:, hh].astype(np.float64)
+        big = np.abs(r) >= floor * np.abs(r).max()
+        if big.any():
+            worst = max(worst, float((np.abs(g - r)[big] / np.abs(r)[big]).max()))
+    return worst
+
+
 def check_layer(inst, s, l, got, tol=None):
     ref = oracle_layer(inst, s, l)
     tol = tol if tol is not None else (TOL_BF16_OUT if inst.w.dtype == "bf16" else TOL_F32)
     err = max_rel_per_head(got, ref)
     assert np.isfinite(got).all(), f"layer {l}: non-finite output"
+    print(f"    slot {s} layer {l}: per-head {err:.2e}, elementwise worst "
+          f"{elementwise_worst(got, ref):.2e}", flush=True)
     assert err <= tol, f"slot {s} layer {l}: max relative error {err:.3e} > {tol}"
     return err
 

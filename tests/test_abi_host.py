@@ -271,3 +271,55 @@ def test_one_hip_runtime_in_process():
     with open("/proc/self/maps") as f:
         paths = {line.split()[-1] for line in f if "libamdhip64" in line}
     assert len(paths) == 1, paths
+
+
+def test_io_list_must_have_one_entry_per_layer():
+    """The binding refuses a per-layer io list of the wrong length before the library could
+    read past the end of the array it builds."""
+    e = make_engine()
+    for layers in (fake_layers()[:3], fake_layers() + fake_layers()[:1], []):
+        with pytest.raises(ValueError):
+            e.forward_tree([(0, [-1, 0], layers)])
+        with pytest.raises(ValueError):
+            e.forward_block(0, 2, layers)
+        with pytest.raises(ValueError):
+            e.forward_span(0, 2, layers)
+    assert e.kv_length(0) == 100
+    e.close()
+
+
+class _FakeBuf:
+    """A device-buffer stand-in: an address and a size, never dereferenced on the host."""
+
+    def __init__(self, ptr, nbytes):
+        self.ptr, self.nbytes = ptr, nbytes
+
+    def data_ptr(self):
+        return self.ptr
+
+    def numel(self):
+        return self.nbytes
+
+    def element_size(self):
+        return 1
+
+
+def test_state_snapshot_size_and_host_refusals():
+    e = make_engine()
+    n = e.state_bytes()
+    # header, the GDN state (3 layers x 4 heads x 64 x 64 float32), no conv tails
+    assert n == 256 + 3 * 4 * 64 * 64 * 4
+    conv_slot = dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=10, length=1,
+                     conv_state=FAKE)
+    ec = make_engine(gdn_conv=4, gdn_conv_weight=FAKE, slots=[conv_slot])
+    C = 2 * 2 * 64 + 4 * 64
+    assert ec.state_bytes() == 256 + 3 * 4 * 64 * 64 * 4 + 3 * 3 * C * 2
+    ec.close()
+    for slot, buf, status in ((5, _FakeBuf(FAKE, n), -1), (0, _FakeBuf(0, n), -1),
+                              (0, _FakeBuf(FAKE + 16, n), -1), (0, _FakeBuf(FAKE, n - 1), -1)):
+        for restore in (False, True):
+            with pytest.raises(hdt.HdtError) as err:
+                e.state_copy(slot, buf, restore=restore)
+            assert err.value.status == status
+    assert e.kv_length(0) == 100
+    e.close()

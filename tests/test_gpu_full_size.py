@@ -45,16 +45,17 @@ def _check_attn_sampled(inst, s, l, nodes, heads):
     ai = sum(1 for x in w.layer_kind[:l] if x == 1)
     got = gu.outputs(inst, s)[l]
     assert np.isfinite(got).all()
-    worst = 0.0
+    worst = ew = 0.0
     for j in heads:
         ref = np.stack([oracle.attn_row(inst.trees[s], inst.lengths[s], inst.h_kc[s][ai],
                                         inst.h_vc[s][ai], h["q"], h["k"], h["v"], i, j)
                         for i in nodes])
         err = rel_err(got[nodes, j], ref)
         worst = max(worst, err)
+        ew = max(ew, gu.elementwise_worst(got[nodes, j][:, None], ref[:, None]))
         assert err <= gu.TOL_BF16_OUT, f"slot {s} layer {l} q head {j}: {err:.3e}"
     _say(f"  slot {s} layer {l} (attention, {len(nodes)} nodes x {len(heads)} heads): "
-         f"max relative error {worst:.2e}")
+         f"max relative error {worst:.2e}, elementwise worst {ew:.2e}")
 
 
 def _check_commit(inst, eng, s, path):
@@ -78,8 +79,9 @@ def _check_commit(inst, eng, s, path):
                     f"slot {s} layer {l}: committed conv tail"
             ref = oracle.gdn_commit(path, inst.h_state[s][gi], k, v, h["alpha"], h["beta"])
             got = inst.state[s][gi].cpu().numpy()
-            err = rel_err(got, ref)
-            assert err <= gu.TOL_F32, f"slot {s} layer {l}: committed state {err:.3e}"
+            for hh in range(w.gdn_hv):  # per head (P17)
+                err = rel_err(got[hh], ref[hh])
+                assert err <= gu.TOL_F32, f"slot {s} layer {l} head {hh}: committed state {err:.3e}"
             gi += 1
         else:
             m = len(path)
@@ -95,7 +97,7 @@ def _check_commit(inst, eng, s, path):
 def _bench_capacity(w, parent):
     """The slot capacity bench.py allocates for the default run (it sets the split size)."""
     path = synth.accepted_path(SEED, f"{w.name}/bench-path", parent)
-    return w.lengths[0] + (5 + 2 * 20) * len(path) + 64
+    return w.lengths[0] + (10 + 2 * 50) * len(path) + 64
 
 
 def _nodes_sample(parent):
@@ -181,4 +183,109 @@ def test_joint4_slice_at_full_size():
     eng.rollback_to(1, L1, gu.stream())
     gu.sync()
     assert eng.kv_length(1) == L1
+    eng.close()
+
+
+# ------------------------------------------------------------------------------ peaked and loud
+
+def _base2_scores(inst, s, l, node, j):
+    """Base-2 scores c2 q.k of row (node, q head j) over the committed keys (float64)."""
+    w, h = inst.w, inst.host[s][l]
+    ai = sum(1 for x in w.layer_kind[:l] if x == 1)
+    m = j // (w.attn_hq // w.attn_hkv)
+    L = inst.lengths[s]
+    q = synth.bf16_bits_to_f32(h["q"][node, j]).astype(np.float64)
+    K = synth.bf16_bits_to_f32(inst.h_kc[s][ai][m, :L]).astype(np.float64)
+    return (K @ q) * (1.0 / np.sqrt(w.attn_d)) / np.log(2.0)
+
+
+def _rescales(scores, split, tile=32, lazy=8.0):
+    """How often, within a split, a tile's max exceeds the running max by more than `lazy`
+    (the rule under which the running max moves after a split's first tile)."""
+    count = 0
+    for s0 in range(0, len(scores), split):
+        run = -np.inf
+        for t0 in range(s0, min(s0 + split, len(scores)), tile):
+            mt = scores[t0:t0 + tile].max()
+            if run > -np.inf and mt > run + lazy:
+                count += 1
+            if mt > run + lazy or run == -np.inf:
+                run = mt
+    return count
+
+
+@pytest.mark.parametrize("wname", ["stack_65k", "stack_262k"])
+def test_peaked_softmax_slice_at_full_size(wname):
+    """Unnormalised keys and queries drawn as 6 N(0,1): scores spread over tens of units, so
+    within the 1,056-key (65,536) and 8,384-key (262,144) splits the running max moves after
+    the first tile, and the split maxima differ widely in the fold.  Sampled rows against
+    the oracle's row routine."""
+    base = synth.WORKLOADS[wname]
+    w = _slice(base)
+    parent = base.tree(SEED, 0)
+    cap = _bench_capacity(base, parent)
+    _say(f"{wname} slice, peaked softmax: L={w.lengths[0]} nodes={len(parent)}")
+    inst = Instance(w, SEED, trees=[parent], capacity=[cap], sharp=True, q_scale=6.0)
+    eng = inst.engine(max_nodes=len(parent))
+    split = eng.split_size(0, w.lengths[0])
+    assert split == (1056 if wname == "stack_65k" else 8384)  # 8,384: two row groups at 32 nodes
+    moves = sum(_rescales(_base2_scores(inst, 0, 3, i, j), split) for i in (0, len(parent) - 1) for j in (0, 23))
+    assert moves > 0, "the inputs never move the running max inside a split"
+    _say(f"  running-max moves inside splits (4 sampled rows, from the inputs): {moves}")
+    eng.forward_tree([inst.tree_arg(0)], gu.stream())
+    gu.sync()
+    _check_attn_sampled(inst, 0, 3, _nodes_sample(parent), [0, 7, 14, 23])
+    eng.close()
+
+
+@pytest.mark.parametrize("wname", ["stack_65k", "stack_262k"])
+def test_loud_tree_rows_slice_at_full_size(wname):
+    """Tree value rows scaled by 4,096 (a power of two, so the bf16 rows stay exact): under
+    the flat softmax of unit keys each tree row then carries a visible share of its
+    descendants' outputs, so a missing, extra or misplaced ancestor row moves a sampled row
+    far past 2e-2.  Every node's rows are checked on four q heads."""
+    base = synth.WORKLOADS[wname]
+    w = _slice(base)
+    parent = base.tree(SEED, 0)
+    cap = _bench_capacity(base, parent)
+    _say(f"{wname} slice, loud tree rows: L={w.lengths[0]} nodes={len(parent)}")
+    inst = Instance(w, SEED, trees=[parent], capacity=[cap], v_scale=4096.0)
+    eng = inst.engine(max_nodes=len(parent))
+    eng.forward_tree([inst.tree_arg(0)], gu.stream())
+    gu.sync()
+    # the tree rows dominate: without them an output row is a flat average of unit-variance
+    # values over the whole context, about 1 / sqrt(L) in size
+    got = gu.outputs(inst, 0)[3]
+    assert np.abs(got).max() > 25.0 / np.sqrt(w.lengths[0])
+    _check_attn_sampled(inst, 0, 3, list(range(len(parent))), [0, 7, 14, 23])
+    eng.close()
+
+
+def test_verify_equals_decode_at_65536():
+    """verified row == decode row bit for bit at the benchmark's length: the shortest leaf
+    path of the draft tree, decoded token by token through the four-layer slice (1,056-key
+    splits, the fold over 62 committed splits)."""
+    base = synth.WORKLOADS["stack_65k"]
+    w = _slice(base)
+    parent = base.tree(SEED, 0)
+    L = w.lengths[0]
+    inst = Instance(w, SEED, trees=[parent], capacity=[_bench_capacity(base, parent)])
+    eng = inst.engine(max_nodes=len(parent))
+    eng.forward_tree([inst.tree_arg(0)], gu.stream())
+    gu.sync()
+    verified = gu.raw_outputs(inst, 0)
+    eng.rollback_to(0, L, gu.stream())
+    d = synth.depths(parent)
+    leaves = [i for i in range(len(parent)) if i not in parent]
+    leaf = min(leaves, key=lambda i: (d[i], i))
+    path = synth.root_path(parent, leaf)
+    _say(f"stack_65k slice: decode of leaf {leaf}'s root path {path} at L={L}")
+    for j in path:
+        step_io = gu.row_io(inst, 0, j)
+        eng.forward_tree([(0, [-1], step_io)], gu.stream())
+        eng.commit_tree(0, [0], gu.stream())
+        gu.sync()
+        for l in range(4):
+            row = to_host(step_io[l]["o"], w.dtype)[0]
+            assert np.array_equal(row, verified[l][j]), f"node {j} layer {l}: verify row != decode row"
     eng.close()
