@@ -13,7 +13,6 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
-#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -85,13 +84,6 @@ struct hdt_engine {
   std::vector<int32_t> kv_ladder;  // bf16 attention: split sizes, ascending
   double prof_ms[6] = {0, 0, 0, 0, 0, 0};
   int64_t prof_count[6] = {0, 0, 0, 0, 0, 0};
-  // committed K/V read-ahead on a stream of the engine's own, forked from and joined to
-  // the caller's stream by events
-  float pf_frac = 0.0f;
-  int pf_mode = 0;
-  hipStream_t pf_stream = nullptr;
-  std::vector<hipEvent_t> pf_ev;
-  uint32_t *pf_sink = nullptr;
 };
 
 namespace {
@@ -231,15 +223,6 @@ hdt_status ensure_alloc(hdt_engine *e) {
       }
     }
   }
-  if (e->pf_frac > 0.0f && e->n_attn > 0 && m.io_dtype == HDT_BF16) {
-    if (hipStreamCreateWithFlags(&e->pf_stream, hipStreamNonBlocking) != hipSuccess ||
-        hipMalloc(reinterpret_cast<void **>(&e->pf_sink), 256) != hipSuccess)
-      return fail(e, HDT_E_HIP, "read-ahead stream or sink allocation failed");
-    e->pf_ev.assign(static_cast<size_t>(e->n_attn) + 2, nullptr);
-    for (auto &ev : e->pf_ev)
-      if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess)
-        return fail(e, HDT_E_HIP, "hipEventCreate failed");
-  }
   if (hipHostMalloc(reinterpret_cast<void **>(&e->walk_m), e->slots.size() * sizeof(int32_t)) != hipSuccess)
     return fail(e, HDT_E_HIP, "hipHostMalloc of the walk results failed");
   for (auto &s : e->slots)
@@ -269,13 +252,6 @@ void free_scratch(hdt_engine *e) {
   }
   if (e->walk_m) (void)hipHostFree(e->walk_m);
   e->walk_m = nullptr;
-  for (auto &ev : e->pf_ev)
-    if (ev) (void)hipEventDestroy(ev);
-  e->pf_ev.clear();
-  if (e->pf_stream) (void)hipStreamDestroy(e->pf_stream);
-  e->pf_stream = nullptr;
-  (void)hipFree(e->pf_sink);
-  e->pf_sink = nullptr;
   e->allocated = false;
 }
 
@@ -345,11 +321,9 @@ void plan_kv_groups(const hdt_engine *e, int64_t L, int32_t n, const int8_t *dep
 // One attention layer with bf16 storage, for group gr of every tree that has one:
 // the split pass over the committed rows, then the tree pass (tree tiles, fold,
 // output, pending rows).
-template <typename AfterSplit>
 hdt_status launch_kv_group(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
                            const int8_t (*par)[kMaxNodes], const int8_t (*dep)[kMaxNodes],
-                           const KvGroups *groups, int gr, int l, int ki, hipStream_t stream,
-                           AfterSplit *after_split, int ev_index) {
+                           const KvGroups *groups, int gr, int l, int ki, hipStream_t stream) {
   const hdt_model_desc &m = e->desc;
   const int G = m.attn_hq / m.attn_hkv;
   KvLaunch a;
@@ -405,26 +379,19 @@ hdt_status launch_kv_group(hdt_engine *e, int32_t n_trees, const hdt_tree *trees
                               "attention split launch");
     if (st != HDT_OK) return st;
   }
-  if (after_split && gr == 0) {
-    hdt_status st = (*after_split)(ev_index);
-    if (st != HDT_OK) return st;
-  }
   ProfScope p(e, 2);
   return check_hip(e, launch_kv_tree(a, m.attn_d, items_b, stream, p.events()), "attention tree launch");
 }
 
 // One attention layer with bf16 storage: one launch pair per group of nodes that
 // share a split size (one group, unless a tree's rows straddle a rung).
-template <typename AfterSplit>
 hdt_status launch_kv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
                            const int8_t (*par)[kMaxNodes], const int8_t (*dep)[kMaxNodes],
-                           const KvGroups *groups, int l, int ki, hipStream_t stream,
-                           AfterSplit *after_split, int ev_index) {
+                           const KvGroups *groups, int l, int ki, hipStream_t stream) {
   int max_groups = 0;
   for (int t = 0; t < n_trees; ++t) max_groups = std::max(max_groups, groups[t].count);
   for (int gr = 0; gr < max_groups; ++gr) {
-    hdt_status st = launch_kv_group(e, n_trees, trees, par, dep, groups, gr, l, ki, stream, after_split,
-                                    ev_index);
+    hdt_status st = launch_kv_group(e, n_trees, trees, par, dep, groups, gr, l, ki, stream);
     if (st != HDT_OK) return st;
   }
   return HDT_OK;
@@ -470,36 +437,6 @@ hdt_status launch_conv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *tre
   return check_hip(e, launch_gdn_conv(c, m.io_dtype == HDT_BF16, stream, p.events()), "GDN conv launch");
 }
 
-// Read-ahead of attention layer ki's committed K/V for every tree, on the engine's
-// read-ahead stream (group 0's split size; a second group reads the same rows).
-hdt_status launch_prefetch(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, const KvGroups *groups,
-                           int ki) {
-  const hdt_model_desc &m = e->desc;
-  PrefetchLaunch a;
-  std::memset(&a, 0, sizeof a);
-  a.hkv = m.attn_hkv;
-  a.row_bytes = m.attn_d * 2;
-  a.mode = e->pf_mode;
-  a.frac = e->pf_frac;
-  a.sink = e->pf_sink;
-  int32_t items = 0;
-  for (int t = 0; t < n_trees; ++t) {
-    const SlotState &s = e->slots[trees[t].slot];
-    PrefetchTree &x = a.t[a.n_trees++];
-    const size_t view = static_cast<size_t>(m.attn_hkv) * s.d.capacity * m.attn_d * 2;
-    x.kc = static_cast<const char *>(s.d.k_cache) + static_cast<size_t>(ki) * view;
-    x.vc = static_cast<const char *>(s.d.v_cache) + static_cast<size_t>(ki) * view;
-    x.cap = s.d.capacity;
-    x.tb0 = s.d.length / kKvTile * kKvTile;
-    x.split = groups[t].split[0];
-    x.n_splits = static_cast<int32_t>((x.tb0 + x.split - 1) / x.split);
-    x.item_begin = items;
-    items += 2 * m.attn_hkv * x.n_splits;
-  }
-  if (items == 0) return HDT_OK;
-  return check_hip(e, launch_kv_prefetch(a, items, e->pf_stream), "read-ahead launch");
-}
-
 // chain_commit: every tree is a chain that will be committed whole (a prefill span):
 // the GDN walk writes each layer's final state straight to the committed state.
 hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, const int8_t (*par)[kMaxNodes],
@@ -514,21 +451,6 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
   if (bf && e->n_attn > 0)
     for (int t = 0; t < n_trees; ++t)
       plan_kv_groups(e, e->slots[trees[t].slot].d.length, trees[t].n_nodes, dep[t], groups[t]);
-  // read-ahead: the first attention layer's rows from the start of the pass; each later
-  // one's once the split pass before it has been enqueued
-  const bool pf = bf && e->pf_stream && e->n_attn > 0 && !chain_commit;
-  int pf_next = 0;  // attention layer (by kind index) read ahead next
-  auto pf_issue = [&](int ev_index) -> hdt_status {
-    if (!pf || pf_next >= e->n_attn) return HDT_OK;
-    if (hipEventRecord(e->pf_ev[ev_index], stream) != hipSuccess ||
-        hipStreamWaitEvent(e->pf_stream, e->pf_ev[ev_index], 0) != hipSuccess)
-      return fail(e, HDT_E_HIP, "read-ahead fork failed");
-    return launch_prefetch(e, n_trees, trees, groups, pf_next++);
-  };
-  {
-    hdt_status st = pf_issue(0);
-    if (st != HDT_OK) return st;
-  }
 
   for (int l = 0; l < m.n_layers; ++l) {
     const int ki = e->kind_index[l];
@@ -590,8 +512,7 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
           check_hip(e, launch_gdn_tree(a, m.gdn_dk, bf, stream, p.events()), "GDN tree launch");
       if (st != HDT_OK) return st;
     } else if (bf) {
-      hdt_status st = launch_kv_layer(e, n_trees, trees, par, dep, groups, l, ki, stream, pf ? &pf_issue : nullptr,
-                                      ki + 1);
+      hdt_status st = launch_kv_layer(e, n_trees, trees, par, dep, groups, l, ki, stream);
       if (st != HDT_OK) return st;
     } else {
       AttnLaunch a;
@@ -662,11 +583,6 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
         if (st != HDT_OK) return st;
       }
     }
-  }
-  if (pf) {  // join: the caller's stream waits for the last read-ahead
-    const size_t j = e->pf_ev.size() - 1;
-    if (hipEventRecord(e->pf_ev[j], e->pf_stream) != hipSuccess || hipStreamWaitEvent(stream, e->pf_ev[j], 0) != hipSuccess)
-      return fail(e, HDT_E_HIP, "read-ahead join failed");
   }
   return HDT_OK;
 }
@@ -849,8 +765,6 @@ hdt_status hdt_create(const hdt_model_desc *desc, int32_t n_slots, const hdt_slo
   if (e->desc.attn_scale <= 0.0f && n_attn > 0) e->desc.attn_scale = 1.0f / std::sqrt(float(m.attn_d));
   e->n_gdn = n_gdn;
   e->n_attn = n_attn;
-  if (const char *f = std::getenv("HDT_PF_FRAC")) e->pf_frac = static_cast<float>(std::atof(f));
-  if (const char *f = std::getenv("HDT_PF_MODE")) e->pf_mode = std::atoi(f);
   e->esz = m.io_dtype == HDT_BF16 ? 2 : 4;
   if (n_gdn == 0) e->desc.gdn_conv = 0;
   e->conv_C = n_gdn > 0 ? 2 * m.gdn_hk * m.gdn_dk + m.gdn_hv * m.gdn_dv : 0;

@@ -549,8 +549,13 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
   if (wave == 0) {
     // ---- ancestors first (scalar walk over the parent array held in a VGPR):
     // lane d holds the node's ancestor at depth d
+    // the parent array as uniform words (scalar loads from the launch block), spread
+    // over the lanes: lane i holds parent[i]
+    const uint32_t *pw = reinterpret_cast<const uint32_t *>(T.parent);
     const int pl = min(lane, T.n - 1);
-    const uint32_t par_w = reinterpret_cast<const uint32_t *>(T.parent)[pl >> 2];
+    uint32_t par_w = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxNodes / 4; ++i) par_w = (pl >> 2) == i ? pw[i] : par_w;
     const int par_v = static_cast<int8_t>((par_w >> (8 * (pl & 3))) & 0xFFu);
     int anc_v = node;
     {
@@ -805,53 +810,7 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
   }
 }
 
-// ============================================================================ read-ahead
-
-// Tile t of a split of nt tiles is read when it is among the share `frac` chosen by `mode`.
-__device__ __forceinline__ bool prefetch_tile(int t, int nt, float frac, int mode) {
-  const int k = static_cast<int>(frac * nt);
-  if (mode == 0) return t < k;
-  if (mode == 2) return t >= nt - k;
-  return static_cast<int>((t + 1) * frac) > static_cast<int>(t * frac);
-}
-
-__global__ __launch_bounds__(256) void kv_prefetch_kernel(const PrefetchLaunch P) {
-  int b = blockIdx.x, ti = 0;
-  while (ti + 1 < P.n_trees && b >= P.t[ti + 1].item_begin) ++ti;
-  const PrefetchTree &T = P.t[ti];
-  b -= T.item_begin;
-  const int which = b & 1, pair = b >> 1;
-  const int h = pair / T.n_splits, s = pair % T.n_splits;
-  if (h >= P.hkv) return;
-  const int64_t r0 = static_cast<int64_t>(s) * T.split;
-  const int64_t r1 = min(r0 + T.split, T.tb0);
-  const int nt = static_cast<int>((r1 - r0 + kKvTile - 1) / kKvTile);
-  const uint4 *base = reinterpret_cast<const uint4 *>(static_cast<const unsigned char *>(which ? T.vc : T.kc) +
-                                                      (static_cast<int64_t>(h) * T.cap + r0) * P.row_bytes);
-  const int per_tile = kKvTile * P.row_bytes / 16;  // 16-byte chunks of one tile's K (or V) rows
-  uint32_t x = 0;
-  for (int t = 0; t < nt; t += 2) {
-    uint4 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int tt = t + u / 4;
-      const int c = (u % 4) * 256 + static_cast<int>(threadIdx.x);
-      const bool take = tt < nt && c < per_tile && prefetch_tile(tt, nt, P.frac, P.mode) &&
-                        r0 + static_cast<int64_t>(tt) * kKvTile + c / (P.row_bytes / 16) < r1;
-      v[u] = take ? base[static_cast<int64_t>(tt) * per_tile + c] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) x ^= v[u].x ^ v[u].w;
-  }
-  if (x == 0x9E3779B9u) P.sink[0] = x;
-}
-
 }  // namespace
-
-hipError_t launch_kv_prefetch(const PrefetchLaunch &a, int n_blocks, hipStream_t s) {
-  hipLaunchKernelGGL(kv_prefetch_kernel, dim3(n_blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
 
 hipError_t launch_kv_split(const KvLaunch &a, int D, int max_items, hipStream_t s, KernelEvents ev) {
   const dim3 grid(max_items, a.n_trees);

@@ -167,31 +167,6 @@ struct KvLaunch {
   float c2;                               // softmax scale times log2(e)
 };
 
-// ---------------------------------------------------------------- committed K/V read-ahead
-// Reads part of every split of one attention layer's committed K/V rows and discards it,
-// while the Gated DeltaNet layers before that attention layer keep the HBM idle, so that
-// the split pass finds those lines in the memory-side cache.  Only committed rows (below
-// the split pass's last tile boundary) are read; nothing is written.  One workgroup per
-// (tree, kv head, split, K or V).
-struct PrefetchTree {
-  const void *kc, *vc;                    // the layer's cache [hkv][cap][D]
-  int64_t cap;
-  int64_t tb0;                            // rows below this are read by the split pass
-  int32_t split;                          // keys per split
-  int32_t n_splits;                       // splits with rows below tb0
-  int32_t item_begin;                     // first workgroup of this tree
-};
-
-struct PrefetchLaunch {
-  PrefetchTree t[kMaxTrees];
-  int32_t n_trees;
-  int32_t hkv, row_bytes;
-  int32_t mode;                           // 0: leading tiles of a split, 1: spread, 2: trailing
-  float frac;                             // share of each split's tiles read
-  uint32_t *sink;                         // a word written only if the discarded data hashes
-                                          // to a fixed value (keeps the loads)
-};
-
 // ---------------------------------------------------------------- attention fold
 struct FoldTree {
   const float *part_acc, *part_ml;
@@ -271,7 +246,6 @@ hipError_t launch_attn_fold(const FoldLaunch &a, int D, int bf16, int n_blocks, 
 hipError_t launch_kv_split(const KvLaunch &a, int D, int max_items, hipStream_t s,
                            KernelEvents ev);
 hipError_t launch_kv_tree(const KvLaunch &a, int D, int max_items, hipStream_t s, KernelEvents ev);
-hipError_t launch_kv_prefetch(const PrefetchLaunch &a, int n_blocks, hipStream_t s);
 hipError_t launch_commit(const CommitLaunch &a, int dk, int bf16, int n_blocks, hipStream_t s,
                          KernelEvents ev);
 hipError_t launch_gdn_conv(const ConvLaunch &a, int bf16, hipStream_t s, KernelEvents ev);
