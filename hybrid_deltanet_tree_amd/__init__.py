@@ -73,6 +73,7 @@ _sigs = {
                         ctypes.POINTER(hdt_slot_desc), ctypes.POINTER(_E)]),
     "hdt_destroy": (None, [_E]),
     "hdt_forward_tree": (_S, [_E, ctypes.c_int32, ctypes.POINTER(hdt_tree), ctypes.c_void_p]),
+    "hdt_forward_tree_noalloc": (_S, [_E, ctypes.c_int32, ctypes.POINTER(hdt_tree), ctypes.c_void_p]),
     "hdt_forward_block": (_S, [_E, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(hdt_layer_io),
                                ctypes.c_void_p]),
     "hdt_commit_tree": (_S, [_E, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
@@ -192,8 +193,7 @@ class Engine:
                                   _ptr(io.get("alpha")), _ptr(io.get("beta")), _ptr(io.get("o")))
         return arr
 
-    def forward_tree(self, trees, stream=0):
-        """trees: list of (slot, parent list, per-layer list of dicts q/k/v/alpha/beta/o)."""
+    def _trees(self, trees):
         arr = (hdt_tree * len(trees))()
         keep = []
         for i, (slot, parent, layers) in enumerate(trees):
@@ -201,7 +201,17 @@ class Engine:
             io = self._io_array(layers)
             keep += [par, io]
             arr[i] = hdt_tree(slot, len(parent), par, io)
+        return arr, keep
+
+    def forward_tree(self, trees, stream=0):
+        """trees: list of (slot, parent list, per-layer list of dicts q/k/v/alpha/beta/o)."""
+        arr, keep = self._trees(trees)
         self._check(hdt_forward_tree(self.h, len(trees), arr, stream))
+
+    def forward_tree_noalloc(self, trees, stream=0):
+        """forward_tree with the library's static scratch: allocates nothing."""
+        arr, keep = self._trees(trees)
+        self._check(hdt_forward_tree_noalloc(self.h, len(trees), arr, stream))
 
     def forward_block(self, slot, n, layers, stream=0):
         self._check(hdt_forward_block(self.h, slot, n, self._io_array(layers), stream))

@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -30,13 +31,13 @@ constexpr int64_t kSplitMax = 16384;
 constexpr float kConvEps = 1e-6f;      // GDN conv: epsilon of the q/k L2 norm, y / sqrt(sum y^2 + eps)
 constexpr int64_t kKvSplitMin = 128;  // bf16 attention: smallest split (> kKvTile - 1 + kMaxNodes - 1)
 
-struct SlotState {
-  hdt_slot_desc d{};
-  int32_t split = 0;          // float32 attention: keys per split (bf16 splits follow each row's position)
-  int32_t nsplit_cap = 0;
-  float *u_pend = nullptr;
-  void *k_pend = nullptr;
-  void *a_pend = nullptr;
+// The scratch of one slot's round: what commit needs of the pass, the attention
+// partials and the conv staging.  Nothing in it has to start at zero: every value is
+// written by the pass before anything reads it.
+struct Scratch {
+  float *u_pend = nullptr;    // [n_gdn][max_nodes][hv][dv] delta-rule corrections
+  void *k_pend = nullptr;     // [n_gdn][max_nodes][hk][dk] copies of k (io dtype)
+  void *a_pend = nullptr;     // [n_gdn][max_nodes][hv] copies of alpha (io dtype)
   float *part_acc = nullptr;  // float32 attention: partials [hkv][nsplit][rows][D]
   float *part_ml = nullptr;   // [hkv][nsplit][rows][2]
   void *part_o = nullptr;     // bf16 attention: normalised fp16 partials [hkv][nsplit][rows][D]
@@ -44,6 +45,18 @@ struct SlotState {
   float *carry_ml = nullptr;  // [hkv][rows][2]
   void *conv_out = nullptr;   // GDN conv: post-conv q | k | v of one layer [max_nodes][..] each
   void *x_pend = nullptr;     // GDN conv: pre-conv rows of the tree [n_gdn][max_nodes][C]
+};
+constexpr int kScratchParts = 10;
+
+struct SlotState {
+  hdt_slot_desc d{};
+  int32_t split = 0;          // float32 attention: keys per split (bf16 splits follow each row's position)
+  int32_t nsplit_cap = 0;
+  Scratch own;                // allocated by the engine at its first launching call
+  Scratch sc;                 // the scratch of the pending round (own, or carved from the
+                              // library's static array by hdt_forward_tree_noalloc)
+  int32_t static_dev = -1;    // sc is the static array of this device ...
+  uint64_t static_gen = 0;    // ... as handed out by this call (a later call reuses it)
   bool pending = false;
   bool walk_pending = false;  // an accept walk's commit is in flight: length not yet known
   int64_t anchor_every = 0;   // state anchors: anchor k holds position (k + 1) * every
@@ -76,6 +89,7 @@ struct hdt_engine {
   bool allocated = false;
   int max_lds = 0;  // dynamic LDS a workgroup may use on the device
   bool profiling = false;
+  bool no_events = false;  // the launch in progress may create no events (hdt_forward_tree_noalloc)
   std::vector<EventPair> ev_live;
   std::vector<EventPair> ev_pool;
   int32_t conv_C = 0;  // channels through the GDN conv: 2 hk dk + hv dv
@@ -186,69 +200,106 @@ hdt_status check_hip(hdt_engine *e, hipError_t r, const char *what) {
   return HDT_OK;
 }
 
-hdt_status ensure_alloc(hdt_engine *e) {
-  if (e->allocated) return HDT_OK;
+// Bytes of each part of one slot's scratch, in the order of the Scratch fields.
+void scratch_sizes(const hdt_engine *e, const SlotState &s, size_t (&b)[kScratchParts]) {
   const hdt_model_desc &m = e->desc;
+  for (auto &x : b) x = 0;
+  const size_t nm = static_cast<size_t>(m.max_nodes);
+  if (e->n_gdn > 0) {
+    const size_t ng = static_cast<size_t>(e->n_gdn);
+    b[0] = ng * nm * m.gdn_hv * m.gdn_dv * sizeof(float);
+    b[1] = ng * nm * m.gdn_hk * m.gdn_dk * e->esz;
+    b[2] = ng * nm * m.gdn_hv * e->esz;
+    if (m.gdn_conv > 0) {
+      b[8] = nm * e->conv_C * e->esz;
+      b[9] = ng * nm * e->conv_C * e->esz;
+    }
+  }
+  if (e->n_attn > 0) {
+    const size_t G = static_cast<size_t>(m.attn_hq / m.attn_hkv);
+    const size_t rows = nm * G;
+    const size_t base = static_cast<size_t>(m.attn_hkv) * s.nsplit_cap * rows;
+    const size_t carry = static_cast<size_t>(m.attn_hkv) * rows;
+    b[4] = base * 2 * sizeof(float);
+    if (m.io_dtype == HDT_BF16) {
+      b[5] = base * m.attn_d * 2;
+      b[6] = carry * m.attn_d * sizeof(float);
+      b[7] = carry * 2 * sizeof(float);
+    } else {
+      b[3] = base * m.attn_d * sizeof(float);
+    }
+  }
+}
+
+void **scratch_part(Scratch &x, int i) {
+  void **p[kScratchParts] = {reinterpret_cast<void **>(&x.u_pend), &x.k_pend, &x.a_pend,
+                             reinterpret_cast<void **>(&x.part_acc), reinterpret_cast<void **>(&x.part_ml),
+                             &x.part_o, reinterpret_cast<void **>(&x.carry_acc),
+                             reinterpret_cast<void **>(&x.carry_ml), &x.conv_out, &x.x_pend};
+  return p[i];
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Bytes of one slot's scratch carved from one block, each part 256-byte aligned.
+size_t scratch_bytes(const hdt_engine *e, const SlotState &s) {
+  size_t b[kScratchParts], total = 0;
+  scratch_sizes(e, s, b);
+  for (size_t x : b) total += align256(x);
+  return total;
+}
+
+// The device's LDS limit per workgroup (an attribute query; nothing is allocated).
+hdt_status query_lds(hdt_engine *e) {
+  if (e->max_lds > 0) return HDT_OK;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&e->max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
     return fail(e, HDT_E_HIP, "cannot query the current HIP device");
-  const int G = m.attn_hkv > 0 ? m.attn_hq / m.attn_hkv : 0;
-  for (auto &s : e->slots) {
-    const size_t nm = static_cast<size_t>(m.max_nodes);
-    if (e->n_gdn > 0) {
-      const size_t ng = static_cast<size_t>(e->n_gdn);
-      if (hipMalloc(&s.u_pend, ng * nm * m.gdn_hv * m.gdn_dv * sizeof(float)) != hipSuccess ||
-          hipMalloc(&s.k_pend, ng * nm * m.gdn_hk * m.gdn_dk * e->esz) != hipSuccess ||
-          hipMalloc(&s.a_pend, ng * nm * m.gdn_hv * e->esz) != hipSuccess)
-        return fail(e, HDT_E_HIP, "hipMalloc of the pending GDN buffers failed");
-      if (m.gdn_conv > 0 &&
-          (hipMalloc(&s.conv_out, nm * e->conv_C * e->esz) != hipSuccess ||
-           hipMalloc(&s.x_pend, static_cast<size_t>(e->n_gdn) * nm * e->conv_C * e->esz) != hipSuccess))
-        return fail(e, HDT_E_HIP, "hipMalloc of the conv buffers failed");
-    }
-    if (e->n_attn > 0) {
-      const size_t rows = nm * G;
-      const size_t base = static_cast<size_t>(m.attn_hkv) * s.nsplit_cap * rows;
-      const size_t carry = static_cast<size_t>(m.attn_hkv) * rows;
-      if (m.io_dtype == HDT_BF16) {
-        if (hipMalloc(&s.part_o, base * m.attn_d * 2) != hipSuccess ||
-            hipMalloc(&s.part_ml, base * 2 * sizeof(float)) != hipSuccess ||
-            hipMalloc(&s.carry_acc, carry * m.attn_d * sizeof(float)) != hipSuccess ||
-            hipMalloc(&s.carry_ml, carry * 2 * sizeof(float)) != hipSuccess)
-          return fail(e, HDT_E_HIP, "hipMalloc of the attention partials failed");
-      } else if (hipMalloc(&s.part_acc, base * m.attn_d * sizeof(float)) != hipSuccess ||
-                 hipMalloc(&s.part_ml, base * 2 * sizeof(float)) != hipSuccess) {
-        return fail(e, HDT_E_HIP, "hipMalloc of the attention partials failed");
-      }
-    }
-  }
-  if (hipHostMalloc(reinterpret_cast<void **>(&e->walk_m), e->slots.size() * sizeof(int32_t)) != hipSuccess)
+  return HDT_OK;
+}
+
+// The pinned word and the event of each slot that hdt_walk_commit uses.
+hdt_status ensure_walk(hdt_engine *e) {
+  if (e->walk_m) return HDT_OK;
+  if (hipHostMalloc(reinterpret_cast<void **>(&e->walk_m), e->slots.size() * sizeof(int32_t)) != hipSuccess) {
+    e->walk_m = nullptr;
     return fail(e, HDT_E_HIP, "hipHostMalloc of the walk results failed");
+  }
   for (auto &s : e->slots)
     if (hipEventCreateWithFlags(&s.walk_ev, hipEventDisableTiming) != hipSuccess)
       return fail(e, HDT_E_HIP, "hipEventCreate failed");
+  return HDT_OK;
+}
+
+// The engine's own scratch, allocated at the first call that launches with it.
+hdt_status ensure_alloc(hdt_engine *e) {
+  if (e->allocated) return HDT_OK;
+  hdt_status st = query_lds(e);
+  if (st != HDT_OK) return st;
+  for (auto &s : e->slots) {
+    size_t b[kScratchParts];
+    scratch_sizes(e, s, b);
+    for (int i = 0; i < kScratchParts; ++i)
+      if (b[i] > 0 && hipMalloc(scratch_part(s.own, i), b[i]) != hipSuccess)
+        return fail(e, HDT_E_HIP, "hipMalloc of the slot scratch failed");
+  }
+  st = ensure_walk(e);
+  if (st != HDT_OK) return st;
   e->allocated = true;
   return HDT_OK;
 }
 
 void free_scratch(hdt_engine *e) {
   for (auto &s : e->slots) {
-    (void)hipFree(s.u_pend);
-    (void)hipFree(s.k_pend);
-    (void)hipFree(s.a_pend);
-    (void)hipFree(s.part_acc);
-    (void)hipFree(s.part_ml);
-    (void)hipFree(s.part_o);
-    (void)hipFree(s.carry_acc);
-    (void)hipFree(s.carry_ml);
-    (void)hipFree(s.conv_out);
-    (void)hipFree(s.x_pend);
+    for (int i = 0; i < kScratchParts; ++i) {
+      void **p = scratch_part(s.own, i);
+      (void)hipFree(*p);
+      *p = nullptr;
+    }
+    s.sc = Scratch{};
     if (s.walk_ev) (void)hipEventDestroy(s.walk_ev);
     s.walk_ev = nullptr;
-    s.u_pend = nullptr;
-    s.k_pend = s.a_pend = s.part_o = s.conv_out = s.x_pend = nullptr;
-    s.part_acc = s.part_ml = s.carry_acc = s.carry_ml = nullptr;
   }
   if (e->walk_m) (void)hipHostFree(e->walk_m);
   e->walk_m = nullptr;
@@ -262,7 +313,7 @@ struct ProfScope {
   EventPair ev{};
   bool on = false;
   ProfScope(hdt_engine *e_, int k) : e(e_) {
-    if (!e->profiling) return;
+    if (!e->profiling || e->no_events) return;
     if (!e->ev_pool.empty()) {
       ev = e->ev_pool.back();
       e->ev_pool.pop_back();
@@ -352,10 +403,10 @@ hdt_status launch_kv_group(hdt_engine *e, int32_t n_trees, const hdt_tree *trees
     x.kc = static_cast<char *>(s.d.k_cache) + static_cast<size_t>(ki) * view;
     x.vc = static_cast<char *>(s.d.v_cache) + static_cast<size_t>(ki) * view;
     x.o = io.o;
-    x.part_o = s.part_o;
-    x.part_ml = s.part_ml;
-    x.carry_acc = s.carry_acc;
-    x.carry_ml = s.carry_ml;
+    x.part_o = s.sc.part_o;
+    x.part_ml = s.sc.part_ml;
+    x.carry_acc = s.sc.carry_acc;
+    x.carry_ml = s.sc.carry_ml;
     x.L = s.d.length;
     x.cap = s.d.capacity;
     x.n = tr.n_nodes;
@@ -425,10 +476,10 @@ hdt_status launch_conv_layer(hdt_engine *e, int32_t n_trees, const hdt_tree *tre
     x.k = io.k;
     x.v = io.v;
     x.tail = static_cast<const char *>(s.d.gdn_conv_state) + static_cast<size_t>(ki) * (m.gdn_conv - 1) * row;
-    x.qo = s.conv_out;
-    x.ko = static_cast<char *>(s.conv_out) + cq;
-    x.vo = static_cast<char *>(s.conv_out) + 2 * cq;
-    x.x_pend = static_cast<char *>(s.x_pend) + static_cast<size_t>(ki) * nm * row;
+    x.qo = s.sc.conv_out;
+    x.ko = static_cast<char *>(s.sc.conv_out) + cq;
+    x.vo = static_cast<char *>(s.sc.conv_out) + 2 * cq;
+    x.x_pend = static_cast<char *>(s.sc.x_pend) + static_cast<size_t>(ki) * nm * row;
     x.n = tr.n_nodes;
     std::memcpy(x.parent, par[t], kMaxNodes);
     std::memcpy(x.depth, dep[t], kMaxNodes);
@@ -474,9 +525,9 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
         GdnTree &g = a.t[t];
         if (m.gdn_conv > 0) {  // the walk reads the conv output of this layer
           const size_t cq = static_cast<size_t>(m.max_nodes) * m.gdn_hk * m.gdn_dk * e->esz;
-          g.q = s.conv_out;
-          g.k = static_cast<char *>(s.conv_out) + cq;
-          g.v = static_cast<char *>(s.conv_out) + 2 * cq;
+          g.q = s.sc.conv_out;
+          g.k = static_cast<char *>(s.sc.conv_out) + cq;
+          g.v = static_cast<char *>(s.sc.conv_out) + 2 * cq;
         } else {
           g.q = io.q;
           g.k = io.k;
@@ -489,10 +540,10 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
         g.state = s.d.gdn_state + static_cast<size_t>(ki) * hs;
         g.commit_state = chain_commit ? s.d.gdn_state + static_cast<size_t>(ki) * hs : nullptr;
         const size_t nm = static_cast<size_t>(m.max_nodes);
-        g.u_pend = s.u_pend + static_cast<size_t>(ki) * nm * m.gdn_hv * m.gdn_dv;
-        g.k_pend = static_cast<char *>(s.k_pend) +
+        g.u_pend = s.sc.u_pend + static_cast<size_t>(ki) * nm * m.gdn_hv * m.gdn_dv;
+        g.k_pend = static_cast<char *>(s.sc.k_pend) +
                    static_cast<size_t>(ki) * nm * m.gdn_hk * m.gdn_dk * e->esz;
-        g.a_pend = static_cast<char *>(s.a_pend) + static_cast<size_t>(ki) * nm * m.gdn_hv * e->esz;
+        g.a_pend = static_cast<char *>(s.sc.a_pend) + static_cast<size_t>(ki) * nm * m.gdn_hv * e->esz;
         g.n = tr.n_nodes;
         std::memcpy(g.parent, par[t], kMaxNodes);
         std::memcpy(g.depth, dep[t], kMaxNodes);
@@ -539,8 +590,8 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
         x.vt = io.v;
         x.kc = static_cast<char *>(s.d.k_cache) + static_cast<size_t>(ki) * view;
         x.vc = static_cast<char *>(s.d.v_cache) + static_cast<size_t>(ki) * view;
-        x.part_acc = s.part_acc;
-        x.part_ml = s.part_ml;
+        x.part_acc = s.sc.part_acc;
+        x.part_ml = s.sc.part_ml;
         x.L = s.d.length;
         x.cap = s.d.capacity;
         x.n = tr.n_nodes;
@@ -558,8 +609,8 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
         items += x.n_tail_items + m.attn_hkv * x.n_shared * x.row_groups;
 
         FoldTree &y = f.t[t];
-        y.part_acc = s.part_acc;
-        y.part_ml = s.part_ml;
+        y.part_acc = s.sc.part_acc;
+        y.part_ml = s.sc.part_ml;
         y.o = io.o;
         y.L = s.d.length;
         y.n = tr.n_nodes;
@@ -599,9 +650,9 @@ hdt_status do_commit(hdt_engine *e, int32_t slot, const int32_t *path, int32_t m
   CommitLaunch c;
   std::memset(&c, 0, sizeof c);
   c.state = s.d.gdn_state;
-  c.u_pend = s.u_pend;
-  c.k_pend = s.k_pend;
-  c.a_pend = s.a_pend;
+  c.u_pend = s.sc.u_pend;
+  c.k_pend = s.sc.k_pend;
+  c.a_pend = s.sc.a_pend;
   c.kc = s.d.k_cache;
   c.vc = s.d.v_cache;
   c.L = s.d.length;
@@ -619,7 +670,7 @@ hdt_status do_commit(hdt_engine *e, int32_t slot, const int32_t *path, int32_t m
   int conv_blocks = 0;
   if (e->n_gdn > 0 && m.gdn_conv > 1) {
     c.conv_state = s.d.gdn_conv_state;
-    c.x_pend = s.x_pend;
+    c.x_pend = s.sc.x_pend;
     c.conv_width = m.gdn_conv;
     c.conv_C = e->conv_C;
     const int64_t chunks = static_cast<int64_t>(e->conv_C) * e->esz / 16;
@@ -694,6 +745,22 @@ int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 int64_t snapshot_bytes(const hdt_engine *e) {
   return kSnapshotHeaderBytes + round256(static_cast<int64_t>(gdn_state_bytes(e))) +
          static_cast<int64_t>(conv_tail_bytes(e));
+}
+
+// hdt_forward_tree_noalloc hands out the library's static scratch array of a device to
+// one call at a time; each call takes the next generation, and a pending round whose
+// generation is no longer the latest has had its scratch reused.
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+uint64_t g_static_gen[kMaxDevices] = {};
+
+hdt_status check_round_scratch(hdt_engine *e, const SlotState &s) {
+  if (s.static_gen == 0) return HDT_OK;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (g_static_gen[s.static_dev] != s.static_gen)
+    return fail(e, HDT_E_ORDER, "the pending round's static scratch was reused by a later "
+                "hdt_forward_tree_noalloc call on this device");
+  return HDT_OK;
 }
 
 // After an accept walk, the slot's new length is known once the device has run the
@@ -807,7 +874,13 @@ void hdt_destroy(hdt_engine *e) {
   delete e;
 }
 
-hdt_status hdt_forward_tree(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// forward_tree with the engine's own scratch (allocated at the first call), or with
+// `noalloc` the scratch carved from the library's static array of the current device.
+hdt_status forward_trees(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, void *stream, bool noalloc) {
   if (!e) return HDT_E_INVALID;
   if (n_trees < 1 || n_trees > HDT_MAX_TREES || !trees)
     return fail(e, HDT_E_INVALID, "n_trees must be 1..%d", HDT_MAX_TREES);
@@ -848,15 +921,50 @@ hdt_status hdt_forward_tree(hdt_engine *e, int32_t n_trees, const hdt_tree *tree
                     t, l);
     }
   }
-  if (!e->allocated) {
-    // the scratch is allocated by the first forward, which must not be captured
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) != hipSuccess ||
-        cs != hipStreamCaptureStatusNone)
-      return fail(e, HDT_E_ORDER, "the first forward allocates scratch: run it outside graph capture");
+  hdt_status st = HDT_OK;
+  Scratch carved[HDT_MAX_TREES];
+  int dev = 0;
+  uint64_t gen = 0;
+  if (noalloc) {
+    size_t need = 0;
+    for (int t = 0; t < n_trees; ++t) need += scratch_bytes(e, e->slots[trees[t].slot]);
+    if (need > kStaticScratchBytes)
+      return fail(e, HDT_E_CAPACITY, "the pass needs %zu bytes of scratch; the static scratch holds %zu",
+                  need, static_cast<size_t>(kStaticScratchBytes));
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+      return fail(e, HDT_E_HIP, "no current HIP device");
+    void *base = nullptr;
+    if (check_hip(e, static_scratch_address(&base), "resolving the static scratch") != HDT_OK) return HDT_E_HIP;
+    st = query_lds(e);
+    if (st != HDT_OK) return st;
+    size_t off = 0;
+    for (int t = 0; t < n_trees; ++t) {
+      size_t b[kScratchParts];
+      scratch_sizes(e, e->slots[trees[t].slot], b);
+      for (int i = 0; i < kScratchParts; ++i) {
+        *scratch_part(carved[t], i) = b[i] > 0 ? static_cast<char *>(base) + off : nullptr;
+        off += align256(b[i]);
+      }
+    }
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    gen = ++g_static_gen[dev];
+  } else {
+    if (!e->allocated) {
+      // the scratch is allocated by the first forward, which must not be captured
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) != hipSuccess ||
+          cs != hipStreamCaptureStatusNone)
+        return fail(e, HDT_E_ORDER, "the first forward allocates scratch: run it outside graph capture");
+    }
+    st = ensure_alloc(e);
+    if (st != HDT_OK) return st;
   }
-  hdt_status st = ensure_alloc(e);
-  if (st != HDT_OK) return st;
+  for (int t = 0; t < n_trees; ++t) {
+    SlotState &s = e->slots[trees[t].slot];
+    s.sc = noalloc ? carved[t] : s.own;
+    s.static_dev = noalloc ? dev : -1;
+    s.static_gen = gen;
+  }
   {
     int32_t n_max = 0;
     for (int t = 0; t < n_trees; ++t) n_max = std::max(n_max, trees[t].n_nodes);
@@ -866,7 +974,9 @@ hdt_status hdt_forward_tree(hdt_engine *e, int32_t n_trees, const hdt_tree *tree
       return fail(e, HDT_E_UNSUPPORTED, "kernels need %zu / %zu bytes of LDS; the device allows %d",
                   need_g, need_a, e->max_lds);
   }
+  e->no_events = noalloc;  // a noalloc call creates no profiling events either
   st = launch_forward(e, n_trees, trees, par, dep, static_cast<hipStream_t>(stream));
+  e->no_events = false;
   if (st != HDT_OK) return st;
   for (int t = 0; t < n_trees; ++t) {
     SlotState &s = e->slots[trees[t].slot];
@@ -878,6 +988,18 @@ hdt_status hdt_forward_tree(hdt_engine *e, int32_t n_trees, const hdt_tree *tree
   }
   e->err.clear();
   return HDT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hdt_status hdt_forward_tree(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, void *stream) {
+  return forward_trees(e, n_trees, trees, stream, false);
+}
+
+hdt_status hdt_forward_tree_noalloc(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, void *stream) {
+  return forward_trees(e, n_trees, trees, stream, true);
 }
 
 hdt_status hdt_forward_block(hdt_engine *e, int32_t slot, int32_t n, const hdt_layer_io *io,
@@ -898,6 +1020,7 @@ hdt_status hdt_commit_tree(hdt_engine *e, int32_t slot, const int32_t *path, int
   if (settle(e, slot) != HDT_OK) return HDT_E_HIP;
   SlotState &s = e->slots[slot];
   if (!s.pending) return fail(e, HDT_E_ORDER, "slot %d has no pending round", slot);
+  if (check_round_scratch(e, s) != HDT_OK) return HDT_E_ORDER;
   if (!path || m < 1 || m > s.n) return fail(e, HDT_E_PATH, "path length %d (tree of %d)", m, s.n);
   if (path[0] != 0) return fail(e, HDT_E_PATH, "path must start at the root");
   for (int d = 1; d < m; ++d)
@@ -942,6 +1065,7 @@ hdt_status hdt_rollback_to(hdt_engine *e, int32_t slot, int64_t n, void *stream)
   if (n > L + s.chain)
     return fail(e, HDT_E_INVALID, "rollback_to(%lld): only the leading chain of %d can be kept",
                 (long long)n, s.chain);
+  if (check_round_scratch(e, s) != HDT_OK) return HDT_E_ORDER;
   int32_t path[HDT_MAX_NODES];
   const int32_t m = static_cast<int32_t>(n - L);
   for (int d = 0; d < m; ++d) path[d] = d;
@@ -981,6 +1105,9 @@ hdt_status hdt_forward_span(hdt_engine *e, int32_t slot, int32_t T, const hdt_la
   }
   hdt_status r = ensure_alloc(e);
   if (r != HDT_OK) return r;
+  s.sc = s.own;
+  s.static_dev = -1;
+  s.static_gen = 0;
   if (gdn_lds_bytes(m.gdn_dk, m.max_nodes, kGdnSaves) > static_cast<size_t>(e->max_lds) && e->n_gdn > 0)
     return fail(e, HDT_E_UNSUPPORTED, "a chain of %d needs more LDS than the device allows", m.max_nodes);
   // bytes per row of each io array, by layer kind
@@ -1090,8 +1217,10 @@ hdt_status hdt_walk_commit(hdt_engine *e, int32_t slot, const int32_t *draft, co
   if (settle(e, slot) != HDT_OK) return HDT_E_HIP;
   SlotState &s = e->slots[slot];
   if (!s.pending) return fail(e, HDT_E_ORDER, "slot %d has no pending round", slot);
+  if (check_round_scratch(e, s) != HDT_OK) return HDT_E_ORDER;
   if (commit_lds_bytes(e->desc.attn_d, e->desc.io_dtype == HDT_BF16, s.n) > static_cast<size_t>(e->max_lds))
     return fail(e, HDT_E_UNSUPPORTED, "commit of %d rows needs more LDS than the device allows", s.n);
+  if (ensure_walk(e) != HDT_OK) return HDT_E_HIP;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   WalkLaunch w;
   std::memset(&w, 0, sizeof w);

@@ -30,6 +30,8 @@
 //    fold in ascending order.
 #include "common.h"
 
+#include <mutex>
+
 #pragma clang fp contract(off)
 
 namespace hdt {
@@ -1282,6 +1284,31 @@ hipError_t launch_attn_fold(const FoldLaunch &a, int D, int bf16, int n_blocks, 
 hipError_t launch_walk(const WalkLaunch &a, hipStream_t s, KernelEvents ev) {
   hipExtLaunchKernelGGL(walk_kernel, dim3(1), dim3(64), 0, s, ev.start, ev.stop, 0, a);
   return hipGetLastError();
+}
+
+// The scratch of hdt_forward_tree_noalloc: one file-scope device array, one copy on every
+// device the library runs on.  In host code its name is a host-side stand-in, never a
+// device address: only the address hipGetSymbolAddress returns on a device is passed to
+// kernels or copies.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch_address(void **out) {
+  constexpr int kDevices = 64;
+  static std::mutex mu;
+  static void *addr[kDevices] = {};
+  int dev = 0;
+  hipError_t r = hipGetDevice(&dev);
+  if (r != hipSuccess) return r;
+  if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {  // first use on this device, with it current
+    void *p = nullptr;
+    r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (r != hipSuccess) return r;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_snapshot_header(const SnapshotHeader &h, void *dst, hipStream_t s) {

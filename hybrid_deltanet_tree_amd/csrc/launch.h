@@ -251,6 +251,12 @@ hipError_t launch_commit(const CommitLaunch &a, int dk, int bf16, int n_blocks, 
 hipError_t launch_gdn_conv(const ConvLaunch &a, int bf16, hipStream_t s, KernelEvents ev);
 hipError_t launch_walk(const WalkLaunch &a, hipStream_t s, KernelEvents ev);
 hipError_t launch_snapshot_header(const SnapshotHeader &h, void *dst, hipStream_t s);
+
+// The library's static scratch array (hdt_forward_tree_noalloc): kStaticScratchBytes per
+// device, held until the process ends.  static_scratch_address resolves its device
+// address on the current device (once per device) and returns it.
+constexpr size_t kStaticScratchBytes = size_t(48) << 20;
+hipError_t static_scratch_address(void **out);
 // Channels one conv thread handles (16 bytes of io dtype).
 constexpr int conv_channels_per_thread(int bf16) { return bf16 ? 8 : 4; }
 

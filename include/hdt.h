@@ -190,6 +190,28 @@ void hdt_destroy(hdt_engine *eng);
 hdt_status hdt_forward_tree(hdt_engine *eng, int32_t n_trees, const hdt_tree *trees,
                             void *stream);
 
+/*
+ * forward_tree that allocates nothing, for callers that cannot allocate: code under HIP
+ * graph capture from the first call on, serving loops and harnesses that forbid
+ * allocation.  The same pass and the same bits as hdt_forward_tree, but the round's scratch
+ * (what commit needs of the pass, the attention partials, the conv staging) is carved from
+ * a static array of the library, 48 MiB per device (HDT_STATIC_SCRATCH_BYTES), held until
+ * the process ends; it makes no hipMalloc, hipHostMalloc, hipFree or event call.  A call
+ * whose trees need more scratch than that (one slot of a 64-layer model at the 27B-like
+ * shapes with max_nodes up to 32 fits) returns HDT_E_CAPACITY and changes nothing.
+ * Every call on a device shares that device's array and it keeps the last call's
+ * contents (nothing in it needs to start at zero).  A pending round made by this call
+ * is closed by hdt_commit_tree, hdt_rollback_to or hdt_walk_commit as usual, but only
+ * before the next hdt_forward_tree_noalloc call on the same device: after it those refuse
+ * the round with HDT_E_ORDER (its scratch was reused) and hdt_rollback_to(length) drops it.
+ * Calls that overlap in time on one device (other engines, other streams or threads)
+ * race on the array.
+ * Errors: those of hdt_forward_tree, and HDT_E_CAPACITY as above.
+ */
+#define HDT_STATIC_SCRATCH_BYTES (48ll << 20)
+hdt_status hdt_forward_tree_noalloc(hdt_engine *eng, int32_t n_trees, const hdt_tree *trees,
+                                    void *stream);
+
 /* forward_block ("Adding a model", step 4 of "The adapter path in ten steps": the hot
  * verb that verifies a block of drafted tokens): forward_tree of one chain of n nodes
  * (parent[i] = i - 1), 1 <= n <= HDT_MAX_NODES.  Same errors as forward_tree. */

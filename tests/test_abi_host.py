@@ -323,3 +323,21 @@ def test_state_snapshot_size_and_host_refusals():
             assert err.value.status == status
     assert e.kv_length(0) == 100
     e.close()
+
+
+def test_noalloc_forward_refuses_more_than_its_static_scratch():
+    """hdt_forward_tree_noalloc checks its scratch against the 48 MiB static array on the host,
+    before it touches the device: a 64-layer model at the 27B-like shapes with 64-node trees
+    needs more (50 MB of pending corrections alone)."""
+    kinds = [1 if l % 4 == 3 else 0 for l in range(64)]
+    slot = [dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=70000, length=65536)]
+    e = make_engine(layer_kind=kinds, gdn_hk=16, gdn_hv=32, gdn_dk=128, gdn_dv=128, attn_hq=24,
+                    attn_hkv=4, attn_d=256, max_nodes=64, slots=slot)
+    with pytest.raises(hdt.HdtError) as err:
+        e.forward_tree_noalloc([(0, [-1, 0], fake_layers(64))])
+    assert err.value.status == -4 and "static scratch" in e.last_error()
+    assert e.kv_length(0) == 65536
+    with pytest.raises(hdt.HdtError) as err:   # ... and is still subject to the pending rules
+        e.commit_tree(0, [0])
+    assert err.value.status == -5
+    e.close()
