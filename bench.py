@@ -270,6 +270,8 @@ def main():
     ap.add_argument("--workload", default="stack_65k")
     ap.add_argument("--nodes", type=int, default=0, metavar="N",
                     help="draft trees of N nodes instead of the workload's own size (1 to 64)")
+    ap.add_argument("--context", type=int, default=0, metavar="L",
+                    help="resident tokens of the first slot instead of the workload's own")
     ap.add_argument("--seed", type=int, default=20261202)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time the eager pass only")
@@ -306,6 +308,8 @@ def main():
         if not 1 <= args.nodes <= 64:
             sys.exit("--nodes takes 1 to 64")
         w = dataclasses.replace(w, n_nodes=args.nodes)
+    if args.context:
+        w = dataclasses.replace(w, lengths=[args.context] + list(w.lengths[1:]))
     ns = w.n_slots  # several slots: one joint pass over every slot's tree
     L0 = w.lengths[0]
     parents = [w.tree(args.seed, s) for s in range(ns)]
