@@ -16,7 +16,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhdt.so")
+# HDT_LIBRARY names another build of the same sources (the sanitizer build of the tests)
+LIB_PATH = os.environ.get("HDT_LIBRARY") or os.path.join(_HERE, "libhdt.so")
 
 HDT_MAX_NODES = 64
 HDT_MAX_TREES = 8

@@ -37,6 +37,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# HDT_ORACLE_LIBRARY names another build of oracle.c (the sanitizer build of the tests)
+_LOAD_PATH = os.environ.get("HDT_ORACLE_LIBRARY") or _LIB_PATH
 MAX_NODES = 64
 
 
@@ -81,9 +83,9 @@ def configure(lib):
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        if _LOAD_PATH == _LIB_PATH and not os.path.exists(_LIB_PATH):
             build()
-        _lib = configure(ctypes.CDLL(_LIB_PATH))
+        _lib = configure(ctypes.CDLL(_LOAD_PATH))
     return _lib
 
 

@@ -24,6 +24,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsynth.so")
+# HDT_SYNTH_LIBRARY names another build of synth.c (the sanitizer build of the tests)
+_LOAD_PATH = os.environ.get("HDT_SYNTH_LIBRARY") or _LIB_PATH
 
 NORMAL, NORMAL_L2, SIGMOID, EXP_NEG_SOFTPLUS = 0, 1, 2, 3
 DEFAULT_SEED = 20261202
@@ -45,9 +47,9 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        if _LOAD_PATH == _LIB_PATH and not os.path.exists(_LIB_PATH):
             build()
-        lib = ctypes.CDLL(_LIB_PATH)
+        lib = ctypes.CDLL(_LOAD_PATH)
         lib.synth_u64.restype = ctypes.c_uint64
         lib.synth_u64.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
         lib.synth_normal.restype = ctypes.c_double
