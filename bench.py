@@ -203,15 +203,18 @@ def copy_bandwidth():
 
 
 def prefill_bench(args):
-    """forward_span of T tokens through the whole stack, K times back to back from the
-    workload's context (each span appends T tokens).  Timing only: every layer of a kind
-    reads the same seeded span inputs."""
+    """A prefill of T tokens through the whole stack, K times back to back from the
+    workload's context (each span appends T tokens): forward_chunked (the WY form of the
+    delta rule and causal attention on the matrix cores) or, with --prefill-mode chain,
+    forward_span (chains of 64 through the verify kernels, bit-equal to decoding).  Timing
+    only: every layer of a kind reads the same seeded span inputs."""
     import statistics
     import torch
     import synth
     from synth.device import Instance, to_device
     w = synth.WORKLOADS[args.workload]
     T, K = args.prefill, args.steps
+    chunked = args.prefill_mode == "chunked"
     L0 = w.lengths[0]
     cap = L0 + T * (K + args.warmup) + 64
     inst = Instance(w, args.seed, lengths=[L0], trees=[[-1]], capacity=[cap], keep_host=False)
@@ -232,32 +235,44 @@ def prefill_bench(args):
         shared[kind] = d
     layers = [shared[k] for k in w.layer_kind]
     stream = torch.cuda.current_stream()
+    run = eng.forward_chunked if chunked else eng.forward_span
     for _ in range(args.warmup):
-        eng.forward_span(0, T, layers, stream.cuda_stream)
+        run(0, T, layers, stream.cuda_stream)
     torch.cuda.synchronize()
     L_start = eng.kv_length(0)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     eng.profile(True)
     for a, b in ev:
         a.record(stream)
-        eng.forward_span(0, T, layers, stream.cuda_stream)
+        run(0, T, layers, stream.cuda_stream)
         b.record(stream)
     torch.cuda.synchronize()
-    prof = {k: eng.profile_read(k) for k in (0, 1, 2, 3, 4)}
+    kinds = ((6, "wy_prep"), (7, "wy_scan"), (8, "attn_prefill"), (9, "attn_prefill_fold")) if chunked else \
+        ((0, "gdn_tree"), (1, "attn_split"), (2, "attn_tree"), (3, "commit"), (4, "gdn_conv"))
+    prof = {k: eng.profile_read(k) for k, _ in kinds}
     eng.profile(False)
     ms = [a.elapsed_time(b) for a, b in ev]
     med = statistics.median(ms)
     kernels = {name: {"avg_us": round(1e3 * prof[k][0] / max(1, prof[k][1]), 2),
-                      "ms_per_span": round(prof[k][0] / K, 3)}
-               for k, name in ((0, "gdn_tree"), (1, "attn_split"), (2, "attn_tree"), (3, "commit"),
-                               (4, "gdn_conv")) if prof[k][1] > 0}
+                      "launches": prof[k][1], "ms_per_span": round(prof[k][0] / K, 3)}
+               for k, name in kinds if prof[k][1] > 0}
+    # causal attention flops of the timed spans: token t of a span starting at L sees
+    # L + t + 1 keys; 2 flops per multiply-add, two products (scores, values)
+    attn_flops = sum(4.0 * w.attn_hq * w.attn_d * (T * (L_start + k * T) + T * (T + 1) / 2)
+                     for k in range(K)) * w.n_attn
+    mode = "chunked (WY delta rule, causal MFMA attention)" if chunked else "chains of 64"
     out = {"metric": f"prefill tokens/s, {T}-token spans appended to a {L0}-token context",
            "value": round(T / (med * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
            "warmup": args.warmup, "ms_per_span": round(med, 3), "higher_is_better": True,
            "dtype": w.dtype, "data": "synthetic; every layer of a kind reads the same span inputs",
            "config": {"workload": f"{w.name}: {w.n_gdn} GDN + {w.n_attn} attention layers, spans of "
-                                  f"{T} tokens in chains of 64 from {L_start} to {eng.kv_length(0)} tokens"},
+                                  f"{T} tokens, {mode}, from {L_start} to {eng.kv_length(0)} tokens"},
            "kernels": kernels}
+    if chunked and prof[8][1] > 0:
+        achieved = attn_flops / (prof[8][0] * 1e-3) / 1e12
+        out["roofline"] = {"bound": "mfma", "kernel": "attn_prefill_kernel", "achieved": round(achieved, 1),
+                           "peak": 2500.0, "unit": "TFLOP/s", "frac": round(achieved / 2500.0, 4),
+                           "traffic": None, "algorithmic_flops": attn_flops}
     eng.close()
     print(json.dumps(out))
 
@@ -276,8 +291,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time the eager pass only")
     ap.add_argument("--prefill", type=int, default=0, metavar="T",
-                    help="instead of the verify, time forward_span prefills of T tokens (chains "
-                         "of 64) appended to the workload's context, and print prefill tokens/s")
+                    help="instead of the verify, time prefills of T tokens appended to the "
+                         "workload's context, and print prefill tokens/s")
+    ap.add_argument("--prefill-mode", choices=("chunked", "chain"), default="chunked",
+                    help="chunked: forward_chunked; chain: forward_span (chains of 64)")
     ap.add_argument("--walk", action="store_true",
                     help="close each round with the on-device accept walk + commit (walk_commit) "
                          "on seeded tokens that accept the same path, instead of commit_tree")

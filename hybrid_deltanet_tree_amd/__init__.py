@@ -25,6 +25,7 @@ HDT_F32, HDT_BF16 = 0, 1
 STATUS = {0: "HDT_OK", -1: "HDT_E_INVALID", -2: "HDT_E_TREE", -3: "HDT_E_PATH",
           -4: "HDT_E_CAPACITY", -5: "HDT_E_ORDER", -6: "HDT_E_HIP", -7: "HDT_E_UNSUPPORTED"}
 KIND_GDN, KIND_ATTN_SPLIT, KIND_ATTN_FOLD, KIND_COMMIT, KIND_CONV, KIND_WALK = 0, 1, 2, 3, 4, 5
+KIND_WY_PREP, KIND_WY_SCAN, KIND_PF_ATTN, KIND_PF_FOLD = 6, 7, 8, 9
 
 # PyTorch owns the device memory and the streams, so libhdt must run on the same
 # HIP runtime instance.  PyTorch ships its own libamdhip64 under the same soname;
@@ -84,6 +85,8 @@ _sigs = {
                              ctypes.c_void_p]),
     "hdt_forward_span": (_S, [_E, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(hdt_layer_io),
                               ctypes.c_void_p]),
+    "hdt_forward_chunked": (_S, [_E, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(hdt_layer_io),
+                                 ctypes.c_void_p]),
     "hdt_set_anchors": (_S, [_E, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                              ctypes.c_void_p]),
     "hdt_anchor_below": (_S, [_E, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
@@ -226,6 +229,11 @@ class Engine:
     def forward_span(self, slot, T, layers, stream=0):
         """Prefill of T tokens: layers as for forward_tree, each array holding T rows."""
         self._check(hdt_forward_span(self.h, slot, T, self._io_array(layers), stream))
+
+    def forward_chunked(self, slot, T, layers, stream=0):
+        """The same prefill computed a chunk at a time on the matrix cores (equal to
+        forward_span up to rounding)."""
+        self._check(hdt_forward_chunked(self.h, slot, T, self._io_array(layers), stream))
 
     def set_anchors(self, slot, every, n_max=0, state=None, conv=None):
         self._check(hdt_set_anchors(self.h, slot, every, n_max, _ptr(state), _ptr(conv)))

@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libhdt.so")
-SOURCES = [os.path.join(HERE, "csrc", name) for name in ("kernels.hip", "kv_attention.hip", "conv.hip", "engine.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", name) for name in ("kernels.hip", "kv_attention.hip", "conv.hip", "prefill.hip", "engine.cpp")]
 
 HIPCC_FLAGS = [
     "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",

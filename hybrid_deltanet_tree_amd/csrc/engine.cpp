@@ -30,6 +30,10 @@ constexpr int64_t kSplitMin = 256;  // float32 attention: smallest split, in key
 constexpr int64_t kSplitMax = 16384;
 constexpr float kConvEps = 1e-6f;      // GDN conv: epsilon of the q/k L2 norm, y / sqrt(sum y^2 + eps)
 constexpr int64_t kKvSplitMin = 128;  // bf16 attention: smallest split (> kKvTile - 1 + kMaxNodes - 1)
+constexpr int kProfKinds = 10;        // kernel classes of hdt_profile_read
+constexpr int32_t kPfPiece = 2048;    // chunked prefill: tokens per piece (one pass through every layer)
+constexpr int32_t kPfMaxSplits = 4;   // chunked prefill: most key splits of an attention layer
+constexpr int32_t kPfItems = 1024;    // chunked prefill: attention items aimed at per layer
 
 // The scratch of one slot's round: what commit needs of the pass, the attention
 // partials and the conv staging.  Nothing in it has to start at zero: every value is
@@ -96,8 +100,15 @@ struct hdt_engine {
   int32_t *walk_m = nullptr;      // pinned host copy of each slot's last accept-walk length
   int64_t kv_per_head = 1;        // bf16 attention: most splits a row may have
   std::vector<int32_t> kv_ladder;  // bf16 attention: split sizes, ascending
-  double prof_ms[6] = {0, 0, 0, 0, 0, 0};
-  int64_t prof_count[6] = {0, 0, 0, 0, 0, 0};
+  double prof_ms[kProfKinds] = {};
+  int64_t prof_count[kProfKinds] = {};
+  // chunked prefill (hdt_forward_chunked): scratch for one piece of up to kPfPiece
+  // tokens, allocated at its first call
+  struct {
+    uint16_t *w_hi = nullptr, *w_lo = nullptr, *mq_hi = nullptr, *mq_lo = nullptr, *kt = nullptr, *qc = nullptr;
+    float *ut = nullptr, *g = nullptr, *part_acc = nullptr, *part_ml = nullptr;
+    bool allocated = false;
+  } pf;
 };
 
 namespace {
@@ -304,6 +315,10 @@ void free_scratch(hdt_engine *e) {
   if (e->walk_m) (void)hipHostFree(e->walk_m);
   e->walk_m = nullptr;
   e->allocated = false;
+  void *pf[] = {e->pf.w_hi, e->pf.w_lo, e->pf.mq_hi, e->pf.mq_lo, e->pf.kt, e->pf.qc,
+                e->pf.ut, e->pf.g, e->pf.part_acc, e->pf.part_ml};
+  for (void *p : pf) (void)hipFree(p);
+  e->pf = {};
 }
 
 // When profiling is on, hands one launch an event pair that its dispatch records
@@ -861,7 +876,7 @@ hdt_status hdt_create(const hdt_model_desc *desc, int32_t n_slots, const hdt_slo
 
 void hdt_destroy(hdt_engine *e) {
   if (!e) return;
-  if (e->allocated || !e->ev_live.empty() || !e->ev_pool.empty()) (void)hipDeviceSynchronize();
+  if (e->allocated || e->pf.allocated || !e->ev_live.empty() || !e->ev_pool.empty()) (void)hipDeviceSynchronize();
   free_scratch(e);
   for (auto &p : e->ev_live) {
     (void)hipEventDestroy(p.a);
@@ -1172,6 +1187,216 @@ hdt_status hdt_forward_span(hdt_engine *e, int32_t slot, int32_t T, const hdt_la
   return HDT_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Sizes of the chunked-prefill scratch for one piece of kPfPiece tokens.
+struct PfSizes {
+  size_t w, mq, kq, ut, g, acc, ml;
+};
+PfSizes pf_sizes(const hdt_model_desc &m) {
+  const size_t nch = kPfPiece / kWyChunk + 1, C = kWyChunk;
+  PfSizes z{};
+  if (m.gdn_hv > 0) {
+    z.w = nch * m.gdn_hv * C * m.gdn_dk * 2;
+    z.mq = nch * m.gdn_hv * C * C * 2;
+    z.kq = nch * m.gdn_hk * C * m.gdn_dk * 2;
+    z.ut = nch * m.gdn_hv * C * m.gdn_dv * 4;
+    z.g = nch * m.gdn_hv * 3 * C * 4;
+  }
+  if (m.attn_hkv > 0) {
+    const size_t G = m.attn_hq / m.attn_hkv;
+    const size_t rows_cap = (kPfPiece * G + kPfRows - 1) / kPfRows * kPfRows;
+    z.acc = static_cast<size_t>(m.attn_hkv) * kPfMaxSplits * rows_cap * m.attn_d * 4;
+    z.ml = static_cast<size_t>(m.attn_hkv) * kPfMaxSplits * rows_cap * 2 * 4;
+  }
+  return z;
+}
+
+hdt_status ensure_pf_alloc(hdt_engine *e) {
+  if (e->pf.allocated) return HDT_OK;
+  const PfSizes z = pf_sizes(e->desc);
+  struct {
+    void **p;
+    size_t n;
+  } parts[] = {{reinterpret_cast<void **>(&e->pf.w_hi), z.w},   {reinterpret_cast<void **>(&e->pf.w_lo), z.w},
+               {reinterpret_cast<void **>(&e->pf.mq_hi), z.mq}, {reinterpret_cast<void **>(&e->pf.mq_lo), z.mq},
+               {reinterpret_cast<void **>(&e->pf.kt), z.kq},    {reinterpret_cast<void **>(&e->pf.qc), z.kq},
+               {reinterpret_cast<void **>(&e->pf.ut), z.ut},    {reinterpret_cast<void **>(&e->pf.g), z.g},
+               {reinterpret_cast<void **>(&e->pf.part_acc), z.acc},
+               {reinterpret_cast<void **>(&e->pf.part_ml), z.ml}};
+  for (auto &x : parts)
+    if (x.n > 0 && hipMalloc(x.p, x.n) != hipSuccess) return fail(e, HDT_E_HIP, "hipMalloc of the prefill scratch failed");
+  e->pf.allocated = true;
+  return HDT_OK;
+}
+
+// One piece of p tokens (span rows [t0, t0 + p)) through every layer, in layer order.
+hdt_status chunked_piece(hdt_engine *e, SlotState &s, const hdt_layer_io *io, int32_t t0, int32_t p,
+                         hipStream_t st) {
+  const hdt_model_desc &m = e->desc;
+  const size_t z = e->esz, t = static_cast<size_t>(t0);
+  const int64_t L = s.d.length;
+  for (int l = 0; l < m.n_layers; ++l) {
+    const hdt_layer_io &x = io[l];
+    const int32_t ki = e->kind_index[l];
+    if (e->kind[l] == 0) {
+      const size_t bqk = static_cast<size_t>(m.gdn_hk) * m.gdn_dk * z, bv = static_cast<size_t>(m.gdn_hv) * m.gdn_dv * z,
+                   bg = static_cast<size_t>(m.gdn_hv) * z;
+      WyPrep a{};
+      a.q = static_cast<const char *>(x.q) + t * bqk;
+      a.k = static_cast<const char *>(x.k) + t * bqk;
+      a.v = static_cast<const char *>(x.v) + t * bv;
+      a.alpha = static_cast<const char *>(x.alpha) + t * bg;
+      a.beta = static_cast<const char *>(x.beta) + t * bg;
+      a.T = p;
+      a.off = static_cast<int32_t>(L % kWyChunk);
+      a.n_chunks = (a.off + p + kWyChunk - 1) / kWyChunk;
+      a.hk = m.gdn_hk;
+      a.hv = m.gdn_hv;
+      a.scale = m.gdn_scale;
+      a.w_hi = e->pf.w_hi;
+      a.w_lo = e->pf.w_lo;
+      a.mq_hi = e->pf.mq_hi;
+      a.mq_lo = e->pf.mq_lo;
+      a.kt = e->pf.kt;
+      a.qc = e->pf.qc;
+      a.ut = e->pf.ut;
+      a.g = e->pf.g;
+      {
+        ProfScope ps(e, 6);
+        if (launch_wy_prep(a, m.gdn_dk, st, ps.events()) != hipSuccess)
+          return fail(e, HDT_E_HIP, "layer %d: WY prep launch failed", l);
+      }
+      WyScan b{};
+      b.w_hi = a.w_hi;
+      b.w_lo = a.w_lo;
+      b.mq_hi = a.mq_hi;
+      b.mq_lo = a.mq_lo;
+      b.kt = a.kt;
+      b.qc = a.qc;
+      b.ut = a.ut;
+      b.g = a.g;
+      b.state = s.d.gdn_state + static_cast<size_t>(ki) * m.gdn_hv * m.gdn_dv * m.gdn_dk;
+      b.o = static_cast<char *>(x.o) + t * bv;
+      b.T = p;
+      b.off = a.off;
+      b.n_chunks = a.n_chunks;
+      b.hk = m.gdn_hk;
+      b.hv = m.gdn_hv;
+      ProfScope ps(e, 7);
+      if (launch_wy_scan(b, m.gdn_dk, st, ps.events()) != hipSuccess)
+        return fail(e, HDT_E_HIP, "layer %d: WY scan launch failed", l);
+    } else {
+      const size_t bq = static_cast<size_t>(m.attn_hq) * m.attn_d * z, bk = static_cast<size_t>(m.attn_hkv) * m.attn_d * z;
+      const size_t view = static_cast<size_t>(m.attn_hkv) * s.d.capacity * m.attn_d * z;
+      PfCopy c{};
+      c.k = static_cast<const char *>(x.k) + t * bk;
+      c.v = static_cast<const char *>(x.v) + t * bk;
+      c.kc = static_cast<char *>(s.d.k_cache) + static_cast<size_t>(ki) * view;
+      c.vc = static_cast<char *>(s.d.v_cache) + static_cast<size_t>(ki) * view;
+      c.cap = s.d.capacity;
+      c.L = L;
+      c.T = p;
+      c.hkv = m.attn_hkv;
+      if (launch_pf_copy(c, m.attn_d, st) != hipSuccess) return fail(e, HDT_E_HIP, "layer %d: row copy failed", l);
+      PfAttn a{};
+      const int32_t G = m.attn_hq / m.attn_hkv;
+      a.q = static_cast<const char *>(x.q) + t * bq;
+      a.kc = c.kc;
+      a.vc = c.vc;
+      a.o = static_cast<char *>(x.o) + t * bq;
+      a.part_acc = e->pf.part_acc;
+      a.part_ml = e->pf.part_ml;
+      a.cap = s.d.capacity;
+      a.L = L;
+      a.T = p;
+      a.hq = m.attn_hq;
+      a.hkv = m.attn_hkv;
+      a.row_tiles = (p * G + kPfRows - 1) / kPfRows;
+      a.rows_cap = a.row_tiles * kPfRows;
+      const int32_t tiles_heads = a.row_tiles * m.attn_hkv;
+      a.nsplit = std::max(1, std::min(kPfMaxSplits, (kPfItems + tiles_heads - 1) / tiles_heads));
+      const int64_t keys = L + p;
+      a.split = static_cast<int32_t>(((keys + a.nsplit - 1) / a.nsplit + kKvTile - 1) / kKvTile * kKvTile);
+      a.nsplit = static_cast<int32_t>((keys + a.split - 1) / a.split);
+      a.items = (tiles_heads * a.nsplit + 7) / 8 * 8;
+      a.c2 = m.attn_scale * 1.4426950408889634f;
+      {
+        ProfScope ps(e, 8);
+        if (launch_pf_attn(a, m.attn_d, st, ps.events()) != hipSuccess)
+          return fail(e, HDT_E_HIP, "layer %d: prefill attention launch failed", l);
+      }
+      if (a.nsplit > 1) {
+        ProfScope ps(e, 9);
+        if (launch_pf_fold(a, m.attn_d, st, ps.events()) != hipSuccess)
+          return fail(e, HDT_E_HIP, "layer %d: prefill fold launch failed", l);
+      }
+    }
+  }
+  return HDT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hdt_status hdt_forward_chunked(hdt_engine *e, int32_t slot, int32_t T, const hdt_layer_io *io, void *stream) {
+  if (!e) return HDT_E_INVALID;
+  if (slot < 0 || slot >= static_cast<int32_t>(e->slots.size()))
+    return fail(e, HDT_E_INVALID, "slot %d out of range", slot);
+  if (T < 1 || !io) return fail(e, HDT_E_INVALID, "span of %d tokens", T);
+  const hdt_model_desc &m = e->desc;
+  if (m.io_dtype != HDT_BF16) return fail(e, HDT_E_UNSUPPORTED, "the chunked prefill needs bf16 storage");
+  if (e->n_gdn > 0 && (m.gdn_dk != 128 || m.gdn_dv != 128))
+    return fail(e, HDT_E_UNSUPPORTED, "the chunked prefill needs GDN heads of 128 by 128");
+  if (e->n_gdn > 0 && m.gdn_conv > 0)
+    return fail(e, HDT_E_UNSUPPORTED, "the chunked prefill does not run the short conv: use hdt_forward_span");
+  if (e->n_attn > 0 && m.attn_d != 256) return fail(e, HDT_E_UNSUPPORTED, "the chunked prefill needs attn_d = 256");
+  if (settle(e, slot) != HDT_OK) return HDT_E_HIP;
+  SlotState &s = e->slots[slot];
+  if (s.pending) return fail(e, HDT_E_ORDER, "slot %d has a pending round", slot);
+  if (s.d.length + T > s.d.capacity)
+    return fail(e, HDT_E_CAPACITY, "slot %d: length %lld + %d tokens exceeds capacity %lld", slot,
+                (long long)s.d.length, T, (long long)s.d.capacity);
+  for (int l = 0; l < m.n_layers; ++l) {
+    const hdt_layer_io &x = io[l];
+    if (!x.q || !x.k || !x.v || !x.o) return fail(e, HDT_E_INVALID, "layer %d: NULL q/k/v/o", l);
+    if (e->kind[l] == 0 && (!x.alpha || !x.beta)) return fail(e, HDT_E_INVALID, "layer %d: NULL alpha/beta", l);
+    if (!aligned16(x.q) || !aligned16(x.k) || !aligned16(x.v) || !aligned16(x.o))
+      return fail(e, HDT_E_INVALID, "layer %d: buffers must be 16-byte aligned", l);
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!e->pf.allocated) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+      return fail(e, HDT_E_ORDER, "the first chunked prefill allocates scratch: run it outside graph capture");
+  }
+  hdt_status r = ensure_pf_alloc(e);
+  if (r != HDT_OK) return r;
+  for (int32_t t0 = 0; t0 < T;) {
+    int32_t p = std::min(kPfPiece, T - t0);
+    if (s.anchor_every > 0) {  // a piece ends at every anchor position
+      const int64_t next = (s.d.length / s.anchor_every + 1) * s.anchor_every;
+      p = static_cast<int32_t>(std::min<int64_t>(p, next - s.d.length));
+    }
+    r = chunked_piece(e, s, io, t0, p, st);
+    if (r != HDT_OK) return r;
+    s.d.length += p;
+    if (s.anchor_every > 0 && s.d.length % s.anchor_every == 0) {
+      const int64_t k = s.d.length / s.anchor_every - 1;
+      if (k < s.anchor_n) {
+        r = anchor_copy(e, slot, static_cast<int32_t>(k), true, st);
+        if (r != HDT_OK) return r;
+      }
+    }
+    t0 += p;
+  }
+  e->err.clear();
+  return HDT_OK;
+}
+
 hdt_status hdt_set_anchors(hdt_engine *e, int32_t slot, int64_t every, int32_t n_max, float *state,
                            void *conv) {
   if (!e) return HDT_E_INVALID;
@@ -1363,7 +1588,7 @@ hdt_status hdt_profile(hdt_engine *e, int32_t enable) {
 }
 
 hdt_status hdt_profile_read(hdt_engine *e, int32_t kind, double *ms, int64_t *launches) {
-  if (!e || kind < 0 || kind > 5 || !ms || !launches) return HDT_E_INVALID;
+  if (!e || kind < 0 || kind >= kProfKinds || !ms || !launches) return HDT_E_INVALID;
   for (auto &p : e->ev_live) {
     if (hipEventSynchronize(p.b) != hipSuccess) return fail(e, HDT_E_HIP, "event wait failed");
     float t = 0.0f;

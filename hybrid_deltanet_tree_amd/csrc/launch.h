@@ -229,6 +229,57 @@ constexpr uint64_t kSnapshotMagic = 0x3150414E53544448ull;  // "HDTSNAP1" little
 constexpr int64_t kSnapshotHeaderBytes = 256;                // sections start 256-byte aligned
 static_assert(sizeof(SnapshotHeader) == 64, "eight 64-bit words");
 
+// ---------------------------------------------------------------- chunked prefill
+// A span of T tokens after the slot's L committed ones.  GDN layers run the chunked
+// (WY) form of the delta rule over chunks anchored at absolute multiples of kWyChunk:
+// chunk c covers span rows [max(0, kWyChunk c - off), min(T, kWyChunk (c + 1) - off)),
+// off = L mod kWyChunk.  Attention layers run causal attention over the cache after
+// the span's own rows were copied into it.
+constexpr int kWyChunk = 64;
+constexpr int kPfRows = 128;   // prefill attention: query rows per workgroup (4 waves x 32)
+constexpr int kPfStages = 4;   // prefill attention: LDS tile ring
+
+struct WyPrep {
+  const void *q, *k, *v, *alpha, *beta;  // span rows of this layer (bf16)
+  int32_t T, off, n_chunks, hk, hv;
+  float scale;                           // readout scale s
+  uint16_t *w_hi, *w_lo;                 // [n_chunks][hv][64][dk] W = T diag(b g) K, split in two bf16
+  uint16_t *mq_hi, *mq_lo;               // [n_chunks][hv][64][64] s (g_i / g_j) q_i.k_j, j <= i
+  uint16_t *kt;                          // [n_chunks][hk][dk][64] K transposed, zero past the chunk
+  uint16_t *qc;                          // [n_chunks][hk][64][dk] Q, zero past the chunk
+  float *ut;                             // [n_chunks][hv][64][dv] U~ = T diag(b) V
+  float *g;                              // [n_chunks][hv][3][64] s g_i | g_n / g_j | g_n at [2][0]
+};
+
+struct WyScan {
+  const uint16_t *w_hi, *w_lo, *mq_hi, *mq_lo, *kt, *qc;
+  const float *ut, *g;
+  float *state;                          // [hv][dv][dk] this layer's state, advanced in place
+  void *o;                               // [T][hv][dv] out (bf16)
+  int32_t T, off, n_chunks, hk, hv;
+};
+
+struct PfCopy {
+  const void *k, *v;                     // [T][hkv][D] span rows
+  void *kc, *vc;                         // [hkv][cap][D] caches of this layer
+  int64_t cap, L;
+  int32_t T, hkv;
+};
+
+struct PfAttn {
+  const void *q;                         // [T][hq][D] span queries (bf16)
+  const void *kc, *vc;                   // [hkv][cap][D], span rows already at [L, L + T)
+  void *o;                               // [T][hq][D] out (bf16), written here when nsplit = 1
+  float *part_acc;                       // [hkv][nsplit][rows_cap][D] unnormalised sums (nsplit > 1)
+  float *part_ml;                        // [hkv][nsplit][rows_cap][2] running max (base 2), sum
+  int64_t cap, L;
+  int32_t T, hq, hkv;
+  int32_t row_tiles, rows_cap;           // rows_cap = kPfRows row_tiles
+  int32_t nsplit, split;                 // key splits of `split` keys (a multiple of kKvTile)
+  int32_t items;                         // hkv nsplit row_tiles, padded to a multiple of 8
+  float c2;                              // softmax scale times log2(e)
+};
+
 // ---------------------------------------------------------------- host entry points
 // Each returns the result of hipGetLastError() after enqueueing.  With ev0 / ev1
 // set, the dispatch itself records its start and end time into them (the
@@ -251,6 +302,11 @@ hipError_t launch_commit(const CommitLaunch &a, int dk, int bf16, int n_blocks, 
 hipError_t launch_gdn_conv(const ConvLaunch &a, int bf16, hipStream_t s, KernelEvents ev);
 hipError_t launch_walk(const WalkLaunch &a, hipStream_t s, KernelEvents ev);
 hipError_t launch_snapshot_header(const SnapshotHeader &h, void *dst, hipStream_t s);
+hipError_t launch_wy_prep(const WyPrep &a, int dk, hipStream_t s, KernelEvents ev);
+hipError_t launch_wy_scan(const WyScan &a, int dk, hipStream_t s, KernelEvents ev);
+hipError_t launch_pf_copy(const PfCopy &a, int D, hipStream_t s);
+hipError_t launch_pf_attn(const PfAttn &a, int D, hipStream_t s, KernelEvents ev);
+hipError_t launch_pf_fold(const PfAttn &a, int D, hipStream_t s, KernelEvents ev);
 
 // The library's static scratch array (hdt_forward_tree_noalloc): kStaticScratchBytes per
 // device, held until the process ends.  static_scratch_address resolves its device

@@ -234,6 +234,31 @@ hdt_status hdt_forward_span(hdt_engine *eng, int32_t slot, int32_t T, const hdt_
                             void *stream);
 
 /*
+ * forward_chunked: the same prefill as hdt_forward_span (T tokens after the slot's
+ * committed ones, io of n_layers entries with T rows each, committed as it goes,
+ * anchors filled), computed a chunk at a time on the matrix cores ("One request, end
+ * to end", 2.5 "The caches decide where the prefill starts": the prompt past the
+ * resident prefix goes through the model once, with state anchors; "How ignis serves
+ * a request", 3 "Prefill reads the prompt", in chunks).
+ *  GDN layers: the chunked (WY) form of the same recurrence over chunks of 64 tokens
+ *    anchored at absolute positions (a multiple of 64); the state between chunks and
+ *    the final state are float32.
+ *  Attention layers: the span's k/v rows are written into the cache at [L, L + T),
+ *    then each row (token t, q head j) attends causally to cache rows 0 .. L + t.
+ * The span is cut into pieces of at most 2048 tokens (and at anchor positions) that
+ * each pass through every layer in order.  Outputs, rows and state equal the
+ * token-by-token recurrence up to rounding (outputs within the io precision), not bit
+ * for bit: hdt_forward_span is the bit-exact chain mode.  Needs bf16 storage, GDN
+ * heads of 128 by 128 with gdn_conv = 0 and attn_d = 256 (else HDT_E_UNSUPPORTED);
+ * alpha in (0, 1].  Buffers 16-byte aligned.  The first call allocates the
+ * library's prefill scratch (not under graph capture).  Needs no pending round;
+ * length + T <= capacity.  length += T.
+ * Errors: HDT_E_INVALID, HDT_E_ORDER, HDT_E_CAPACITY, HDT_E_UNSUPPORTED, HDT_E_HIP.
+ */
+hdt_status hdt_forward_chunked(hdt_engine *eng, int32_t slot, int32_t T, const hdt_layer_io *io,
+                               void *stream);
+
+/*
  * State anchors of a slot ("One request, end to end", 2.5: recurrent-state anchors
  * every 1,024 tokens let a later turn resume inside the resident prefix).  Device
  * buffers owned by the caller: state float32 [n_max][n_gdn][gdn_hv][gdn_dv][gdn_dk]
@@ -348,7 +373,8 @@ hdt_status hdt_split_size(const hdt_engine *eng, int32_t slot, int64_t position,
  * event pair around every launch on the launch stream; hdt_profile_read waits
  * for the recorded events and returns, for kernel class `kind` (0 = GDN tree
  * walk, 1 = attention split pass, 2 = attention fold, 3 = commit, 4 = GDN conv,
- * 5 = accept walk), the summed
+ * 5 = accept walk, 6 = chunked-prefill GDN prep, 7 = its GDN scan, 8 = its attention,
+ * 9 = its attention merge), the summed
  * milliseconds and the launch count since the last read; then clears them.
  */
 hdt_status hdt_profile(hdt_engine *eng, int32_t enable);

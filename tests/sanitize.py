@@ -51,7 +51,7 @@ def build() -> dict:
     orc_src = [os.path.join(ROOT, "oracle", "oracle.c")]
     syn_src = [os.path.join(ROOT, "synth", "synth.c")]
     csrc = os.path.join(ROOT, "hybrid_deltanet_tree_amd", "csrc")
-    hdt_src = [os.path.join(csrc, n) for n in ("kernels.hip", "kv_attention.hip", "conv.hip", "engine.cpp")]
+    hdt_src = [os.path.join(csrc, n) for n in ("kernels.hip", "kv_attention.hip", "conv.hip", "prefill.hip", "engine.cpp")]
     hdt_dep = hdt_src + glob.glob(os.path.join(csrc, "*.h")) + [os.path.join(ROOT, "include", "hdt.h")]
     orc = _build(os.path.join(OUT, "liboracle.so"), orc_src,
                  [LLVM, "-O1", "-g", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", *SAN,

@@ -1,0 +1,208 @@
+"""The chunked prefill (forward_chunked): the WY form of the delta rule and causal attention
+on the matrix cores, against the oracle.
+
+  * every output row of a span, the committed state and the K/V rows it writes, against
+    the oracle's sequential recurrence and attention of each token over every earlier
+    position: spans whose chunks start and end off the 64-token grid, a one-token span, a
+    span that fills exactly one chunk, and a span of two pieces (longer than 2,048 tokens)
+    with sampled attention rows;
+  * anchors hold the oracle's state at their positions; rollback to an anchor and forwarding
+    the rest again gives the same bits (the pass is deterministic);
+  * full size: the stack's head shapes at 65,536 resident tokens and a 2,048-token span,
+    four sampled GDN heads and sampled attention rows over the whole context.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth.device import Instance, to_device, to_host
+from tests import gpu_util as gu
+from tests.brute import rel_err
+from tests.test_gpu_span import SEED, SPAN, check_span_against_oracle, span_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import hybrid_deltanet_tree_amd as hdt  # noqa: E402
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _f32(a):
+    return synth.bf16_bits_to_f32(a)
+
+
+@pytest.mark.parametrize("L,T", [(300, 200), (300, 37), (300, 1), (256, 64), (0, 100)])
+def test_chunked_matches_oracle(L, T):
+    _say(f"chunked prefill: {T} tokens at {L}")
+    inst = Instance(SPAN, SEED, lengths=[L], capacity=[L + T + 64])
+    eng = inst.engine()
+    host, dev = span_inputs(inst, T)
+    eng.forward_chunked(0, T, dev, gu.stream())
+    gu.sync()
+    assert eng.kv_length(0) == L + T
+    check_span_against_oracle(inst, host, dev, L, T)
+    eng.close()
+
+
+def oracle_chain(S0, q, k, v, a, b, piece=256):
+    """Outputs and final state of the sequential recurrence over a long chain, in pieces
+    of `piece` tokens (each piece starts from the state the previous one ended in)."""
+    T = q.shape[0]
+    outs, S = [], S0
+    for t0 in range(0, T, piece):
+        t1 = min(T, t0 + piece)
+        o, states = oracle.gdn_tree(synth.chain_tree(t1 - t0), S, q[t0:t1], k[t0:t1], v[t0:t1],
+                                    a[t0:t1], b[t0:t1], want_states=True)
+        outs.append(o)
+        S = states[-1]
+    return np.concatenate(outs), S
+
+
+def _check_attn_rows(got, h, Kc, Vc, L, tokens, heads):
+    """Rows (t, j) against the oracle: token t sees positions 0 .. L + t (the span's own
+    rows already in Kc, Vc)."""
+    worst = 0.0
+    for t in tokens:
+        for j in heads:
+            ref = oracle.attn_row([-1], L + t, Kc, Vc, h["q"][t:t + 1], h["k"][t:t + 1], h["v"][t:t + 1], 0, j)
+            err = rel_err(got[t, j], ref)
+            worst = max(worst, err)
+            assert err <= gu.TOL_BF16_OUT, f"token {t} head {j}: {err:.3e}"
+    return worst
+
+
+def test_chunked_two_pieces():
+    L, T = 300, 2100  # pieces of 2,048 and 52 tokens
+    _say(f"chunked prefill: {T} tokens at {L} (two pieces)")
+    inst = Instance(SPAN, SEED, lengths=[L], capacity=[L + T + 64])
+    eng = inst.engine()
+    host, dev = span_inputs(inst, T)
+    eng.forward_chunked(0, T, dev, gu.stream())
+    gu.sync()
+    assert eng.kv_length(0) == L + T
+    w = inst.w
+    gi = ai = 0
+    tokens = sorted(set(list(range(0, T, 97)) + [2046, 2047, 2048, 2049, T - 1]))
+    for l, kind in enumerate(w.layer_kind):
+        h = host[l]
+        got = _f32(to_host(dev[l]["o"], w.dtype))
+        if kind == 0:
+            ref, S = oracle_chain(inst.h_state[0][gi], h["q"], h["k"], h["v"], h["alpha"], h["beta"])
+            err = gu.max_rel_per_head(got, ref)
+            assert err <= gu.TOL_BF16_OUT, f"layer {l}: {err:.3e}"
+            serr = rel_err(inst.state[0][gi].cpu().numpy(), S)
+            assert serr <= gu.TOL_F32, f"layer {l} state: {serr:.3e}"
+            _say(f"  layer {l} (GDN): outputs {err:.2e}, state {serr:.2e}")
+            gi += 1
+        else:
+            Kf = inst.h_kc[0][ai].copy()
+            Vf = inst.h_vc[0][ai].copy()
+            Kf[:, L:L + T] = np.transpose(h["k"], (1, 0, 2))
+            Vf[:, L:L + T] = np.transpose(h["v"], (1, 0, 2))
+            worst = _check_attn_rows(got, h, Kf, Vf, L, tokens, range(w.attn_hq))
+            for name, cache in (("k", inst.kc[0]), ("v", inst.vc[0])):
+                rows = to_host(cache[ai, :, L:L + T], w.dtype)
+                assert np.array_equal(rows, np.transpose(h[name], (1, 0, 2)))
+            _say(f"  layer {l} (attention, {len(tokens)} tokens): {worst:.2e}")
+            ai += 1
+    eng.close()
+
+
+def test_chunked_anchors_and_rollback():
+    L, T, every = 300, 300, 128  # anchors at 384 and 512
+    inst = Instance(SPAN, SEED, lengths=[L], capacity=[L + T + 64])
+    eng = inst.engine()
+    w = inst.w
+    n_max = 8
+    astate = torch.zeros((n_max, w.n_gdn, w.gdn_hv, w.gdn_dv, w.gdn_dk), dtype=torch.float32, device="cuda")
+    eng.set_anchors(0, every, n_max, astate)
+    host, dev = span_inputs(inst, T)
+    S0 = [s.copy() for s in inst.h_state[0]]
+    eng.forward_chunked(0, T, dev, gu.stream())
+    gu.sync()
+    first = [to_host(d["o"], w.dtype).copy() for d in dev]
+    final = inst.state[0].clone()
+    gdn = [l for l, kind in enumerate(w.layer_kind) if kind == 0]
+    for pos in (384, 512):
+        assert eng.anchor_below(0, pos) == pos
+        k = pos // every - 1
+        for gi, l in enumerate(gdn):
+            h = host[l]
+            ref = oracle.gdn_commit(list(range(pos - L)), S0[gi], h["k"], h["v"], h["alpha"], h["beta"])
+            err = rel_err(astate[k, gi].cpu().numpy(), ref)
+            assert err <= gu.TOL_F32, f"anchor {pos} layer {l}: {err:.3e}"
+    # back to 384, then the rest of the span again
+    eng.rollback_to(0, 384, gu.stream())
+    gu.sync()
+    assert eng.kv_length(0) == 384
+    rest = [{name: x[384 - L:] for name, x in d.items()} for d in dev]
+    for d in rest:
+        d["o"].zero_()
+    eng.forward_chunked(0, T - (384 - L), rest, gu.stream())
+    gu.sync()
+    assert eng.kv_length(0) == L + T
+    for l, d in enumerate(dev):
+        assert np.array_equal(to_host(d["o"], w.dtype)[384 - L:], first[l][384 - L:]), f"layer {l}"
+    assert torch.equal(inst.state[0], final)
+    eng.close()
+
+
+def test_chunked_full_size_sampled():
+    """The stack's head shapes (16 q/k and 32 v GDN heads of 128 x 128; 24 q / 4 kv heads of
+    256) at 65,536 resident tokens, one GDN and one attention layer, a 2,048-token span."""
+    base = synth.WORKLOADS["stack_65k"]
+    w = synth.Workload("stack_65k_prefill", [0, 1], base.gdn_hk, base.gdn_hv, base.gdn_dk, base.gdn_dv,
+                       base.attn_hq, base.attn_hkv, base.attn_d, base.dtype, [65536], 16, "draft")
+    L, T = 65536, 2048
+    _say(f"chunked prefill, full size: {T} tokens at {L}")
+    inst = Instance(w, SEED, capacity=[L + T + 64])
+    eng = inst.engine()
+    host, dev = span_inputs(inst, T, tag="prefill")
+    eng.forward_chunked(0, T, dev, gu.stream())
+    gu.sync()
+    assert eng.kv_length(0) == L + T
+    # GDN: v heads 0, 1 (q/k head 0) and 30, 31 (q/k head 15)
+    h = host[0]
+    vh, kh = [0, 1, 30, 31], [0, 15]
+    ref, S = oracle_chain(inst.h_state[0][0][vh], h["q"][:, kh], h["k"][:, kh], h["v"][:, vh],
+                          h["alpha"][:, vh], h["beta"][:, vh], piece=512)
+    got = _f32(to_host(dev[0]["o"], w.dtype))[:, vh]
+    err = gu.max_rel_per_head(got, ref)
+    assert err <= gu.TOL_BF16_OUT, f"GDN outputs: {err:.3e}"
+    serr = rel_err(inst.state[0][0][vh].cpu().numpy(), S)
+    assert serr <= gu.TOL_F32, f"GDN state: {serr:.3e}"
+    _say(f"  GDN (4 heads): outputs {err:.2e}, state {serr:.2e}")
+    # attention: sampled tokens, every q head, over all 65,536 + t keys
+    h = host[1]
+    Kf = inst.h_kc[0][0].copy()
+    Vf = inst.h_vc[0][0].copy()
+    Kf[:, L:L + T] = np.transpose(h["k"], (1, 0, 2))
+    Vf[:, L:L + T] = np.transpose(h["v"], (1, 0, 2))
+    got = _f32(to_host(dev[1]["o"], w.dtype))
+    worst = _check_attn_rows(got, h, Kf, Vf, L, [0, 1, 21, 22, 127, 1000, 2047], range(w.attn_hq))
+    _say(f"  attention (7 tokens x 24 heads): {worst:.2e}")
+    eng.close()
+
+
+def test_chunked_refusals_change_nothing():
+    inst = Instance(SPAN, SEED, lengths=[300], capacity=[400])
+    eng = inst.engine()
+    host, dev = span_inputs(inst, 64)
+    before = inst.state[0].clone()
+    with pytest.raises(hdt.HdtError) as e:
+        eng.forward_chunked(0, 101, dev, gu.stream())  # past capacity
+    assert e.value.status == -4
+    eng.forward_tree([inst.tree_arg(0)], gu.stream())
+    with pytest.raises(hdt.HdtError) as e:
+        eng.forward_chunked(0, 64, dev, gu.stream())  # a round is pending
+    assert e.value.status == -5
+    gu.sync()
+    assert torch.equal(inst.state[0], before) and eng.kv_length(0) == 300
+    eng.close()
