@@ -376,7 +376,7 @@ __global__ __launch_bounds__(256) void gdn_wy_scan_kernel(const WyScan P) {
       *reinterpret_cast<uint2 *>(&s_hi[ln][d]) = *reinterpret_cast<const uint2 *>(hi);
       *reinterpret_cast<uint2 *>(&s_lo[ln][d]) = *reinterpret_cast<const uint2 *>(lo);
     }
-    __syncthreads();
+    lds_barrier();  // the next chunk's operand loads stay in flight
     // ---- W S and Q S for tokens [16 w, 16 w + 16)
     floatx4 ws = floatx4{0.f, 0.f, 0.f, 0.f}, qs = ws;
 #pragma unroll
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(256) void gdn_wy_scan_kernel(const WyScan P) {
       *reinterpret_cast<uint2 *>(&w_hi[ln][t]) = *reinterpret_cast<const uint2 *>(vh);
       *reinterpret_cast<uint2 *>(&w_lo[ln][t]) = *reinterpret_cast<const uint2 *>(vl);
     }
-    __syncthreads();
+    lds_barrier();  // the next chunk's operand loads stay in flight
     // ---- O += Mq U, written for the chunk's tokens
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -503,45 +503,52 @@ struct PfLane {
 // exceeds it by more than this (base-2 units).
 constexpr float kPfLazy = 8.0f;
 
-// One tile of 32 keys from absolute position tb for this wave's 32 rows.  Register r of
-// the scores holds key 8 (r / 4) + 4 h + r % 4; the probability operand of the value
-// MFMA for keys 16 s .. 16 s + 15 is registers 8 s .. 8 s + 7, which the transposed
-// value reads match key for key.  MASK: keys past the lane's `pos` get probability 0;
-// a row with no key yet keeps m = -inf, l = 0 and acc = 0.
-template <int D, bool MASK>
-__device__ __forceinline__ void pf_tile(PfRows<D> &st, uint32_t tile, const PfLane<D> &ofs, int64_t tb,
-                                        int64_t pos, float c2) {
-  using C = PfCfg<D>;
-  constexpr int KQ = C::KQ, DB = C::DB;
-  constexpr int KB16 = 16 * C::ROWB;
-  constexpr int KPRE = 8;  // score operand reads in flight ahead of their MFMA
-  const int lane = threadIdx.x & 63, h = lane >> 5;
+// Scores S^T = K Q^T of one tile (its K half at `tile`) for this wave's 32 rows.
+// Register r holds key 8 (r / 4) + 4 (l / 32) + r % 4 of the lane's row.  Even and odd
+// k-steps accumulate in two independent chains.
+template <int D>
+__device__ __forceinline__ floatx16 pf_scores(const PfRows<D> &st, uint32_t tile, const PfLane<D> &ofs) {
+  constexpr int KQ = PfCfg<D>::KQ;
   typedef __attribute__((address_space(3))) const bf16x8 *lds_b8;
   bf16x8 ka[KQ];
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // no LDS read of this wave is outstanding
 #pragma unroll
-  for (int kk = 0; kk < KPRE; ++kk) ka[kk] = *(lds_b8)(lds_ptr(tile + ofs.ko[kk]));
-  __builtin_amdgcn_sched_barrier(0);
+  for (int kk = 0; kk < KQ; ++kk) ka[kk] = *(lds_b8)(lds_ptr(tile + ofs.ko[kk]));
   floatx16 s0 = floatx16{}, s1 = floatx16{};
 #pragma unroll
   for (int kk = 0; kk < KQ; ++kk) {
-    if (kk + KPRE < KQ) ka[kk + KPRE] = *(lds_b8)(lds_ptr(tile + ofs.ko[kk + KPRE]));
     if (kk & 1)
       s1 = mfma32(ka[kk], st.q[kk], s1);
     else
       s0 = mfma32(ka[kk], st.q[kk], s0);
   }
-  const floatx16 s = s0 + s1;
+  return s0 + s1;
+}
+
+// One step of the pipelined tile loop: the online softmax of tile t's scores `s`
+// (keys from absolute position tb) and its value product (V half at `tv`), with the
+// score MFMAs of tile t + 1 (K half at `tk`) interleaved into the softmax so that the
+// matrix cores and the vector ALU work at once; returns tile t + 1's scores.  The
+// probability operand of the value MFMA for keys 16 s .. 16 s + 15 is registers 8 s ..
+// 8 s + 7, which the transposed value reads match key for key.  MASK: keys past the
+// lane's `pos` get probability 0; a row with no key yet keeps m = -inf, l = 0, acc = 0.
+template <int D, bool MASK>
+__device__ __forceinline__ floatx16 pf_step(PfRows<D> &st, const floatx16 &s, uint32_t tk, uint32_t tv,
+                                            const PfLane<D> &ofs, int64_t tb, int64_t pos, float c2) {
+  using C = PfCfg<D>;
+  constexpr int DB = C::DB;
+  constexpr int KB16 = 16 * C::ROWB;
+  const int lane = threadIdx.x & 63, h = lane >> 5;
   bf16x8 va[DB][2];
 #pragma unroll
   for (int j = 0; j < DB; ++j)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const shortx4 lo = ds_read_tr_at(tile + ofs.vo[j][0] + kb * KB16);
-      const shortx4 hi = ds_read_tr_at(tile + ofs.vo[j][1] + kb * KB16);
+      const shortx4 lo = ds_read_tr_at(tv + ofs.vo[j][0] + kb * KB16);
+      const shortx4 hi = ds_read_tr_at(tv + ofs.vo[j][1] + kb * KB16);
       va[j][kb] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
                                                  lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
     }
+  const floatx16 sn = pf_scores<D>(st, tk, ofs);
   float z[16];
   float mt = -INFINITY;
 #pragma unroll
@@ -572,6 +579,12 @@ __device__ __forceinline__ void pf_tile(PfRows<D> &st, uint32_t tile, const PfLa
   lt = pair_sum(lt);
   st.l = st.l * corr + lt;
   st.m = mn;
+  // the LDS reads first, then each score MFMA followed by a share of the softmax
+#pragma unroll
+  for (int i = 0; i < C::KQ; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five VALU instructions
+  }
   if (__any(corr != 1.0f)) {
 #pragma unroll
     for (int j = 0; j < DB; ++j) st.acc[j] = st.acc[j] * corr;
@@ -580,6 +593,7 @@ __device__ __forceinline__ void pf_tile(PfRows<D> &st, uint32_t tile, const PfLa
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int j = 0; j < DB; ++j) st.acc[j] = mfma32(va[j][kb], pb[kb], st.acc[j]);
+  return sn;
 }
 
 // This wave's quarter of the direct-to-LDS loads of a tile: wave w issues loads
@@ -628,7 +642,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const PfAttn P) {
   using C = PfCfg<D>;
   constexpr int S = kPfStages;
   constexpr int IPW = PfDma<D>::N;
-  static_assert((S - 2) * IPW <= 63, "loads in flight per wave");
+  static_assert(S >= 3 && (S - 2) * IPW <= 63, "tiles t and t + 1 resident; loads in flight per wave");
   __shared__ __align__(1024) unsigned char ring[S][C::TILE];
   const int b = blockIdx.x;
   const int item = (b % 8) * (P.items / 8) + b / 8;
@@ -676,27 +690,33 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const PfAttn P) {
   st.m = -INFINITY;
   st.l = 0.0f;
   const uint32_t ring0 = lds_addr(ring[0]);
+  // Tile t's softmax and value product run in iteration t together with tile t + 1's
+  // scores, so tiles t and t + 1 are in LDS during it; the iteration's barrier frees the
+  // stage of tile t - 1 for tile t + S - 1.  The last iteration scores a stale stage and
+  // drops the result.
+  floatx16 sc = pf_scores<D>(st, ring0, ofs);
   int stage = 0;
   for (int tt = 0; tt < ntiles; ++tt) {
     if (tt > 0) {
-      const int ahead = min(S - 2, ntiles - 1 - tt);
-      if (ahead >= 2) {
-        wait_vm<2 * IPW>();
-      } else if (ahead == 1) {
+      // tiles up to min(tt + S - 2, ntiles - 1) are issued; wait for tile tt + 1
+      const int ahead = min(S - 3, ntiles - 2 - tt);
+      if (ahead >= 1) {
         wait_vm<IPW>();
-      } else {
+      } else if (ahead == 0) {
         wait_vm<0>();
       }
-      bare_barrier();  // tile tt landed for every wave; tile tt - 1 is no longer read
+      bare_barrier();  // tile tt + 1 landed for every wave; tile tt - 1 is no longer read
     }
     if (tt + S - 1 < ntiles)
       dma.issue(ring[stage == 0 ? S - 1 : stage - 1], kres, vres, k0 + static_cast<int64_t>(tt + S - 1) * kKvTile);
+    const int nstage = stage == S - 1 ? 0 : stage + 1;
     const int64_t tb = k0 + static_cast<int64_t>(tt) * kKvTile;
+    const uint32_t tk = ring0 + nstage * C::TILE, tv = ring0 + stage * C::TILE;
     if (tb + kKvTile - 1 > pos_min)
-      pf_tile<D, true>(st, ring0 + stage * C::TILE, ofs, tb, pos, P.c2);
+      sc = pf_step<D, true>(st, sc, tk, tv, ofs, tb, pos, P.c2);
     else
-      pf_tile<D, false>(st, ring0 + stage * C::TILE, ofs, tb, pos, P.c2);
-    stage = stage == S - 1 ? 0 : stage + 1;
+      sc = pf_step<D, false>(st, sc, tk, tv, ofs, tb, pos, P.c2);
+    stage = nstage;
   }
   // ---- out: lane l holds row r0 + l % 32, columns 32 j + 8 b + 4 (l / 32) + e
   if (r0 + (lane & 31) >= M) return;
