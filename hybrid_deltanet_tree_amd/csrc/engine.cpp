@@ -44,7 +44,7 @@ struct Scratch {
   void *a_pend = nullptr;     // [n_gdn][max_nodes][hv] copies of alpha (io dtype)
   float *part_acc = nullptr;  // float32 attention: partials [hkv][nsplit][rows][D]
   float *part_ml = nullptr;   // [hkv][nsplit][rows][2]
-  void *part_o = nullptr;     // bf16 attention: normalised fp16 partials [hkv][nsplit][rows][D]
+  void *part_o = nullptr;     // bf16 attention: normalised bf16 partials [hkv][nsplit][rows][D]
   float *carry_acc = nullptr; // bf16 attention: state of split n_full below tb0 [hkv][rows][D]
   float *carry_ml = nullptr;  // [hkv][rows][2]
   void *conv_out = nullptr;   // GDN conv: post-conv q | k | v of one layer [max_nodes][..] each

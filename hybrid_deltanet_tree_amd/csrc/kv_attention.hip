@@ -14,7 +14,7 @@
 //                   into a kKvStages-deep LDS ring (buffer_load ... lds), scores
 //                   S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16, and
 //                   an online softmax in base 2.  A split wholly below L leaves one
-//                   normalised fp16 partial per row; the tiles of split L / split
+//                   normalised bf16 partial per row; the tiles of split L / split
 //                   below tb0 = kKvTile * (L / kKvTile) leave their float32 state.
 //  kv_tree_kernel   one workgroup per (kv head, node, quarter of the output columns):
 //                   wave 0 continues that state through the tiles from tb0 to the
@@ -33,7 +33,7 @@
 //  - masked slots hold a finite row (the node's own) and get probability 0;
 //  - the running max moves only when a tile exceeds it by more than kLazyMax, a
 //    rule that depends on the row's scores alone;
-//  - every split but a row's last enters the fold as its normalised fp16 partial,
+//  - every split but a row's last enters the fold as its normalised bf16 partial,
 //    whichever kernel finished it.  The committed splits fold in chunks of
 //    kFoldChunk (the chunk's max, then weighted sums in ascending split order; the
 //    chunks merge in order), then the split finished in the tree pass if the node's
@@ -247,26 +247,17 @@ __device__ __forceinline__ void kv_tile(KvRows<D, NB, NDB> &st, uint32_t tile, c
       st.acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j], pb[b], st.acc[b][j], 0, 0, 0);
 }
 
-// Normalised partial of 4 columns: acc / l rounded to fp16, packed.
-__device__ __forceinline__ uint2 norm_half4(floatx4 acc, float inv_l) {
-  const _Float16 h0 = static_cast<_Float16>(acc[0] * inv_l);
-  const _Float16 h1 = static_cast<_Float16>(acc[1] * inv_l);
-  const _Float16 h2 = static_cast<_Float16>(acc[2] * inv_l);
-  const _Float16 h3 = static_cast<_Float16>(acc[3] * inv_l);
+// Normalised partial of 4 columns: acc / l rounded to bf16 (the float32 range, so any
+// finite value row stays finite), packed.
+__device__ __forceinline__ uint2 norm_part4(floatx4 acc, float inv_l) {
   uint2 r;
-  r.x = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h0)) |
-        (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
-  r.y = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h2)) |
-        (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h3)) << 16);
+  r.x = static_cast<uint32_t>(bf16_bits(acc[0] * inv_l)) | (static_cast<uint32_t>(bf16_bits(acc[1] * inv_l)) << 16);
+  r.y = static_cast<uint32_t>(bf16_bits(acc[2] * inv_l)) | (static_cast<uint32_t>(bf16_bits(acc[3] * inv_l)) << 16);
   return r;
 }
 
-__device__ __forceinline__ float half_lo(uint32_t w) {
-  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu)));
-}
-__device__ __forceinline__ float half_hi(uint32_t w) {
-  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
-}
+__device__ __forceinline__ float part_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float part_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // A producer wave's share (IPW wave-wide loads) of the direct-to-LDS loads of a tile
 // of one kv head, with NP producer waves.  Lane l of a wave-wide load lands at LDS
@@ -313,7 +304,7 @@ struct KvDma {
 
 // ============================================================================ split pass
 
-// Byte offset of (row, column) in the fp16 partials of (kv head h, split s): rows
+// Byte offset of (row, column) in the bf16 partials of (kv head h, split s): rows
 // of D values, so that the fold reads 16 contiguous bytes per 8 columns.
 template <int D>
 __device__ __forceinline__ int64_t part_off(const KvTree &T, int h, int s, int row, int col) {
@@ -424,7 +415,7 @@ __global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
     stage = stage == S - 1 ? 0 : stage + 1;
   }
   // ---- epilogue.  The partials go out as whole rows: each wave writes its block's
-  // normalised fp16 values into its own padded region of the (now idle) ring, then
+  // normalised bf16 values into its own padded region of the (now idle) ring, then
   // stores them back 16 contiguous bytes per lane, two rows per wave-wide store.
   constexpr int SROW = C::ROWB + 16;  // padded row: the 16 rows of a column group hit distinct banks
   static_assert(CW * 16 * SROW <= S * C::TILE, "staging area");
@@ -439,7 +430,7 @@ __global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
       const float inv_l = 1.0f / st.l[k];
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
-        *reinterpret_cast<uint2 *>(stage_w + ln * SROW + (16 * db + 4 * g) * 2) = norm_half4(st.acc[k][db], inv_l);
+        *reinterpret_cast<uint2 *>(stage_w + ln * SROW + (16 * db + 4 * g) * 2) = norm_part4(st.acc[k][db], inv_l);
       if (g == 0 && row < M) {
         const int64_t prow = (static_cast<int64_t>(h) * T.nsplit_cap + s) * T.rows_cap + row;
         *reinterpret_cast<float2 *>(T.part_ml + prow * 2) = make_float2(st.m[k], st.l[k]);
@@ -518,7 +509,7 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
   constexpr int MAX_TILES = 3;  // (kKvTile - 1 + kMaxNodes - 1) / kKvTile + 1
   static_assert((kKvTile - 1 + kMaxNodes - 1) / kKvTile + 1 <= MAX_TILES, "tree tiles");
   __shared__ __align__(1024) unsigned char tiles[MAX_TILES][C::TILE];
-  __shared__ __align__(16) float x_o[16][QD];   // finished split n_full (crossing), fp16 values
+  __shared__ __align__(16) float x_o[16][QD];   // finished split n_full (crossing), bf16 values
   __shared__ float x_ml[16][2];
   __shared__ __align__(16) float f_acc[16][QD];  // the row's last split, float32 state
   __shared__ float f_ml[16][2];
@@ -638,12 +629,12 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
           const float inv_l = 1.0f / st.l[0];
 #pragma unroll
           for (int j = 0; j < QDB; ++j) {
-            const uint2 hv = norm_half4(st.acc[0][j], inv_l);
+            const uint2 hv = norm_part4(st.acc[0][j], inv_l);
             float *dst = &x_o[ln][16 * j + 4 * g];
-            dst[0] = half_lo(hv.x);
-            dst[1] = half_hi(hv.x);
-            dst[2] = half_lo(hv.y);
-            dst[3] = half_hi(hv.y);
+            dst[0] = part_lo(hv.x);
+            dst[1] = part_hi(hv.x);
+            dst[2] = part_lo(hv.y);
+            dst[3] = part_hi(hv.y);
           }
           if (g == 0) {
             x_ml[ln][0] = st.m[0];
@@ -726,14 +717,14 @@ __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) o[e] = x_o[r][8 * co + e];
         } else {
-          o[0] = half_lo(ov[j].x);
-          o[1] = half_hi(ov[j].x);
-          o[2] = half_lo(ov[j].y);
-          o[3] = half_hi(ov[j].y);
-          o[4] = half_lo(ov[j].z);
-          o[5] = half_hi(ov[j].z);
-          o[6] = half_lo(ov[j].w);
-          o[7] = half_hi(ov[j].w);
+          o[0] = part_lo(ov[j].x);
+          o[1] = part_hi(ov[j].x);
+          o[2] = part_lo(ov[j].y);
+          o[3] = part_hi(ov[j].y);
+          o[4] = part_lo(ov[j].z);
+          o[5] = part_hi(ov[j].z);
+          o[6] = part_lo(ov[j].w);
+          o[7] = part_hi(ov[j].w);
         }
         ch.l = ch.l + w;
 #pragma unroll

@@ -130,7 +130,7 @@ struct AttnLaunch {
 // split sizes; each launch pair then covers one group of nodes that share a split
 // size (`nodes`, `gn`), and a second pair covers the rest.  The split pass
 // (kv_split_kernel) streams every split wholly below L for all (node, q head) rows
-// of the group's nodes of a kv head and writes one normalised fp16 partial per
+// of the group's nodes of a kv head and writes one normalised bf16 partial per
 // (row, split); it also runs the tiles of split n_full = L / split that lie below
 // tb0 = kKvTile * (L / kKvTile) and leaves their float32 running state (the carry).
 // The tree pass (kv_tree_kernel) takes one (kv head, node, column quarter): it
@@ -142,7 +142,7 @@ struct KvTree {
   const void *kt, *vt;                    // tree rows [n][hkv][D]
   void *kc, *vc;                          // cache of this layer [hkv][cap][D]
   void *o;                                // [n][hq][D]
-  void *part_o;                           // fp16 [hkv][nsplit_cap][rows_cap][D]
+  void *part_o;                           // bf16 [hkv][nsplit_cap][rows_cap][D]
   float *part_ml;                         // [hkv][nsplit_cap][rows_cap][2]: max (base 2), sum
   float *carry_acc;                       // [hkv][rows_cap][D]
   float *carry_ml;                        // [hkv][rows_cap][2]

@@ -297,13 +297,14 @@ def attn_inputs(w: Workload, seed: int, slot: int, layer: int, n: int, tag: str 
 
 
 def kv_rows(w: Workload, seed: int, slot: int, layer: int, head: int, row0: int, rows: int,
-            sharp: bool = False):
-    """Resident cache rows [row0, row0+rows) of one kv head: K (unit rows), V (normal)."""
+            sharp: bool = False, v_scale: float = 1.0):
+    """Resident cache rows [row0, row0+rows) of one kv head: K (unit rows), V (normal, times
+    v_scale: a parity-only variant whose values pass the fp16 range)."""
     base = f"{w.name}/s{slot}/l{layer}/h{head}"
     K = fill(seed, base + "/K", NORMAL if sharp else NORMAL_L2, (row0 + rows, w.attn_d),
              dtype=w.dtype, row0=row0, rows=rows)
     V = fill(seed, base + "/V", NORMAL, (row0 + rows, w.attn_d), dtype=w.dtype, row0=row0,
-             rows=rows)
+             rows=rows, scale=v_scale)
     return K, V
 
 

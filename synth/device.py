@@ -54,7 +54,8 @@ class Instance:
 
     def __init__(self, w: synth.Workload, seed: int, *, device="cuda", lengths=None,
                  trees=None, n_nodes=None, capacity=None, sharp=False, poison=False,
-                 keep_host=True, tag="verify", q_scale=1.0, v_scale=1.0, host_layers=None):
+                 keep_host=True, tag="verify", q_scale=1.0, v_scale=1.0, host_layers=None,
+                 kv_v_scale=1.0):
         torch = _torch()
         self.w, self.seed, self.device, self.sharp = w, seed, device, sharp
         self.q_scale, self.v_scale = q_scale, v_scale
@@ -117,7 +118,7 @@ class Instance:
                     hK = np.zeros((w.attn_hkv, cap, w.attn_d), np.uint16 if dt == "bf16" else np.float32)
                     hV = np.zeros_like(hK)
                 for h in range(w.attn_hkv):
-                    K, V = synth.kv_rows(w, seed, s, l, h, 0, L, sharp=sharp)
+                    K, V = synth.kv_rows(w, seed, s, l, h, 0, L, sharp=sharp, v_scale=kv_v_scale)
                     if L > 0:
                         kc[ai, h, :L] = to_device(K, dt, device)
                         vc[ai, h, :L] = to_device(V, dt, device)

@@ -96,6 +96,19 @@ def test_forward_matches_oracle_sharp_softmax():
         gu.check_layer(inst, 0, l, got[l])
 
 
+def test_resident_values_past_the_fp16_range():
+    # resident V of magnitude ~2^20 (split averages past 65,504) over many splits: the partials keep
+    # the float32 range, so every output is finite and matches the oracle
+    inst = Instance(MINI, SEED, lengths=[6000], kv_v_scale=1048576.0)
+    eng = inst.engine()
+    assert eng.split_size(0, 6000) < 6000  # several committed splits per row
+    run_verify(inst, eng)
+    got = gu.outputs(inst, 0)
+    for l in range(4):
+        assert np.isfinite(got[l]).all(), f"layer {l}"
+        gu.check_layer(inst, 0, l, got[l])
+
+
 @pytest.mark.parametrize("wname,L", [("tiny", 256), ("mini", 1000)])
 def test_commit_matches_oracle(wname, L):
     w = MINI if wname == "mini" else W[wname]
