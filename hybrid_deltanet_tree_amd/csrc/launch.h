@@ -237,7 +237,7 @@ static_assert(sizeof(SnapshotHeader) == 64, "eight 64-bit words");
 // the span's own rows were copied into it.
 constexpr int kWyChunk = 64;
 constexpr int kPfRows = 128;   // prefill attention: query rows per workgroup (4 waves x 32)
-constexpr int kPfStages = 4;   // prefill attention: LDS tile ring
+constexpr int kPfStages = 5;   // prefill attention: LDS tile ring
 
 struct WyPrep {
   const void *q, *k, *v, *alpha, *beta;  // span rows of this layer (bf16)

@@ -455,9 +455,14 @@ struct PfCfg {
   static_assert(D == 256 && kKvTile == 32, "tile shape");
 };
 
-// XOR swizzle of the 16-byte chunks of tile row `row`: the score operand reads (32 keys
-// at one chunk) and the transposed value reads (4 keys at two chunks) hit distinct banks.
-__device__ __forceinline__ int pf_swz(int row) { return (2 * row) & 31; }
+// XOR swizzle of the 16-byte chunks of tile row `row`.  gfx950's LDS serves a
+// ds_read_b128 32 lanes (512 bytes, every bank once) at a time, so a read is free of bank
+// conflicts when its 32 lanes hit distinct 16-byte units modulo 32.  The score operand
+// reads take 32 rows at one chunk, so the swizzle is a bijection of the 32 rows; a
+// transposed value read takes rows 8 s .. 8 s + 7 at four consecutive chunks, so the low
+// three row bits move the chunk's upper bits and the next two its lower ones.  The
+// swizzle repeats every 32 rows: 16 rows further, chunk bit 1 flips.
+__device__ __forceinline__ int pf_swz(int row) { return ((row & 7) << 2) | ((row >> 3) & 3); }
 template <int D>
 __device__ __forceinline__ int pf_off(int row, int c) {
   return row * PfCfg<D>::ROWB + ((c ^ pf_swz(row)) << 4);
@@ -476,7 +481,7 @@ struct PfRows {
 // Tile-invariant LDS offsets of this lane's operand reads: ko[kk] the score operand
 // (key row l % 32, d chunk 2 kk + l / 32); vo[j][r] the transposed value reads of
 // column block j for keys 4 h + e (r = 0) and 8 + 4 h + e (r = 1) of the first 16 keys
-// (the second 16 sit 16 rows further).  In each 16-lane group lane p addresses row
+// (the second 16 sit 16 rows further, at the offset with bit 5 flipped: pf_swz).  In each 16-lane group lane p addresses row
 // 4 h + p / 4 (+ 8 r) at columns 32 j + 16 ((l / 16) % 2) + 4 (p % 4), so the group's
 // transposed read gives lane p column 32 j + 16 ((l / 16) % 2) + p of the four rows.
 template <int D>
@@ -504,8 +509,9 @@ struct PfLane {
 constexpr float kPfLazy = 8.0f;
 
 // Scores S^T = K Q^T of one tile (its K half at `tile`) for this wave's 32 rows.
-// Register r holds key 8 (r / 4) + 4 (l / 32) + r % 4 of the lane's row.  Even and odd
-// k-steps accumulate in two independent chains.
+// Register r holds key 8 (r / 4) + 4 (l / 32) + r % 4 of the lane's row.  One
+// accumulation chain: a dependent 32x32x16 MFMA issues about 8 cycles later than an
+// independent one, and a second chain would hold 16 more registers.
 template <int D>
 __device__ __forceinline__ floatx16 pf_scores(const PfRows<D> &st, uint32_t tile, const PfLane<D> &ofs) {
   constexpr int KQ = PfCfg<D>::KQ;
@@ -513,15 +519,10 @@ __device__ __forceinline__ floatx16 pf_scores(const PfRows<D> &st, uint32_t tile
   bf16x8 ka[KQ];
 #pragma unroll
   for (int kk = 0; kk < KQ; ++kk) ka[kk] = *(lds_b8)(lds_ptr(tile + ofs.ko[kk]));
-  floatx16 s0 = floatx16{}, s1 = floatx16{};
+  floatx16 sc = floatx16{};
 #pragma unroll
-  for (int kk = 0; kk < KQ; ++kk) {
-    if (kk & 1)
-      s1 = mfma32(ka[kk], st.q[kk], s1);
-    else
-      s0 = mfma32(ka[kk], st.q[kk], s0);
-  }
-  return s0 + s1;
+  for (int kk = 0; kk < KQ; ++kk) sc = mfma32(ka[kk], st.q[kk], sc);
+  return sc;
 }
 
 // One step of the pipelined tile loop: the online softmax of tile t's scores `s`
@@ -543,8 +544,10 @@ __device__ __forceinline__ floatx16 pf_step(PfRows<D> &st, const floatx16 &s, ui
   for (int j = 0; j < DB; ++j)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const shortx4 lo = ds_read_tr_at(tv + ofs.vo[j][0] + kb * KB16);
-      const shortx4 hi = ds_read_tr_at(tv + ofs.vo[j][1] + kb * KB16);
+      // the stage base is 32 KiB aligned, so flipping bit 5 of the sum flips it in the
+      // offset; taken per tile, it costs no register across the loop
+      const shortx4 lo = ds_read_tr_at(kb ? ((tv + ofs.vo[j][0]) ^ 32u) + KB16 : tv + ofs.vo[j][0]);
+      const shortx4 hi = ds_read_tr_at(kb ? ((tv + ofs.vo[j][1]) ^ 32u) + KB16 : tv + ofs.vo[j][1]);
       va[j][kb] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
                                                  lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
     }
@@ -700,7 +703,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const PfAttn P) {
     if (tt > 0) {
       // tiles up to min(tt + S - 2, ntiles - 1) are issued; wait for tile tt + 1
       const int ahead = min(S - 3, ntiles - 2 - tt);
-      if (ahead >= 1) {
+      static_assert(S <= 5, "at most two tiles ahead of the one waited for");
+      if (ahead >= 2) {
+        wait_vm<2 * IPW>();
+      } else if (ahead == 1) {
         wait_vm<IPW>();
       } else if (ahead == 0) {
         wait_vm<0>();
