@@ -136,6 +136,23 @@ __device__ __forceinline__ void colsum2(float &a, float &b) {
   }
 }
 
+// Sum over the N consecutive lanes (8, 16 or 32) that hold one node's chunks: the first
+// 3 or 4 butterfly stages of a DPP row, joined across two rows for 32.  Every lane of the
+// group gets the same bits.
+template <int N>
+__device__ __forceinline__ float groupsum(float x) {
+  static_assert(N == 8 || N == 16 || N == 32, "lanes per node");
+  x = x + dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = x + dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = x + dpp<0x141>(x);  // row_half_mirror
+  if constexpr (N >= 16) x = x + dpp<0x140>(x);  // row_mirror
+  if constexpr (N == 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return x;
+}
+
 // One node's operands, in the registers of a lane: its key rows and s*q rows,
 // {alpha, beta, k . s q, parent} and the value of the lane's column.
 template <int R>
@@ -238,24 +255,31 @@ __global__ __launch_bounds__(gdn_threads(DK)) void gdn_tree_kernel(const GdnLaun
       x = dep[nm + x];
     }
   }
+  // k . s q of every node (it does not depend on the state), taken here: a node's CPR
+  // chunks sit on CPR consecutive lanes, so an in-lane dot and a CPR-lane sum give it
   const bool keep_k = (cg == 0) && (h % ratio == 0);
 #pragma unroll
   for (int x = 0; x < MAXC; ++x) {
     const int c = tid + x * NT;
+    const int i = c / CPR, cc = c % CPR;
+    float kq = 0.0f;
     if (c < nch) {
-      const int i = c / CPR, cc = c % CPR;
       float kv[EPC], qv[EPC];
       unpack16<BF>(kc[x], kv);
       unpack16<BF>(qc[x], qv);
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
+        qv[e] = P.scale * qv[e];
         kf[i * DK + cc * EPC + e] = kv[e];
-        qs[i * DK + cc * EPC + e] = P.scale * qv[e];
+        qs[i * DK + cc * EPC + e] = qv[e];
       }
+      kq = lane_dot<EPC>(kv, qv);
       if (keep_k)  // commit replays the accepted path with these exact k bits
         *reinterpret_cast<uint4 *>(static_cast<unsigned char *>(T.k_pend) +
                                    (static_cast<int64_t>(i) * P.hk + qh) * DK * ESZ + cc * 16) = kc[x];
     }
+    kq = groupsum<CPR>(kq);  // every lane takes part: the lanes past the nodes add zeros
+    if (c < nch && cc == 0) nsc[i].z = kq;
   }
   if (tid < n * VCH) {
     const int i = tid / VCH, cc = tid % VCH;
@@ -273,20 +297,10 @@ __global__ __launch_bounds__(gdn_threads(DK)) void gdn_tree_kernel(const GdnLaun
       a = araw;
       b = braw;
     }
-    nsc[tid] = make_float4(a, b, 0.0f, __int_as_float((par_i & 0xFF) | ((save_i & 0xFF) << 8)));
+    nsc[tid].x = a;  // .z, k . s q, is written by the staging above
+    nsc[tid].y = b;
+    nsc[tid].w = __int_as_float((par_i & 0xFF) | ((save_i & 0xFF) << 8));
     if (cg == 0) static_cast<io_t<BF> *>(T.a_pend)[static_cast<int64_t>(tid) * P.hv + h] = araw;
-  }
-  __syncthreads();
-  // ---- k . s q of every node (it does not depend on the state), one 16-lane row
-  // per node with the walk's own dot product and reduction
-  for (int i0 = 0; i0 < n; i0 += NT / LPC) {
-    const int i = i0 + tid / LPC;
-    const int ii = min(i, n - 1);
-    float kk[R], qq[R];
-    lds_row<R>(kf + ii * DK + g * R, kk);
-    lds_row<R>(qs + ii * DK + g * R, qq);
-    const float d = colsum<LPC>(lane_dot<R>(kk, qq));
-    if (i < n && g == 0) nsc[i].z = d;
   }
   __syncthreads();
 
