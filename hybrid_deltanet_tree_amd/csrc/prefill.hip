@@ -361,10 +361,9 @@ __global__ __launch_bounds__(256) void gdn_wy_scan_kernel(const WyScan P) {
   floatx4 s[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) s[rb] = *reinterpret_cast<const floatx4 *>(st + DK / 4 * wave + 16 * rb + 4 * qd);
-  WyOps<DK> cur, nxt;
-  wy_load<DK, DV>(cur, P, 0, h, gk, c0);
-  for (int ch = 0; ch < P.n_chunks; ++ch) {
-    if (ch + 1 < P.n_chunks) wy_load<DK, DV>(nxt, P, ch + 1, h, gk, c0);
+  // one chunk with the operands `cur`; the next chunk's operands load into the other
+  // set meanwhile (two sets used in turn: no register copy waits for a load)
+  auto step = [&](const WyOps<DK> &cur, int ch) {
     const int t0 = max(0, C * ch - P.off), n = min(P.T, C * (ch + 1) - P.off) - t0;
     // ---- publish S as [column][dim] bf16 pairs
 #pragma unroll
@@ -434,7 +433,15 @@ __global__ __launch_bounds__(256) void gdn_wy_scan_kernel(const WyScan P) {
       }
       s[rb] = a;
     }
-    cur = nxt;
+  };
+  WyOps<DK> opa, opb;
+  wy_load<DK, DV>(opa, P, 0, h, gk, c0);
+  for (int ch = 0; ch < P.n_chunks; ch += 2) {
+    if (ch + 1 < P.n_chunks) wy_load<DK, DV>(opb, P, ch + 1, h, gk, c0);
+    step(opa, ch);
+    if (ch + 1 >= P.n_chunks) break;
+    if (ch + 2 < P.n_chunks) wy_load<DK, DV>(opa, P, ch + 2, h, gk, c0);
+    step(opb, ch + 1);
   }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) *reinterpret_cast<floatx4 *>(st + DK / 4 * wave + 16 * rb + 4 * qd) = s[rb];
