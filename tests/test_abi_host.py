@@ -162,6 +162,41 @@ def test_span_and_anchor_rejections_on_the_host():
     e.close()
 
 
+def test_chunked_prefill_rejections_on_the_host():
+    """forward_chunked refuses bad arguments and the shapes it does not run before anything
+    touches the device, and a refused call changes nothing."""
+    ok = dict(gdn_dk=128, gdn_dv=128, attn_hq=12, attn_hkv=2, attn_d=256)
+    e = make_engine(**ok)
+    layers = fake_layers()
+    for args, status in (((0, 0, layers), -1), ((7, 4, layers), -1), ((1, 6, layers), -4)):
+        with pytest.raises(hdt.HdtError) as err:
+            e.forward_chunked(*args)
+        assert err.value.status == status
+    bad = [dict(l) for l in layers]
+    bad[0]["v"] = FAKE + 8  # 16-byte alignment
+    with pytest.raises(hdt.HdtError) as err:
+        e.forward_chunked(0, 4, bad)
+    assert err.value.status == -1
+    no_gates = [dict(l) for l in layers]
+    no_gates[1]["alpha"] = None
+    with pytest.raises(hdt.HdtError) as err:
+        e.forward_chunked(0, 4, no_gates)
+    assert err.value.status == -1
+    assert e.kv_length(0) == 100 and e.kv_length(1) == 295
+    e.close()
+    conv_slot = dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=1000, length=100,
+                     conv_state=FAKE)
+    for kw in (dict(ok, gdn_dk=64, gdn_dv=64), dict(ok, attn_hq=4, attn_d=64),
+               dict(ok, io_dtype=hdt.HDT_F32, attn_hq=4, attn_d=64),
+               dict(ok, gdn_conv=4, gdn_conv_weight=FAKE, slots=[conv_slot])):
+        e = make_engine(**kw)
+        with pytest.raises(hdt.HdtError) as err:
+            e.forward_chunked(0, 4, layers)
+        assert err.value.status == -7, kw
+        assert e.kv_length(0) == 100
+        e.close()
+
+
 def fake_layers(n_layers=4):
     return [dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, o=FAKE) for _ in range(n_layers)]
 
@@ -284,6 +319,8 @@ def test_io_list_must_have_one_entry_per_layer():
             e.forward_block(0, 2, layers)
         with pytest.raises(ValueError):
             e.forward_span(0, 2, layers)
+        with pytest.raises(ValueError):
+            e.forward_chunked(0, 2, layers)
     assert e.kv_length(0) == 100
     e.close()
 
