@@ -50,6 +50,41 @@ __device__ __forceinline__ floatx16 mfma32(const bf16x8 &a, const bf16x8 &b, con
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// acc *= c for an accumulator the matrix cores keep in AGPRs.  The value passes through
+// a VGPR eight registers at a time inside one asm block, so the compiler keeps the
+// accumulator where the MFMAs want it instead of copying all of it to VGPRs on every
+// tile in case the (rare) rescale runs.  Each read, multiply and write is eight
+// instructions from the one it depends on.
+__device__ __forceinline__ void scale_agpr8(float &x0, float &x1, float &x2, float &x3, float &x4, float &x5,
+                                            float &x6, float &x7, float c) {
+  float t0, t1, t2, t3, t4, t5, t6, t7;
+  asm volatile(
+      "v_accvgpr_read_b32 %8, %0\n\tv_accvgpr_read_b32 %9, %1\n\t"
+      "v_accvgpr_read_b32 %10, %2\n\tv_accvgpr_read_b32 %11, %3\n\t"
+      "v_accvgpr_read_b32 %12, %4\n\tv_accvgpr_read_b32 %13, %5\n\t"
+      "v_accvgpr_read_b32 %14, %6\n\tv_accvgpr_read_b32 %15, %7\n\t"
+      "v_mul_f32 %8, %16, %8\n\tv_mul_f32 %9, %16, %9\n\t"
+      "v_mul_f32 %10, %16, %10\n\tv_mul_f32 %11, %16, %11\n\t"
+      "v_mul_f32 %12, %16, %12\n\tv_mul_f32 %13, %16, %13\n\t"
+      "v_mul_f32 %14, %16, %14\n\tv_mul_f32 %15, %16, %15\n\t"
+      "v_accvgpr_write_b32 %0, %8\n\tv_accvgpr_write_b32 %1, %9\n\t"
+      "v_accvgpr_write_b32 %2, %10\n\tv_accvgpr_write_b32 %3, %11\n\t"
+      "v_accvgpr_write_b32 %4, %12\n\tv_accvgpr_write_b32 %5, %13\n\t"
+      "v_accvgpr_write_b32 %6, %14\n\tv_accvgpr_write_b32 %7, %15"
+      : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3), "+a"(x4), "+a"(x5), "+a"(x6), "+a"(x7),
+        "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
+      : "v"(c));
+}
+__device__ __forceinline__ void scale_acc(floatx16 &a, float c) {
+  float x[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) x[e] = a[e];
+  scale_agpr8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7], c);
+  scale_agpr8(x[8], x[9], x[10], x[11], x[12], x[13], x[14], x[15], c);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) a[e] = x[e];
+}
+
 // A float32 value as the sum of two bf16 values (hi = x rounded, lo = the rest rounded):
 // products of two such pairs keep the three larger partial products, so a bf16 matrix
 // core multiplies float32 operands to about 2^-16 relative.
@@ -597,7 +632,7 @@ __device__ __forceinline__ floatx16 pf_step(PfRows<D> &st, const floatx16 &s, ui
   }
   if (__any(corr != 1.0f)) {
 #pragma unroll
-    for (int j = 0; j < DB; ++j) st.acc[j] = st.acc[j] * corr;
+    for (int j = 0; j < DB; ++j) scale_acc(st.acc[j], corr);
   }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
