@@ -115,6 +115,53 @@ def test_chunked_two_pieces():
     eng.close()
 
 
+def _moves(scores, keys, tile=32, lazy=8.0):
+    """How often a tile's max exceeds the running max by more than `lazy` within the first
+    `keys` keys (the rule under which the running max moves after the first tile)."""
+    count, run = 0, -np.inf
+    for t0 in range(0, keys, tile):
+        mt = scores[t0:t0 + tile].max()
+        if run > -np.inf and mt > run + lazy:
+            count += 1
+        if mt > run + lazy or run == -np.inf:
+            run = mt
+    return count
+
+
+def test_chunked_peaked_softmax():
+    """Unnormalised keys and queries drawn as 12 N(0,1): scores spread over tens of units, so
+    the running max of a row moves after its first tile and the accumulators are rescaled in
+    the tile loop.  With at most four key splits and L + T >= 1,024 every split holds at least
+    256 keys, so moves within the first 256 keys happen inside the first split."""
+    L, T = 2000, 200
+    _say(f"chunked prefill, peaked softmax: {T} tokens at {L}")
+    inst = Instance(SPAN, SEED, lengths=[L], capacity=[L + T + 64], sharp=True, q_scale=12.0)
+    eng = inst.engine()
+    host, dev = span_inputs(inst, T, sharp=True, q_scale=12.0)
+    w = inst.w
+    l = 1  # the first attention layer
+    h = host[l]
+    G = w.attn_hq // w.attn_hkv
+    moves = 0
+    for t in (0, T - 1):
+        for j in (0, w.attn_hq - 1):
+            q = _f32(h["q"][t, j]).astype(np.float64)
+            K = _f32(inst.h_kc[0][0][j // G, :L]).astype(np.float64)
+            moves += _moves((K @ q) * (1.0 / np.sqrt(w.attn_d)) / np.log(2.0), 256)
+    assert moves > 0, "the inputs never move the running max after the first tile"
+    _say(f"  running-max moves in the first 256 keys (4 sampled rows, from the inputs): {moves}")
+    eng.forward_chunked(0, T, dev, gu.stream())
+    gu.sync()
+    got = _f32(to_host(dev[l]["o"], w.dtype))
+    Kf = inst.h_kc[0][0].copy()
+    Vf = inst.h_vc[0][0].copy()
+    Kf[:, L:L + T] = np.transpose(h["k"], (1, 0, 2))
+    Vf[:, L:L + T] = np.transpose(h["v"], (1, 0, 2))
+    worst = _check_attn_rows(got, h, Kf, Vf, L, [0, 1, 63, 64, 127, 150, T - 1], range(w.attn_hq))
+    _say(f"  attention (7 tokens x {w.attn_hq} heads): {worst:.2e}")
+    eng.close()
+
+
 def test_chunked_anchors_and_rollback():
     L, T, every = 300, 300, 128  # anchors at 384 and 512
     inst = Instance(SPAN, SEED, lengths=[L], capacity=[L + T + 64])

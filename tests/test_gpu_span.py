@@ -32,8 +32,9 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def span_inputs(inst, T, tag="span"):
-    """Per-layer host arrays and device tensors holding T rows."""
+def span_inputs(inst, T, tag="span", sharp=False, q_scale=1.0):
+    """Per-layer host arrays and device tensors holding T rows (attention q and k drawn as
+    for Instance(sharp=..., q_scale=...))."""
     w = inst.w
     host, dev = [], []
     for l, kind in enumerate(w.layer_kind):
@@ -43,7 +44,7 @@ def span_inputs(inst, T, tag="span"):
             h = dict(q=q, k=k, v=v, alpha=a, beta=b)
             oshape = (T, w.gdn_hv, w.gdn_dv)
         else:
-            q, k, v = synth.attn_inputs(w, SEED, 0, l, T, tag)
+            q, k, v = synth.attn_inputs(w, SEED, 0, l, T, tag, sharp=sharp, q_scale=q_scale)
             h = dict(q=q, k=k, v=v)
             oshape = (T, w.attn_hq, w.attn_d)
         d = {name: to_device(a, w.dtype, "cuda") for name, a in h.items()}
