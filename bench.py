@@ -247,7 +247,7 @@ def prefill_bench(args):
         run(0, T, layers, stream.cuda_stream)
         b.record(stream)
     torch.cuda.synchronize()
-    kinds = ((6, "wy_prep"), (7, "wy_scan"), (8, "attn_prefill"), (9, "attn_prefill_fold")) if chunked else \
+    kinds = ((4, "gdn_conv"), (6, "wy_prep"), (7, "wy_scan"), (8, "attn_prefill"), (9, "attn_prefill_fold")) if chunked else \
         ((0, "gdn_tree"), (1, "attn_split"), (2, "attn_tree"), (3, "commit"), (4, "gdn_conv"))
     prof = {k: eng.profile_read(k) for k, _ in kinds}
     eng.profile(False)

@@ -107,6 +107,7 @@ struct hdt_engine {
   struct {
     uint16_t *w_hi = nullptr, *w_lo = nullptr, *mq_hi = nullptr, *mq_lo = nullptr, *kt = nullptr, *qc = nullptr;
     float *ut = nullptr, *g = nullptr, *part_acc = nullptr, *part_ml = nullptr;
+    void *conv = nullptr;  // post-conv q, k, v of a piece (models with the short conv)
     bool allocated = false;
   } pf;
 };
@@ -316,7 +317,7 @@ void free_scratch(hdt_engine *e) {
   e->walk_m = nullptr;
   e->allocated = false;
   void *pf[] = {e->pf.w_hi, e->pf.w_lo, e->pf.mq_hi, e->pf.mq_lo, e->pf.kt, e->pf.qc,
-                e->pf.ut, e->pf.g, e->pf.part_acc, e->pf.part_ml};
+                e->pf.ut, e->pf.g, e->pf.part_acc, e->pf.part_ml, e->pf.conv};
   for (void *p : pf) (void)hipFree(p);
   e->pf = {};
 }
@@ -1193,7 +1194,7 @@ namespace {
 
 // Sizes of the chunked-prefill scratch for one piece of kPfPiece tokens.
 struct PfSizes {
-  size_t w, mq, kq, ut, g, acc, ml;
+  size_t w, mq, kq, ut, g, acc, ml, conv;
 };
 PfSizes pf_sizes(const hdt_model_desc &m) {
   const size_t nch = kPfPiece / kWyChunk + 1, C = kWyChunk;
@@ -1204,6 +1205,9 @@ PfSizes pf_sizes(const hdt_model_desc &m) {
     z.kq = nch * m.gdn_hk * C * m.gdn_dk * 2;
     z.ut = nch * m.gdn_hv * C * m.gdn_dv * 4;
     z.g = nch * m.gdn_hv * 3 * C * 4;
+    if (m.gdn_conv > 0)
+      z.conv = static_cast<size_t>(kPfPiece) * (2 * m.gdn_hk * m.gdn_dk + m.gdn_hv * m.gdn_dv) *
+               (m.io_dtype == HDT_BF16 ? 2 : 4);
   }
   if (m.attn_hkv > 0) {
     const size_t G = m.attn_hq / m.attn_hkv;
@@ -1225,7 +1229,8 @@ hdt_status ensure_pf_alloc(hdt_engine *e) {
                {reinterpret_cast<void **>(&e->pf.kt), z.kq},    {reinterpret_cast<void **>(&e->pf.qc), z.kq},
                {reinterpret_cast<void **>(&e->pf.ut), z.ut},    {reinterpret_cast<void **>(&e->pf.g), z.g},
                {reinterpret_cast<void **>(&e->pf.part_acc), z.acc},
-               {reinterpret_cast<void **>(&e->pf.part_ml), z.ml}};
+               {reinterpret_cast<void **>(&e->pf.part_ml), z.ml},
+               {&e->pf.conv, z.conv}};
   for (auto &x : parts)
     if (x.n > 0 && hipMalloc(x.p, x.n) != hipSuccess) return fail(e, HDT_E_HIP, "hipMalloc of the prefill scratch failed");
   e->pf.allocated = true;
@@ -1248,6 +1253,35 @@ hdt_status chunked_piece(hdt_engine *e, SlotState &s, const hdt_layer_io *io, in
       a.q = static_cast<const char *>(x.q) + t * bqk;
       a.k = static_cast<const char *>(x.k) + t * bqk;
       a.v = static_cast<const char *>(x.v) + t * bv;
+      if (m.gdn_conv > 0) {
+        // the short conv over the piece after the layer's tail; the WY kernels read its
+        // output, and the tail rolls to the piece's last rows
+        PfConv c{};
+        c.q = a.q;
+        c.k = a.k;
+        c.v = a.v;
+        c.tail = static_cast<char *>(s.d.gdn_conv_state) +
+                 static_cast<size_t>(ki) * (m.gdn_conv - 1) * e->conv_C * z;
+        c.qo = e->pf.conv;
+        c.ko = static_cast<char *>(e->pf.conv) + static_cast<size_t>(p) * bqk;
+        c.vo = static_cast<char *>(e->pf.conv) + 2 * static_cast<size_t>(p) * bqk;
+        c.weight = m.gdn_conv_weight + static_cast<size_t>(ki) * e->conv_C * m.gdn_conv;
+        c.T = p;
+        c.width = m.gdn_conv;
+        c.hk = m.gdn_hk;
+        c.dk = m.gdn_dk;
+        c.hv = m.gdn_hv;
+        c.dv = m.gdn_dv;
+        c.eps = kConvEps;
+        {
+          ProfScope ps(e, 4);
+          if (launch_pf_conv(c, m.io_dtype == HDT_BF16, st, ps.events()) != hipSuccess)
+            return fail(e, HDT_E_HIP, "layer %d: span conv launch failed", l);
+        }
+        a.q = c.qo;
+        a.k = c.ko;
+        a.v = c.vo;
+      }
       a.alpha = static_cast<const char *>(x.alpha) + t * bg;
       a.beta = static_cast<const char *>(x.beta) + t * bg;
       a.T = p;
@@ -1351,8 +1385,6 @@ hdt_status hdt_forward_chunked(hdt_engine *e, int32_t slot, int32_t T, const hdt
   if (m.io_dtype != HDT_BF16) return fail(e, HDT_E_UNSUPPORTED, "the chunked prefill needs bf16 storage");
   if (e->n_gdn > 0 && (m.gdn_dk != 128 || m.gdn_dv != 128))
     return fail(e, HDT_E_UNSUPPORTED, "the chunked prefill needs GDN heads of 128 by 128");
-  if (e->n_gdn > 0 && m.gdn_conv > 0)
-    return fail(e, HDT_E_UNSUPPORTED, "the chunked prefill does not run the short conv: use hdt_forward_span");
   if (e->n_attn > 0 && m.attn_d != 256) return fail(e, HDT_E_UNSUPPORTED, "the chunked prefill needs attn_d = 256");
   if (settle(e, slot) != HDT_OK) return HDT_E_HIP;
   SlotState &s = e->slots[slot];

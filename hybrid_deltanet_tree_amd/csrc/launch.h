@@ -90,6 +90,18 @@ struct ConvLaunch {
   float eps;
 };
 
+// The conv over a prefill span of T tokens (rows [0, T) of q, k, v) after the slot's
+// tail, in front of the chunked GDN layer; then the tail is rolled to the span's last
+// width - 1 rows.
+struct PfConv {
+  const void *q, *k, *v;                 // pre-conv span rows [T][hk][dk], [T][hk][dk], [T][hv][dv]
+  void *tail;                            // this layer's tail [width-1][C], read, then rolled
+  void *qo, *ko, *vo;                    // post-conv rows, same layouts as the inputs
+  const float *weight;                   // this layer's taps [C][width]
+  int32_t T, width, hk, dk, hv, dv;
+  float eps;
+};
+
 // ---------------------------------------------------------------- attention split pass
 // Work items of one tree, in block order: first the tail items (kv head x group of
 // up to kAttnWaves nodes), which cover every position from the first split that is
@@ -300,6 +312,8 @@ hipError_t launch_kv_tree(const KvLaunch &a, int D, int max_items, hipStream_t s
 hipError_t launch_commit(const CommitLaunch &a, int dk, int bf16, int n_blocks, hipStream_t s,
                          KernelEvents ev);
 hipError_t launch_gdn_conv(const ConvLaunch &a, int bf16, hipStream_t s, KernelEvents ev);
+// pf_conv_kernel over the span, then (width > 1) pf_conv_tail_kernel rolls the tail.
+hipError_t launch_pf_conv(const PfConv &a, int bf16, hipStream_t s, KernelEvents ev);
 hipError_t launch_walk(const WalkLaunch &a, hipStream_t s, KernelEvents ev);
 hipError_t launch_snapshot_header(const SnapshotHeader &h, void *dst, hipStream_t s);
 hipError_t launch_wy_prep(const WyPrep &a, int dk, hipStream_t s, KernelEvents ev);

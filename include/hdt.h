@@ -240,16 +240,18 @@ hdt_status hdt_forward_span(hdt_engine *eng, int32_t slot, int32_t T, const hdt_
  * to end", 2.5 "The caches decide where the prefill starts": the prompt past the
  * resident prefix goes through the model once, with state anchors; "How ignis serves
  * a request", 3 "Prefill reads the prompt", in chunks).
- *  GDN layers: the chunked (WY) form of the same recurrence over chunks of 64 tokens
- *    anchored at absolute positions (a multiple of 64); the state between chunks and
- *    the final state are float32.
+ *  GDN layers: with gdn_conv > 0, the short causal conv over the span's q, k, v rows
+ *    after the layer's committed tail first (then the tail holds the span's last
+ *    gdn_conv - 1 pre-conv rows); then the chunked (WY) form of the same recurrence
+ *    over chunks of 64 tokens anchored at absolute positions (a multiple of 64); the
+ *    state between chunks and the final state are float32.
  *  Attention layers: the span's k/v rows are written into the cache at [L, L + T),
  *    then each row (token t, q head j) attends causally to cache rows 0 .. L + t.
  * The span is cut into pieces of at most 2048 tokens (and at anchor positions) that
  * each pass through every layer in order.  Outputs, rows and state equal the
  * token-by-token recurrence up to rounding (outputs within the io precision), not bit
  * for bit: hdt_forward_span is the bit-exact chain mode.  Needs bf16 storage, GDN
- * heads of 128 by 128 with gdn_conv = 0 and attn_d = 256 (else HDT_E_UNSUPPORTED);
+ * heads of 128 by 128 and attn_d = 256 (else HDT_E_UNSUPPORTED);
  * alpha in (0, 1].  Buffers 16-byte aligned.  The first call allocates the
  * library's prefill scratch (not under graph capture).  Needs no pending round;
  * length + T <= capacity.  length += T.

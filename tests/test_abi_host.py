@@ -184,11 +184,8 @@ def test_chunked_prefill_rejections_on_the_host():
     assert err.value.status == -1
     assert e.kv_length(0) == 100 and e.kv_length(1) == 295
     e.close()
-    conv_slot = dict(gdn_state=FAKE, k_cache=FAKE, v_cache=FAKE, capacity=1000, length=100,
-                     conv_state=FAKE)
     for kw in (dict(ok, gdn_dk=64, gdn_dv=64), dict(ok, attn_hq=4, attn_d=64),
-               dict(ok, io_dtype=hdt.HDT_F32, attn_hq=4, attn_d=64),
-               dict(ok, gdn_conv=4, gdn_conv_weight=FAKE, slots=[conv_slot])):
+               dict(ok, io_dtype=hdt.HDT_F32, attn_hq=4, attn_d=64)):
         e = make_engine(**kw)
         with pytest.raises(hdt.HdtError) as err:
             e.forward_chunked(0, 4, layers)

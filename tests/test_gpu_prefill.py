@@ -19,7 +19,7 @@ import synth
 from synth.device import Instance, to_device, to_host
 from tests import gpu_util as gu
 from tests.brute import rel_err
-from tests.test_gpu_span import SEED, SPAN, check_span_against_oracle, span_inputs
+from tests.test_gpu_span import SEED, SPAN, SPAN_CONV, check_span_against_oracle, span_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +48,76 @@ def test_chunked_matches_oracle(L, T):
     gu.sync()
     assert eng.kv_length(0) == L + T
     check_span_against_oracle(inst, host, dev, L, T)
+    eng.close()
+
+
+@pytest.mark.parametrize("L,T", [(300, 150), (300, 2), (256, 64)])
+def test_chunked_conv_matches_oracle(L, T):
+    """The short conv in front of each GDN layer: outputs and state against the oracle's conv
+    and recurrence, and the tail afterwards holds the last width - 1 pre-conv rows of (old
+    tail, span) bit for bit (with T = 2, one of them from the old tail)."""
+    w = SPAN_CONV
+    _say(f"chunked prefill with the short conv: {T} tokens at {L}")
+    inst = Instance(w, SEED, lengths=[L], capacity=[L + T + 64])
+    eng = inst.engine()
+    host, dev = span_inputs(inst, T)
+    eng.forward_chunked(0, T, dev, gu.stream())
+    gu.sync()
+    assert eng.kv_length(0) == L + T
+    check_span_against_oracle(inst, host, dev, L, T)
+    gi = 0
+    for l, kind in enumerate(w.layer_kind):
+        if kind != 0:
+            continue
+        h = host[l]
+        want = oracle.conv_tail_commit(inst.h_tail[0][gi], h["q"], h["k"], h["v"], list(range(T)))
+        assert np.array_equal(to_host(inst.tail[0][gi], w.dtype), want), f"layer {l} tail"
+        gi += 1
+    eng.close()
+
+
+def test_chunked_conv_anchors_and_rollback():
+    """Anchors of a conv model hold the oracle's state and the tail at their positions;
+    rollback to an anchor and forwarding the rest again gives the same bits."""
+    w = SPAN_CONV
+    L, T, every = 300, 300, 128  # anchors at 384 and 512
+    inst = Instance(w, SEED, lengths=[L], capacity=[L + T + 64])
+    eng = inst.engine()
+    n_max = 8
+    astate = torch.zeros((n_max,) + tuple(inst.state[0].shape), dtype=torch.float32, device="cuda")
+    aconv = torch.zeros((n_max,) + tuple(inst.tail[0].shape), dtype=inst.tail[0].dtype, device="cuda")
+    eng.set_anchors(0, every, n_max, astate, aconv)
+    host, dev = span_inputs(inst, T)
+    S0 = [x.copy() for x in inst.h_state[0]]
+    tail0 = [x.copy() for x in inst.h_tail[0]]
+    eng.forward_chunked(0, T, dev, gu.stream())
+    gu.sync()
+    first = [to_host(d["o"], w.dtype).copy() for d in dev]
+    final = (inst.state[0].clone(), inst.tail[0].clone())
+    gdn = [l for l, kind in enumerate(w.layer_kind) if kind == 0]
+    for pos in (384, 512):
+        assert eng.anchor_below(0, pos) == pos
+        k, n = pos // every - 1, pos - L
+        for gi, l in enumerate(gdn):
+            h = host[l]
+            _, (_, kc, vc) = oracle.gdn_conv_layer(synth.chain_tree(T), S0[gi], tail0[gi], h["q"], h["k"],
+                                                   h["v"], h["alpha"], h["beta"], inst.h_conv_w[gi])
+            ref = oracle.gdn_commit(list(range(n)), S0[gi], kc, vc, h["alpha"], h["beta"])
+            err = rel_err(astate[k, gi].cpu().numpy(), ref)
+            assert err <= gu.TOL_F32, f"anchor {pos} layer {l}: {err:.3e}"
+            want = oracle.conv_tail_commit(tail0[gi], h["q"], h["k"], h["v"], list(range(n)))
+            assert np.array_equal(to_host(aconv[k, gi], w.dtype), want), f"anchor {pos} layer {l} tail"
+    eng.rollback_to(0, 384, gu.stream())
+    gu.sync()
+    assert eng.kv_length(0) == 384
+    rest = [{name: x[384 - L:] for name, x in d.items()} for d in dev]
+    for d in rest:
+        d["o"].zero_()
+    eng.forward_chunked(0, T - (384 - L), rest, gu.stream())
+    gu.sync()
+    for l, d in enumerate(dev):
+        assert np.array_equal(to_host(d["o"], w.dtype)[384 - L:], first[l][384 - L:]), f"layer {l}"
+    assert torch.equal(inst.state[0], final[0]) and torch.equal(inst.tail[0], final[1])
     eng.close()
 
 
