@@ -51,13 +51,21 @@ def test_chunked_matches_oracle(L, T):
     eng.close()
 
 
-@pytest.mark.parametrize("L,T", [(300, 150), (300, 2), (256, 64)])
-def test_chunked_conv_matches_oracle(L, T):
+def _span_conv(width):
+    if width == 4:
+        return SPAN_CONV
+    return synth.Workload(f"span_conv{width}", [0, 0, 1], 2, 4, 128, 128, 12, 2, 256, "bf16", [300], 16,
+                          "draft", extra={"conv": width})
+
+
+@pytest.mark.parametrize("width,L,T", [(4, 300, 150), (4, 300, 2), (4, 256, 64), (2, 300, 70), (1, 300, 70)])
+def test_chunked_conv_matches_oracle(width, L, T):
     """The short conv in front of each GDN layer: outputs and state against the oracle's conv
     and recurrence, and the tail afterwards holds the last width - 1 pre-conv rows of (old
-    tail, span) bit for bit (with T = 2, one of them from the old tail)."""
-    w = SPAN_CONV
-    _say(f"chunked prefill with the short conv: {T} tokens at {L}")
+    tail, span) bit for bit (with T = 2 and width 4, one of them from the old tail; width 1
+    has no tail)."""
+    w = _span_conv(width)
+    _say(f"chunked prefill with the width-{width} conv: {T} tokens at {L}")
     inst = Instance(w, SEED, lengths=[L], capacity=[L + T + 64])
     eng = inst.engine()
     host, dev = span_inputs(inst, T)
@@ -67,7 +75,7 @@ def test_chunked_conv_matches_oracle(L, T):
     check_span_against_oracle(inst, host, dev, L, T)
     gi = 0
     for l, kind in enumerate(w.layer_kind):
-        if kind != 0:
+        if kind != 0 or width == 1:
             continue
         h = host[l]
         want = oracle.conv_tail_commit(inst.h_tail[0][gi], h["q"], h["k"], h["v"], list(range(T)))
