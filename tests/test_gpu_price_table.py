@@ -1,4 +1,5 @@
-"""The price-table sweep runs on the device: one small entry with two joint slots."""
+"""The price-table sweep runs on the device: one small entry with two joint slots, and two
+entries of the shipped MI355X price file measured again."""
 import pytest
 
 pytestmark = pytest.mark.gpu
@@ -14,4 +15,26 @@ def test_price_entry_small():
     assert r["commit_path"] == 4
     assert 0 < r["verify_p10_ms"] <= r["verify_ms"] <= r["verify_p90_ms"] < 1000
     assert 0 < r["commit_ms"] < 1000
+    torch.cuda.synchronize()
+
+
+def test_price_entries_match_the_shipped_file():
+    """A fresh measurement of two entries of the shipped file (4 and 16 nodes over 8,192
+    tokens, one slot) lands within a factor of 1.5 of the file's figures, lookup returns those
+    figures at measured points, and the 16-node pass costs at least as much as the 4-node one
+    in the file and in the fresh measurement."""
+    import torch
+    from hybrid_deltanet_tree_amd import price_table as pt
+    table = pt.load()
+    mem = pt.make_slots(1, 8192 + 16 + 64, 20261202)
+    fresh, shipped = {}, {}
+    for n in (4, 16):
+        print(f"price entry: {n} nodes, 8192 tokens, 1 slot", flush=True)
+        r = pt.measure(n, 8192, 1, mem, reps=5, warmup=1)
+        e = next(x for x in table["entries"] if x["n_nodes"] == n and x["context"] == 8192 and x["slots"] == 1)
+        fresh[n], shipped[n] = r["verify_ms"], e["verify_ms"]
+        assert pt.lookup(table, n, 8192, 1) == e["verify_ms"]
+        assert e["verify_ms"] / 1.5 <= r["verify_ms"] <= e["verify_ms"] * 1.5, (n, r["verify_ms"], e["verify_ms"])
+    assert shipped[16] >= shipped[4] and fresh[16] >= 0.95 * fresh[4], (shipped, fresh)
+    del mem
     torch.cuda.synchronize()
