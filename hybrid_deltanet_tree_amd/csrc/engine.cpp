@@ -32,8 +32,8 @@ constexpr float kConvEps = 1e-6f;      // GDN conv: epsilon of the q/k L2 norm, 
 constexpr int64_t kKvSplitMin = 128;  // bf16 attention: smallest split (> kKvTile - 1 + kMaxNodes - 1)
 constexpr int kProfKinds = 10;        // kernel classes of hdt_profile_read
 constexpr int32_t kPfPiece = 2048;    // chunked prefill: tokens per piece (one pass through every layer)
-constexpr int32_t kPfMaxSplits = 4;   // chunked prefill: most key splits of an attention layer
-constexpr int32_t kPfItems = 1024;    // chunked prefill: attention items aimed at per layer
+constexpr int32_t kPfMaxSplits = 8;   // chunked prefill: most key splits of an attention layer
+constexpr int32_t kPfItems = 768;     // chunked prefill: attention items aimed at per layer (3 per CU)
 
 // The scratch of one slot's round: what commit needs of the pass, the attention
 // partials and the conv staging.  Nothing in it has to start at zero: every value is
@@ -1192,6 +1192,14 @@ hdt_status hdt_forward_span(hdt_engine *e, int32_t slot, int32_t T, const hdt_la
 
 namespace {
 
+// Key splits of a prefill attention layer with `tiles_heads` (row tile, kv head) pairs:
+// enough for about kPfItems workgroups (a few per CU, so that none waits on a last one),
+// at most kPfMaxSplits.  The split itself is then rounded up to whole tiles, which can
+// only lower the count.
+int32_t pf_splits(int32_t tiles_heads) {
+  return std::max(1, std::min(kPfMaxSplits, (kPfItems + tiles_heads - 1) / tiles_heads));
+}
+
 // Sizes of the chunked-prefill scratch for one piece of kPfPiece tokens.
 struct PfSizes {
   size_t w, mq, kq, ut, g, acc, ml, conv;
@@ -1211,9 +1219,14 @@ PfSizes pf_sizes(const hdt_model_desc &m) {
   }
   if (m.attn_hkv > 0) {
     const size_t G = m.attn_hq / m.attn_hkv;
-    const size_t rows_cap = (kPfPiece * G + kPfRows - 1) / kPfRows * kPfRows;
-    z.acc = static_cast<size_t>(m.attn_hkv) * kPfMaxSplits * rows_cap * m.attn_d * 4;
-    z.ml = static_cast<size_t>(m.attn_hkv) * kPfMaxSplits * rows_cap * 2 * 4;
+    // the most (kv head, split, row tile) items any piece length takes
+    size_t items = 0;
+    for (int32_t p = 1; p <= kPfPiece; ++p) {
+      const int32_t th = static_cast<int32_t>((p * G + kPfRows - 1) / kPfRows) * m.attn_hkv;
+      items = std::max(items, static_cast<size_t>(th) * pf_splits(th));
+    }
+    z.acc = items * kPfRows * m.attn_d * 4;
+    z.ml = items * kPfRows * 2 * 4;
   }
   return z;
 }
@@ -1351,7 +1364,7 @@ hdt_status chunked_piece(hdt_engine *e, SlotState &s, const hdt_layer_io *io, in
       a.row_tiles = (p * G + kPfRows - 1) / kPfRows;
       a.rows_cap = a.row_tiles * kPfRows;
       const int32_t tiles_heads = a.row_tiles * m.attn_hkv;
-      a.nsplit = std::max(1, std::min(kPfMaxSplits, (kPfItems + tiles_heads - 1) / tiles_heads));
+      a.nsplit = pf_splits(tiles_heads);
       const int64_t keys = L + p;
       a.split = static_cast<int32_t>(((keys + a.nsplit - 1) / a.nsplit + kKvTile - 1) / kKvTile * kKvTile);
       a.nsplit = static_cast<int32_t>((keys + a.split - 1) / a.split);
