@@ -3,8 +3,9 @@
 A step is one pass of the whole path over one round: forward_tree through every
 layer of the stack (Gated DeltaNet tree walk, attention split pass and tree pass),
 then commit_tree of a seeded accepted path.  `value` is the median forward_tree
-time of the pass captured as one HIP graph and replayed (at the length reached
-after the eager steps); the eager median is reported beside it.  The default workload is the 64-layer
+time over K rounds run through the library's reusable graph (hdt_graph_forward:
+one graph launch per round, the instantiated graph updated in place from round to
+round, each round committed); the eager median is reported beside it.  The default workload is the 64-layer
 3:1 stack (48 GDN + 16 attention layers) at 65,536 resident tokens with a
 16-node draft tree; inputs are seeded synthetic data resident in HBM before the
 timed region.  Prints one JSON line.
@@ -335,7 +336,7 @@ def main():
     paths = [synth.accepted_path(args.seed, f"{w.name}/bench-path" + (f"/{s}" if s else ""), parents[s])
              for s in range(ns)]
     path = paths[0]
-    steps_total = args.warmup + 2 * args.steps
+    steps_total = args.warmup + 3 * args.steps + 2 + 5
     caps = [w.lengths[s] + steps_total * len(paths[s]) + 64 for s in range(ns)]
     t_setup = time.perf_counter()
     inst = Instance(w, args.seed, lengths=list(w.lengths), trees=parents, capacity=caps, keep_host=False)
@@ -388,29 +389,39 @@ def main():
     verify_ms = [a.elapsed_time(b) for a, b in ev]
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    # ---- the same pass captured as one HIP graph and replayed at a fixed length:
-    # forward_tree enqueues only kernels, and a replay repeats the round's pass
-    graph_ms = []
-    L_graph = lens()
+    # ---- K more rounds through the library's reusable graph (hdt_graph_forward): each
+    # round's pass is one graph launch, the instantiated graph updated in place from the
+    # last round's; the verify is bracketed by events, then the round is committed
+    graph_ms, graph_lengths, graph_host_us, graph_counts = [], [], [], (0, 0)
     if not args.no_graph:
-        g = torch.cuda.CUDAGraph()
+        graph = eng.graph()
+        for _ in range(2):  # the two graphs used in turn are instantiated here
+            graph.forward(tree, sp)
+            close_round()
         torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=torch.cuda.Stream()):  # captured off the default stream
-            eng.forward_tree(tree, torch.cuda.current_stream().cuda_stream)
         gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
-        for _ in range(2):
-            g.replay()
-        torch.cuda.synchronize()
         for a, b in gev:
+            graph_lengths.append(lens())
             a.record(stream)
-            g.replay()
+            graph.forward(tree, sp)
             b.record(stream)
+            close_round()
         torch.cuda.synchronize()
         graph_ms = [a.elapsed_time(b) for a, b in gev]
-        for s in range(ns):
-            eng.rollback_to(s, eng.kv_length(s), sp)
-        del g
+        # host time of a call (capture, update in place, launch) with the device idle, so
+        # that no wait for an earlier launch is counted
+        for _ in range(5):
+            torch.cuda.synchronize()
+            h0 = time.perf_counter()
+            graph.forward(tree, sp)
+            graph_host_us.append((time.perf_counter() - h0) * 1e6)
+            close_round()
+        torch.cuda.synchronize()
+        graph_counts = graph.stats()
+        graph.close()
+    L_graph = ([round(sum(x[s] for x in graph_lengths) / len(graph_lengths), 1) for s in range(ns)]
+               if graph_lengths else lens())
 
     # ---- per-kernel HIP events (library-recorded, on the launch stream) over K more steps
     eng.profile(True)
@@ -481,7 +492,9 @@ def main():
                    "parallelism": "single GPU"},
         "verify": {"median_ms": round(med, 4), "p10_ms": round(sorted(times)[len(times) // 10], 4),
                    "p90_ms": round(sorted(times)[(9 * len(times)) // 10], 4),
-                   "timed_as": "hip graph replay" if graph_ms else "eager",
+                   "timed_as": "reusable hip graph, updated every round" if graph_ms else "eager",
+                   "graph_instantiations": graph_counts[0], "graph_updates": graph_counts[1],
+                   "graph_host_us_median": round(statistics.median(graph_host_us), 1) if graph_host_us else None,
                    "eager_median_ms": round(eager_med, 4),
                    "algorithmic_bytes": int(verify_bytes), "achieved_gbps": round(verify_gbps, 1),
                    "frac_of_peak": round(verify_gbps / PEAK_HBM_GBS, 4),

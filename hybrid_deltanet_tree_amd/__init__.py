@@ -76,6 +76,10 @@ _sigs = {
     "hdt_destroy": (None, [_E]),
     "hdt_forward_tree": (_S, [_E, ctypes.c_int32, ctypes.POINTER(hdt_tree), ctypes.c_void_p]),
     "hdt_forward_tree_noalloc": (_S, [_E, ctypes.c_int32, ctypes.POINTER(hdt_tree), ctypes.c_void_p]),
+    "hdt_graph_create": (_S, [_E, ctypes.POINTER(ctypes.c_void_p)]),
+    "hdt_graph_forward": (_S, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(hdt_tree), ctypes.c_void_p]),
+    "hdt_graph_stats": (_S, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
+    "hdt_graph_destroy": (None, [ctypes.c_void_p]),
     "hdt_forward_block": (_S, [_E, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(hdt_layer_io),
                                ctypes.c_void_p]),
     "hdt_commit_tree": (_S, [_E, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
@@ -110,6 +114,30 @@ for _name, (_res, _args) in _sigs.items():
     globals()[_name] = _f
 
 EXPORTED = tuple(_sigs)
+
+
+class Graph:
+    """hdt_graph of an Engine (see Engine.graph)."""
+
+    def __init__(self, engine):
+        self.engine = engine
+        h = ctypes.c_void_p()
+        engine._check(hdt_graph_create(engine.h, ctypes.byref(h)))
+        self.h = h
+
+    def forward(self, trees, stream=0):
+        arr, keep = self.engine._trees(trees)
+        self.engine._check(hdt_graph_forward(self.h, len(trees), arr, stream))
+
+    def stats(self):
+        a, b = ctypes.c_int64(), ctypes.c_int64()
+        self.engine._check(hdt_graph_stats(self.h, ctypes.byref(a), ctypes.byref(b)))
+        return a.value, b.value
+
+    def close(self):
+        if getattr(self, "h", None):
+            hdt_graph_destroy(self.h)
+            self.h = None
 
 
 class HdtError(RuntimeError):
@@ -216,6 +244,12 @@ class Engine:
         """forward_tree with the library's static scratch: allocates nothing."""
         arr, keep = self._trees(trees)
         self._check(hdt_forward_tree_noalloc(self.h, len(trees), arr, stream))
+
+    def graph(self):
+        """A reusable graph of the verify pass (hdt_graph_create): .forward(trees, stream) is
+        forward_tree as one graph launch, .stats() the (instantiations, updates) counts,
+        .close() destroys it (before the engine)."""
+        return Graph(self)
 
     def forward_block(self, slot, n, layers, stream=0):
         self._check(hdt_forward_block(self.h, slot, n, self._io_array(layers), stream))

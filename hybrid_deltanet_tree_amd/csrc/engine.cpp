@@ -15,6 +15,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -892,11 +893,69 @@ void hdt_destroy(hdt_engine *e) {
 
 }  // extern "C"
 
+// A reusable graph of the verify pass: two instantiated graphs used in turn, each with
+// the event recorded after its last launch.
+struct hdt_graph {
+  hdt_engine *e = nullptr;
+  hipStream_t cap = nullptr;  // the private stream the pass is captured on
+  hipGraphExec_t exec[2] = {nullptr, nullptr};
+  hipEvent_t done[2] = {nullptr, nullptr};
+  bool launched[2] = {false, false};
+  int next = 0;
+  int64_t instantiations = 0, updates = 0;
+};
+
 namespace {
 
+// The pass as one graph launch: captured on the graph's stream, then either an update in
+// place of the instantiated graph whose turn it is (same kernel sequence) or a new
+// instantiation.  That graph is touched only once its previous launch has finished.
+hdt_status launch_graph(hdt_engine *e, hdt_graph *g, int32_t n_trees, const hdt_tree *trees,
+                        const int8_t (*par)[kMaxNodes], const int8_t (*dep)[kMaxNodes], hipStream_t stream) {
+  const int k = g->next;
+  if (g->launched[k] && hipEventSynchronize(g->done[k]) != hipSuccess)
+    return fail(e, HDT_E_HIP, "waiting for the graph's previous launch failed");
+  if (hipStreamBeginCapture(g->cap, hipStreamCaptureModeThreadLocal) != hipSuccess)
+    return fail(e, HDT_E_HIP, "graph capture could not begin");
+  const hdt_status st = launch_forward(e, n_trees, trees, par, dep, g->cap);
+  hipGraph_t graph = nullptr;
+  const hipError_t ce = hipStreamEndCapture(g->cap, &graph);
+  if (st != HDT_OK || ce != hipSuccess || !graph) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return st != HDT_OK ? st : fail(e, HDT_E_HIP, "graph capture failed");
+  }
+  if (g->exec[k]) {
+    hipGraphNode_t bad = nullptr;
+    hipGraphExecUpdateResult res = hipGraphExecUpdateError;
+    if (hipGraphExecUpdate(g->exec[k], graph, &bad, &res) == hipSuccess && res == hipGraphExecUpdateSuccess) {
+      ++g->updates;
+    } else {
+      (void)hipGetLastError();  // a refused update is not an error of the pass
+      (void)hipGraphExecDestroy(g->exec[k]);
+      g->exec[k] = nullptr;
+    }
+  }
+  if (!g->exec[k]) {
+    if (hipGraphInstantiate(&g->exec[k], graph, nullptr, nullptr, 0) != hipSuccess) {
+      g->exec[k] = nullptr;
+      (void)hipGraphDestroy(graph);
+      return fail(e, HDT_E_HIP, "graph instantiation failed");
+    }
+    ++g->instantiations;
+  }
+  (void)hipGraphDestroy(graph);
+  if (check_hip(e, hipGraphLaunch(g->exec[k], stream), "graph launch") != HDT_OK) return HDT_E_HIP;
+  if (check_hip(e, hipEventRecord(g->done[k], stream), "graph event") != HDT_OK) return HDT_E_HIP;
+  g->launched[k] = true;
+  g->next = 1 - k;
+  return HDT_OK;
+}
+
 // forward_tree with the engine's own scratch (allocated at the first call), or with
-// `noalloc` the scratch carved from the library's static array of the current device.
-hdt_status forward_trees(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, void *stream, bool noalloc) {
+// `noalloc` the scratch carved from the library's static array of the current device;
+// with `g` the kernels go out as one launch of that reusable graph.
+hdt_status forward_trees(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, void *stream, bool noalloc,
+                         hdt_graph *g = nullptr) {
   if (!e) return HDT_E_INVALID;
   if (n_trees < 1 || n_trees > HDT_MAX_TREES || !trees)
     return fail(e, HDT_E_INVALID, "n_trees must be 1..%d", HDT_MAX_TREES);
@@ -990,8 +1049,9 @@ hdt_status forward_trees(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, 
       return fail(e, HDT_E_UNSUPPORTED, "kernels need %zu / %zu bytes of LDS; the device allows %d",
                   need_g, need_a, e->max_lds);
   }
-  e->no_events = noalloc;  // a noalloc call creates no profiling events either
-  st = launch_forward(e, n_trees, trees, par, dep, static_cast<hipStream_t>(stream));
+  e->no_events = noalloc || g;  // a noalloc or graph call creates no profiling events either
+  st = g ? launch_graph(e, g, n_trees, trees, par, dep, static_cast<hipStream_t>(stream))
+         : launch_forward(e, n_trees, trees, par, dep, static_cast<hipStream_t>(stream));
   e->no_events = false;
   if (st != HDT_OK) return st;
   for (int t = 0; t < n_trees; ++t) {
@@ -1016,6 +1076,46 @@ hdt_status hdt_forward_tree(hdt_engine *e, int32_t n_trees, const hdt_tree *tree
 
 hdt_status hdt_forward_tree_noalloc(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, void *stream) {
   return forward_trees(e, n_trees, trees, stream, true);
+}
+
+hdt_status hdt_graph_create(hdt_engine *e, hdt_graph **out) {
+  if (!e || !out) return HDT_E_INVALID;
+  *out = nullptr;
+  hdt_graph *g = new (std::nothrow) hdt_graph;
+  if (!g) return fail(e, HDT_E_INVALID, "out of host memory");
+  g->e = e;
+  bool ok = hipStreamCreateWithFlags(&g->cap, hipStreamNonBlocking) == hipSuccess;
+  for (int k = 0; k < 2 && ok; ++k) ok = hipEventCreateWithFlags(&g->done[k], hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    hdt_graph_destroy(g);
+    return fail(e, HDT_E_HIP, "graph stream or events could not be created");
+  }
+  *out = g;
+  e->err.clear();
+  return HDT_OK;
+}
+
+hdt_status hdt_graph_forward(hdt_graph *g, int32_t n_trees, const hdt_tree *trees, void *stream) {
+  if (!g || !g->e) return HDT_E_INVALID;
+  return forward_trees(g->e, n_trees, trees, stream, false, g);
+}
+
+hdt_status hdt_graph_stats(const hdt_graph *g, int64_t *instantiations, int64_t *updates) {
+  if (!g || !instantiations || !updates) return HDT_E_INVALID;
+  *instantiations = g->instantiations;
+  *updates = g->updates;
+  return HDT_OK;
+}
+
+void hdt_graph_destroy(hdt_graph *g) {
+  if (!g) return;
+  for (int k = 0; k < 2; ++k) {
+    if (g->launched[k]) (void)hipEventSynchronize(g->done[k]);
+    if (g->exec[k]) (void)hipGraphExecDestroy(g->exec[k]);
+    if (g->done[k]) (void)hipEventDestroy(g->done[k]);
+  }
+  if (g->cap) (void)hipStreamDestroy(g->cap);
+  delete g;
 }
 
 hdt_status hdt_forward_block(hdt_engine *e, int32_t slot, int32_t n, const hdt_layer_io *io,

@@ -191,6 +191,29 @@ hdt_status hdt_forward_tree(hdt_engine *eng, int32_t n_trees, const hdt_tree *tr
                             void *stream);
 
 /*
+ * A reusable graph of the verify pass, kept across rounds for a given set of tree sizes and
+ * slots ("How ignis serves a request", 4 "Decode generates, one round for every lane": a
+ * round replays a graph captured for its exact batch width; "Parallel requests", "What a
+ * slot costs": a slot keeps its verify graphs).  hdt_graph_forward is hdt_forward_tree with
+ * the round's kernels enqueued as one HIP graph launch on `stream`: the pass is captured on
+ * the graph's own stream, and the instantiated graph is updated in place (kernel arguments
+ * and grids) when the kernel sequence is the one it holds, else instantiated again.  The
+ * results are hdt_forward_tree's bits, and so is the round's bookkeeping (a pending round
+ * per slot, closed by commit or rollback).  Two instantiated graphs are used in turn and
+ * each is updated only after its previous launch has finished (the host waits for that if
+ * needed), so the host may prepare a round while the one before runs.  The first call on an
+ * engine that has not yet run a forward allocates the engine's scratch first.
+ * hdt_graph_stats counts instantiations and in-place updates.  A graph belongs to its
+ * engine and must be destroyed before it; neither is thread-safe.
+ * Errors: those of hdt_forward_tree.
+ */
+typedef struct hdt_graph hdt_graph;
+hdt_status hdt_graph_create(hdt_engine *eng, hdt_graph **out);
+hdt_status hdt_graph_forward(hdt_graph *g, int32_t n_trees, const hdt_tree *trees, void *stream);
+hdt_status hdt_graph_stats(const hdt_graph *g, int64_t *instantiations, int64_t *updates);
+void hdt_graph_destroy(hdt_graph *g);
+
+/*
  * forward_tree that allocates nothing, for callers that cannot allocate: code under HIP
  * graph capture from the first call on, serving loops and harnesses that forbid
  * allocation.  The same pass and the same bits as hdt_forward_tree, but the round's scratch

@@ -151,9 +151,13 @@ int main(void) {
   CHECK_HIP(hipMemcpy(go, io[0].o, (size_t)N * HV * DK * 2, hipMemcpyDeviceToHost));
   orc_gdn_tree(DK, DK, HK, HV, N, parent, S, q, k, v, a, b, 1, (float)(1.0 / sqrt(DK)), ref, NULL);
   const double e_gdn = rel_err(go, 1, ref, (size_t)N * HV * DK);
+  uint16_t *eager_gdn = (uint16_t *)malloc((size_t)N * HV * DK * 2);
+  memcpy(eager_gdn, go, (size_t)N * HV * DK * 2);
   CHECK_HIP(hipMemcpy(go, io[1].o, (size_t)N * HQ * D * 2, hipMemcpyDeviceToHost));
   orc_attn_tree(HQ, HKV, D, N, parent, L, CAP, Kc, Vc, aq, ak, av, 1, 1.0f / 16.0f, ref);
   const double e_att = rel_err(go, 1, ref, (size_t)N * HQ * D);
+  uint16_t *eager_att = (uint16_t *)malloc((size_t)N * HQ * D * 2);
+  memcpy(eager_att, go, (size_t)N * HQ * D * 2);
 
   /* a state snapshot before the commit (restored at the end) */
   int64_t snap_bytes = 0;
@@ -188,12 +192,28 @@ int main(void) {
   CHECK_HDT(eng, hdt_kv_length(eng, 0, &len_back));
   const int restored = memcmp(gS, S, sizeof(float) * HV * DK * DK) == 0 && len_back == L;
   CHECK_HIP(hipFree(snap));
+
+  /* the same round through a reusable graph: the eager pass's bits; then dropped */
+  hdt_graph *graph = NULL;
+  CHECK_HDT(eng, hdt_graph_create(eng, &graph));
+  CHECK_HIP(hipMemset(io[0].o, 0, (size_t)N * HV * DK * 2));
+  CHECK_HIP(hipMemset(io[1].o, 0, (size_t)N * HQ * D * 2));
+  CHECK_HDT(eng, hdt_graph_forward(graph, 1, &tree, NULL));
+  CHECK_HIP(hipDeviceSynchronize());
+  CHECK_HIP(hipMemcpy(go, io[0].o, (size_t)N * HV * DK * 2, hipMemcpyDeviceToHost));
+  int graph_same = memcmp(go, eager_gdn, (size_t)N * HV * DK * 2) == 0;
+  CHECK_HIP(hipMemcpy(go, io[1].o, (size_t)N * HQ * D * 2, hipMemcpyDeviceToHost));
+  graph_same &= memcmp(go, eager_att, (size_t)N * HQ * D * 2) == 0;
+  CHECK_HDT(eng, hdt_rollback_to(eng, 0, L, NULL));
+  hdt_graph_destroy(graph);
   hdt_destroy(eng);
 
   printf("gdn output %.3e, attention output %.3e, committed state %.3e, rows %s, length %lld, "
-         "snapshot restore %s\n",
-         e_gdn, e_att, e_state, rows_ok ? "equal" : "DIFFER", (long long)len, restored ? "exact" : "WRONG");
-  const int ok = e_gdn <= 2e-2 && e_att <= 2e-2 && e_state <= 2e-3 && rows_ok && len == L + 4 && restored;
+         "snapshot restore %s, graph round %s\n",
+         e_gdn, e_att, e_state, rows_ok ? "equal" : "DIFFER", (long long)len, restored ? "exact" : "WRONG",
+         graph_same ? "equal" : "DIFFER");
+  const int ok = e_gdn <= 2e-2 && e_att <= 2e-2 && e_state <= 2e-3 && rows_ok && len == L + 4 && restored &&
+                 graph_same;
   printf("%s\n", ok ? "PASS" : "FAIL");
   return ok ? 0 : 1;
 }

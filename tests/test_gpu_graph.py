@@ -1,4 +1,5 @@
-"""forward_tree captured into a HIP graph: every replay writes the eager pass's bits.
+"""forward_tree captured into a HIP graph: every replay writes the eager pass's bits; the
+reusable graph (hdt_graph_forward) equals an eager twin round after round.
 
 The pass enqueues kernels only (no allocation, copy or fill), so a captured round
 can be replayed; each replay is checked against the eager outputs, with eager work
@@ -60,3 +61,47 @@ def test_graph_replays_match_eager():
     assert eng.kv_length(0) == 1000
     del g
     eng.close()
+
+
+@pytest.mark.parametrize("lengths", [[1000], [1000, 3000]])
+def test_reusable_graph_across_rounds(lengths):
+    """hdt_graph_forward over rounds that each verify a different 16-node tree and commit a
+    path, so the lengths and the split plan move from round to round: every round's outputs,
+    and the states and cache rows at the end, equal an eager twin's bit for bit, and after
+    its two first instantiations the graph is updated in place rather than rebuilt."""
+    import torch
+    rounds = 8
+    cap = [L + 16 * rounds + 64 for L in lengths]
+    a = Instance(MINI, SEED, lengths=lengths, capacity=cap)
+    b = Instance(MINI, SEED, lengths=lengths, capacity=cap)
+    ea, eb = a.engine(), b.engine()
+    graph = eb.graph()
+    stream = torch.cuda.current_stream().cuda_stream
+    slots = range(len(lengths))
+    for r in range(rounds):
+        trees = [synth.draft_tree(SEED + r, f"graph/round{r}/slot{s}", 16, 15) for s in slots]
+        paths = [synth.accepted_path(SEED + r, f"graph/path{r}/slot{s}", t) for s, t in zip(slots, trees)]
+        for inst in (a, b):
+            for s in slots:
+                for io in inst.io[s]:
+                    io["o"].zero_()
+        ea.forward_tree([(s, trees[s], a.io[s]) for s in slots], stream)
+        graph.forward([(s, trees[s], b.io[s]) for s in slots], stream)
+        torch.cuda.synchronize()
+        for s in slots:
+            got, want = gu.raw_outputs(b, s), gu.raw_outputs(a, s)
+            for l in range(len(MINI.layer_kind)):
+                assert np.array_equal(got[l], want[l]), f"round {r} slot {s} layer {l}"
+        for s in slots:
+            ea.commit_tree(s, paths[s], stream)
+            eb.commit_tree(s, paths[s], stream)
+        assert [eb.kv_length(s) for s in slots] == [ea.kv_length(s) for s in slots]
+    torch.cuda.synchronize()
+    for s in slots:
+        assert torch.equal(a.state[s], b.state[s]) and torch.equal(a.kc[s], b.kc[s]) and torch.equal(a.vc[s], b.vc[s])
+    inst_n, upd = graph.stats()
+    print(f"graph: {inst_n} instantiations, {upd} updates over {rounds} rounds", flush=True)
+    assert inst_n + upd == rounds and inst_n >= 2 and upd >= rounds - 4
+    graph.close()
+    ea.close()
+    eb.close()
