@@ -375,3 +375,15 @@ def test_noalloc_forward_refuses_more_than_its_static_scratch():
         e.commit_tree(0, [0])
     assert err.value.status == -5
     e.close()
+
+
+def test_graph_entry_points_refuse_null_on_the_host():
+    """The reusable-graph verbs refuse a missing graph or output pointer before any HIP call."""
+    import ctypes
+    e = make_engine()
+    assert hdt.hdt_graph_create(e.h, None) == -1
+    assert hdt.hdt_graph_forward(None, 1, None, None) == -1
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    assert hdt.hdt_graph_stats(None, ctypes.byref(a), ctypes.byref(b)) == -1
+    hdt.hdt_graph_destroy(None)  # a no-op
+    e.close()
