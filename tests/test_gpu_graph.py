@@ -63,17 +63,22 @@ def test_graph_replays_match_eager():
     eng.close()
 
 
-@pytest.mark.parametrize("lengths", [[1000], [1000, 3000]])
-def test_reusable_graph_across_rounds(lengths):
+CONV = synth.Workload("graph_conv", [0, 1, 0, 0, 1], 16, 32, 128, 128, 24, 4, 256, "bf16", [1000], 16,
+                      "draft", extra={"conv": 4})
+
+
+@pytest.mark.parametrize("wname,lengths", [("mini", [1000]), ("mini", [1000, 3000]), ("conv", [1000])])
+def test_reusable_graph_across_rounds(wname, lengths):
     """hdt_graph_forward over rounds that each verify a different 16-node tree and commit a
     path, so the lengths and the split plan move from round to round: every round's outputs,
-    and the states and cache rows at the end, equal an eager twin's bit for bit, and after
-    its two first instantiations the graph is updated in place rather than rebuilt."""
+    and the states, conv tails and cache rows at the end, equal an eager twin's bit for bit,
+    and after its two first instantiations the graph is updated in place rather than rebuilt."""
     import torch
+    w = {"mini": MINI, "conv": CONV}[wname]
     rounds = 8
     cap = [L + 16 * rounds + 64 for L in lengths]
-    a = Instance(MINI, SEED, lengths=lengths, capacity=cap)
-    b = Instance(MINI, SEED, lengths=lengths, capacity=cap)
+    a = Instance(w, SEED, lengths=lengths, capacity=cap)
+    b = Instance(w, SEED, lengths=lengths, capacity=cap)
     ea, eb = a.engine(), b.engine()
     graph = eb.graph()
     stream = torch.cuda.current_stream().cuda_stream
@@ -90,7 +95,7 @@ def test_reusable_graph_across_rounds(lengths):
         torch.cuda.synchronize()
         for s in slots:
             got, want = gu.raw_outputs(b, s), gu.raw_outputs(a, s)
-            for l in range(len(MINI.layer_kind)):
+            for l in range(len(w.layer_kind)):
                 assert np.array_equal(got[l], want[l]), f"round {r} slot {s} layer {l}"
         for s in slots:
             ea.commit_tree(s, paths[s], stream)
@@ -99,6 +104,8 @@ def test_reusable_graph_across_rounds(lengths):
     torch.cuda.synchronize()
     for s in slots:
         assert torch.equal(a.state[s], b.state[s]) and torch.equal(a.kc[s], b.kc[s]) and torch.equal(a.vc[s], b.vc[s])
+        if a.conv > 1:
+            assert torch.equal(a.tail[s], b.tail[s])
     inst_n, upd = graph.stats()
     print(f"graph: {inst_n} instantiations, {upd} updates over {rounds} rounds", flush=True)
     assert inst_n + upd == rounds and inst_n >= 2 and upd >= rounds - 4
