@@ -260,6 +260,8 @@ __global__ __launch_bounds__(gdn_threads(DK)) void gdn_tree_kernel(const GdnLaun
   const bool keep_k = (cg == 0) && (h % ratio == 0);
 #pragma unroll
   for (int x = 0; x < MAXC; ++x) {
+    // a wave whose first chunk lies past the last node has none in this or a later round
+    if (x * NT + __builtin_amdgcn_readfirstlane(tid) >= nch) break;
     const int c = tid + x * NT;
     const int i = c / CPR, cc = c % CPR;
     float kq = 0.0f;

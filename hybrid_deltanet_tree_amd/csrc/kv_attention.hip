@@ -417,6 +417,8 @@ __global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
   // ---- epilogue.  The partials go out as whole rows: each wave writes its block's
   // normalised bf16 values into its own padded region of the (now idle) ring, then
   // stores them back 16 contiguous bytes per lane, two rows per wave-wide store.
+  // The stores are non-temporal: every workgroup writes its partials at about the same
+  // time, at the end of the pass, and the tree pass reads them once.
   constexpr int SROW = C::ROWB + 16;  // padded row: the 16 rows of a column group hit distinct banks
   static_assert(CW * 16 * SROW <= S * C::TILE, "staging area");
   bare_barrier();  // every wave is past its last tile
@@ -433,7 +435,7 @@ __global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
         *reinterpret_cast<uint2 *>(stage_w + ln * SROW + (16 * db + 4 * g) * 2) = norm_part4(st.acc[k][db], inv_l);
       if (g == 0 && row < M) {
         const int64_t prow = (static_cast<int64_t>(h) * T.nsplit_cap + s) * T.rows_cap + row;
-        *reinterpret_cast<float2 *>(T.part_ml + prow * 2) = make_float2(st.m[k], st.l[k]);
+        __builtin_nontemporal_store(floatx2{st.m[k], st.l[k]}, reinterpret_cast<floatx2 *>(T.part_ml + prow * 2));
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // the wave's staged rows are in LDS
       unsigned char *po = static_cast<unsigned char *>(T.part_o);
@@ -441,7 +443,9 @@ __global__ __launch_bounds__(W * 64) void kv_split_kernel(const KvLaunch P) {
       for (int i = 0; i < 16 * C::CPR / 64; ++i) {
         const int x = 64 * i + lane, rl = x / C::CPR, cc = x % C::CPR;
         const uint4 v = *reinterpret_cast<const uint4 *>(stage_w + rl * SROW + cc * 16);
-        if (16 * blk + rl < M) *reinterpret_cast<uint4 *>(po + part_off<D>(T, h, s, 16 * blk + rl, cc * 8)) = v;
+        if (16 * blk + rl < M)
+          __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
+                                      reinterpret_cast<u32x4 *>(po + part_off<D>(T, h, s, 16 * blk + rl, cc * 8)));
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // read back before the next block reuses the region
     } else if (row < M) {
