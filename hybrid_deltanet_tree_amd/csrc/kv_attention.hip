@@ -264,7 +264,10 @@ __device__ __forceinline__ float part_hi(uint32_t w) { return __uint_as_float(w 
 // (M0 + 16 l); the lane picks the global chunk that the swizzle puts there.  The
 // loads are issued from inline assembly so that the compiler does not fence later
 // LDS reads on them; the caller waits with wait_vm before the barrier that
-// publishes the tile.
+// publishes the tile.  They are non-temporal (nt): each resident row is read once per
+// pass, and a layer's K/V (about 270 MB at 65,536 tokens) is larger than the last-level
+// cache.  With the hint a 65,536-token pass measured 49-50 us instead of 55-56 us per
+// launch, and the commit after it 49 instead of 53 us.
 template <int D, int NP>
 struct KvDma {
   static constexpr int IPW = KvCfg<D>::LOADS / NP;
@@ -294,7 +297,7 @@ struct KvDma {
     for (int x = 0; x < IPW; ++x) {
       const int ins = ins0 + x;
       const bool v = ins >= C::LOADS / 2;  // uniform over the wave
-      asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+      asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen nt lds"
                    :
                    : "v"(base + off[x]), "s"(__builtin_amdgcn_readfirstlane(lds + ins * 1024)), "s"(v ? vres : kres)
                    : "memory", "m0");
