@@ -301,7 +301,9 @@ __global__ __launch_bounds__(gdn_threads(DK)) void gdn_tree_kernel(const GdnLaun
     }
     nsc[tid].x = a;  // .z, k . s q, is written by the staging above
     nsc[tid].y = b;
-    nsc[tid].w = __int_as_float((par_i & 0xFF) | ((save_i & 0xFF) << 8));
+    // parent, the node's own kept slot, the parent's kept slot (-1: none), one byte each
+    const int psave = par_i >= 0 ? static_cast<int>(savel[par_i]) : -1;
+    nsc[tid].w = __int_as_float((par_i & 0xFF) | ((save_i & 0xFF) << 8) | ((psave & 0xFF) << 16));
     if (cg == 0) static_cast<io_t<BF> *>(T.a_pend)[static_cast<int64_t>(tid) * P.hv + h] = araw;
   }
   __syncthreads();
@@ -330,15 +332,12 @@ __global__ __launch_bounds__(gdn_threads(DK)) void gdn_tree_kernel(const GdnLaun
     sc_at += 1;
     v_at += kGdnCols;
   };
-  auto restore = [&](int p) {
-    // the parent's state: kept in LDS, or replayed from the committed state along
-    // its root path with the same rank-1 write as the step below
-    if (p >= 0) {
-      const int sl = __builtin_amdgcn_readfirstlane(static_cast<int>(savel[p]));
-      if (sl >= 0) {
-        lds_row<R>(kept + (sl * kGdnCols + lc) * DK + g * R, cur);
-        return;
-      }
+  auto restore = [&](int p, int sl) {
+    // the parent's state: kept in LDS (slot sl >= 0), or replayed from the committed
+    // state along its root path with the same rank-1 write as the step below
+    if (sl >= 0) {
+      lds_row<R>(kept + (sl * kGdnCols + lc) * DK + g * R, cur);
+      return;
     }
 #pragma unroll
     for (int a = 0; a < R; ++a) cur[a] = base[a];
@@ -368,7 +367,7 @@ __global__ __launch_bounds__(gdn_threads(DK)) void gdn_tree_kernel(const GdnLaun
   auto prepare = [&](int i, const GdnNode<R> &x) {
     if ((restore_mask >> i) & 1) {
       const int w = __builtin_amdgcn_readfirstlane(__float_as_int(x.sc.w));
-      restore(static_cast<int8_t>(w & 0xFF));
+      restore(static_cast<int8_t>(w & 0xFF), static_cast<int8_t>((w >> 16) & 0xFF));
     }
   };
   auto step = [&](int i, const GdnNode<R> &x) {
