@@ -403,7 +403,7 @@ hdt_status launch_kv_group(hdt_engine *e, int32_t n_trees, const hdt_tree *trees
   // only issue the tile loads, kKvRowsPerItem rows per workgroup; a tree with more
   // rows takes several row groups, placed on one XCD so that they read each tile
   // through the same L2.
-  int32_t items_a = 0, items_b = 0;
+  int32_t items_a = 0, items_b = 0, tiles_b = 1;
   for (int t = 0; t < n_trees; ++t) {
     if (gr >= groups[t].count) continue;
     const hdt_tree &tr = trees[t];
@@ -438,6 +438,10 @@ hdt_status launch_kv_group(hdt_engine *e, int32_t n_trees, const hdt_tree *trees
     const int pairs = m.attn_hkv * x.a_splits;  // (kv head, split)
     items_a = std::max(items_a, (pairs + 7) / 8 * 8 * x.row_groups);
     items_b = std::max(items_b, m.attn_hkv * x.gn * kKvQuarters);
+    for (int i = 0; i < x.gn; ++i) {  // tiles from tb0 to each node's position
+      const int64_t pos = s.d.length + dep[t][static_cast<int>(x.nodes[i])];
+      tiles_b = std::max(tiles_b, static_cast<int32_t>((pos / kKvTile * kKvTile - tb0) / kKvTile + 1));
+    }
     std::memcpy(x.parent, par[t], kMaxNodes);
     std::memcpy(x.depth, dep[t], kMaxNodes);
   }
@@ -448,7 +452,7 @@ hdt_status launch_kv_group(hdt_engine *e, int32_t n_trees, const hdt_tree *trees
     if (st != HDT_OK) return st;
   }
   ProfScope p(e, 2);
-  return check_hip(e, launch_kv_tree(a, m.attn_d, items_b, stream, p.events()), "attention tree launch");
+  return check_hip(e, launch_kv_tree(a, m.attn_d, items_b, tiles_b, stream, p.events()), "attention tree launch");
 }
 
 // One attention layer with bf16 storage: one launch pair per group of nodes that

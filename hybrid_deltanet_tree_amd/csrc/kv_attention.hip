@@ -509,12 +509,16 @@ __device__ __forceinline__ Fold8 fold8_partner(const Fold8 &f) {
 
 constexpr int kFoldChunk = 16;  // split partials in flight per fold lane
 
-template <int D>
+// MAX_TILES: the most kKvTile-key tiles from tb0 to a node's position over the launch's
+// nodes (the host picks it).  Two tiles (a node within 2 kKvTile - 1 keys of tb0, as in
+// every tree of depth < kKvTile) leave room for two workgroups on a CU; three cover any
+// tree (kKvTile - 1 committed rows past tb0 and depth up to kMaxNodes - 1).
+template <int D, int MAX_TILES>
 __global__ __launch_bounds__(kKvThreads) void kv_tree_kernel(const KvLaunch P) {
   using C = KvCfg<D>;
   constexpr int QD = C::QD, QDB = C::QDB, QO = QD / 8;  // 8-column groups per quarter
-  constexpr int MAX_TILES = 3;  // (kKvTile - 1 + kMaxNodes - 1) / kKvTile + 1
-  static_assert((kKvTile - 1 + kMaxNodes - 1) / kKvTile + 1 <= MAX_TILES, "tree tiles");
+  static_assert(MAX_TILES == 2 || MAX_TILES == 3, "tree tiles");
+  static_assert((kKvTile - 1 + kMaxNodes - 1) / kKvTile + 1 <= 3, "three tiles cover any tree");
   __shared__ __align__(1024) unsigned char tiles[MAX_TILES][C::TILE];
   __shared__ __align__(16) float x_o[16][QD];   // finished split n_full (crossing), bf16 values
   __shared__ float x_ml[16][2];
@@ -823,15 +827,19 @@ hipError_t launch_kv_split(const KvLaunch &a, int D, int max_items, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_kv_tree(const KvLaunch &a, int D, int max_items, hipStream_t s, KernelEvents ev) {
+hipError_t launch_kv_tree(const KvLaunch &a, int D, int max_items, int tiles, hipStream_t s, KernelEvents ev) {
   const dim3 grid(max_items, a.n_trees);
+  if (tiles < 1 || tiles > 3) return hipErrorInvalidValue;
+#define HDT_TREE(DD, NT) \
+  hipExtLaunchKernelGGL((kv_tree_kernel<DD, NT>), grid, dim3(kKvThreads), 0, s, ev.start, ev.stop, 0, a)
   if (D == 256) {
-    hipExtLaunchKernelGGL((kv_tree_kernel<256>), grid, dim3(kKvThreads), 0, s, ev.start, ev.stop, 0, a);
+    if (tiles <= 2) HDT_TREE(256, 2); else HDT_TREE(256, 3);
   } else if (D == 64) {
-    hipExtLaunchKernelGGL((kv_tree_kernel<64>), grid, dim3(kKvThreads), 0, s, ev.start, ev.stop, 0, a);
+    if (tiles <= 2) HDT_TREE(64, 2); else HDT_TREE(64, 3);
   } else {
     return hipErrorInvalidValue;
   }
+#undef HDT_TREE
   return hipGetLastError();
 }
 

@@ -305,10 +305,12 @@ hipError_t launch_attn_split(const AttnLaunch &a, int D, int bf16, int n_blocks,
                              KernelEvents ev);
 hipError_t launch_attn_fold(const FoldLaunch &a, int D, int bf16, int n_blocks, hipStream_t s,
                             KernelEvents ev);
-// Split pass with `waves` waves of `nb` 16-row blocks each: (8, 1) or (4, 3).
 hipError_t launch_kv_split(const KvLaunch &a, int D, int max_items, hipStream_t s,
                            KernelEvents ev);
-hipError_t launch_kv_tree(const KvLaunch &a, int D, int max_items, hipStream_t s, KernelEvents ev);
+// Tree pass; `tiles` (1..3) is the most kKvTile-key tiles from tb0 to a node's position
+// over the launch's nodes.
+hipError_t launch_kv_tree(const KvLaunch &a, int D, int max_items, int tiles, hipStream_t s,
+                          KernelEvents ev);
 hipError_t launch_commit(const CommitLaunch &a, int dk, int bf16, int n_blocks, hipStream_t s,
                          KernelEvents ev);
 hipError_t launch_gdn_conv(const ConvLaunch &a, int bf16, hipStream_t s, KernelEvents ev);
