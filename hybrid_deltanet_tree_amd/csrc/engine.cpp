@@ -573,7 +573,7 @@ hdt_status launch_forward(hdt_engine *e, int32_t n_trees, const hdt_tree *trees,
         for (int c = 1; c < tr.n_nodes; ++c) {
           if (par[t][c] != c - 1) {
             g.restore_mask |= uint64_t{1} << c;
-            if (g.save[par[t][c]] < 0) g.need_anc = 1;
+            if (g.save[par[t][c]] < 0) g.need_anc = a.any_anc = 1;
           }
         }
         for (int c = 0; c < tr.n_nodes; ++c)
@@ -1047,7 +1047,7 @@ hdt_status forward_trees(hdt_engine *e, int32_t n_trees, const hdt_tree *trees, 
   {
     int32_t n_max = 0;
     for (int t = 0; t < n_trees; ++t) n_max = std::max(n_max, trees[t].n_nodes);
-    const size_t need_g = e->n_gdn > 0 ? gdn_lds_bytes(m.gdn_dk, n_max, kGdnSaves) : 0;
+    const size_t need_g = e->n_gdn > 0 ? gdn_lds_bytes(m.gdn_dk, n_max, kGdnSaves, 1) : 0;
     const size_t need_a = e->n_attn > 0 ? attn_lds_bytes(m.attn_d, m.io_dtype == HDT_BF16, n_max) : 0;
     if (need_g > static_cast<size_t>(e->max_lds) || need_a > static_cast<size_t>(e->max_lds))
       return fail(e, HDT_E_UNSUPPORTED, "kernels need %zu / %zu bytes of LDS; the device allows %d",
@@ -1228,7 +1228,7 @@ hdt_status hdt_forward_span(hdt_engine *e, int32_t slot, int32_t T, const hdt_la
   s.sc = s.own;
   s.static_dev = -1;
   s.static_gen = 0;
-  if (gdn_lds_bytes(m.gdn_dk, m.max_nodes, kGdnSaves) > static_cast<size_t>(e->max_lds) && e->n_gdn > 0)
+  if (gdn_lds_bytes(m.gdn_dk, m.max_nodes, kGdnSaves, 1) > static_cast<size_t>(e->max_lds) && e->n_gdn > 0)
     return fail(e, HDT_E_UNSUPPORTED, "a chain of %d needs more LDS than the device allows", m.max_nodes);
   // bytes per row of each io array, by layer kind
   const size_t z = e->esz;

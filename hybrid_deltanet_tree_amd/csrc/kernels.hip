@@ -52,7 +52,8 @@ __device__ __forceinline__ float rowsum16(float x) {
 // LDS layout of the GDN walk: k[n+1][dk] and s*q[n+1][dk] (float); per node
 // {alpha, beta, k . s q, parent} (float4) [n+1]; v[n+1][16], u[n][16], o[n][16]
 // (float); depth[n] and parent[n] (int); then the kept states [n_saves][16][dk]
-// (float); then anc[n][64] and save[n] (int8).  Row n of the operand arrays is never
+// (float); then save[n] and, when some tree of the launch replays a root path,
+// anc[n][64] (int8).  Row n of the operand arrays is never
 // written: the walk's operand load after the last node reads it and drops it.
 __host__ __device__ constexpr size_t gdn_lds_floats(int dk, int n) {
   return static_cast<size_t>(n + 1) * (2 * dk + 4 + kGdnCols) + static_cast<size_t>(n) * 2 * kGdnCols +
@@ -193,8 +194,8 @@ __global__ __launch_bounds__(gdn_threads(DK)) void gdn_tree_kernel(const GdnLaun
   float *ol = ul + nm * kGdnCols;
   int *dep = reinterpret_cast<int *>(ol + nm * kGdnCols);  // depth[n], then parent[n]
   float *kept = reinterpret_cast<float *>(dep + ((2 * nm + 3) & ~3));  // 16-byte aligned
-  int8_t *anc = reinterpret_cast<int8_t *>(kept + P.n_saves * kGdnCols * DK);
-  int8_t *savel = anc + nm * kMaxNodes;
+  int8_t *savel = reinterpret_cast<int8_t *>(kept + P.n_saves * kGdnCols * DK);
+  int8_t *anc = savel + nm;  // allocated when P.any_anc (touched only when T.need_anc)
 
   const int cgroups = P.dv / kGdnCols;
   const int local = blockIdx.x;
@@ -1242,9 +1243,9 @@ hipError_t set_lds(K kernel, size_t bytes) {
 
 }  // namespace
 
-size_t gdn_lds_bytes(int dk, int n_max, int n_saves) {
+size_t gdn_lds_bytes(int dk, int n_max, int n_saves, int anc) {
   return (gdn_lds_floats(dk, n_max) + static_cast<size_t>(n_saves) * kGdnCols * dk) * sizeof(float) +
-         static_cast<size_t>(n_max) * (kMaxNodes + 1);
+         static_cast<size_t>(n_max) * (anc ? kMaxNodes + 1 : 1);
 }
 
 size_t attn_lds_bytes(int D, int bf16, int n_max) {
@@ -1262,7 +1263,7 @@ size_t commit_lds_bytes(int D, int bf16, int m) {
 
 hipError_t launch_gdn_tree(const GdnLaunch &a, int dk, int bf16, hipStream_t s, KernelEvents ev) {
   const dim3 blocks(a.hv * (a.dv / kGdnCols), a.n_trees);
-  const size_t lds = gdn_lds_bytes(dk, a.n_max, a.n_saves);
+  const size_t lds = gdn_lds_bytes(dk, a.n_max, a.n_saves, a.any_anc);
 #define HDT_GDN(BF, DK)                                                                   \
   do {                                                                                    \
     (void)set_lds(gdn_tree_kernel<BF, DK>, lds);                                                \

@@ -63,6 +63,8 @@ struct GdnLaunch {
   int32_t hk, hv, dv;
   int32_t n_max;                         // largest n over the trees (sizes LDS)
   int32_t n_saves;                       // largest number of kept states over the trees
+  int32_t any_anc;                       // some tree replays a root path (need_anc): LDS holds the
+                                         // ancestor table
   float scale;
 };
 
@@ -333,7 +335,7 @@ hipError_t static_scratch_address(void **out);
 constexpr int conv_channels_per_thread(int bf16) { return bf16 ? 8 : 4; }
 
 // Dynamic LDS bytes each kernel asks for (the host checks them against the device).
-size_t gdn_lds_bytes(int dk, int n_max, int n_saves);
+size_t gdn_lds_bytes(int dk, int n_max, int n_saves, int anc);
 size_t attn_lds_bytes(int D, int bf16, int n_max);
 // Work decomposition of the float32 attention split pass: rows per shared item
 // and nodes per tail item.
