@@ -1046,7 +1046,7 @@ __global__ __launch_bounds__(kGdnThreads) void commit_kernel(const CommitLaunch 
   constexpr int R = DK / 16;
   constexpr int ESZ = BF ? 2 : 4;
   constexpr int KW = R * ESZ / 4;    // 32-bit words of a lane's k slice (2, 4 or 8)
-  constexpr int B = 8;               // path steps whose operands are in flight together
+  constexpr int B = 4;               // path steps whose operands are in flight together
   const int bid = blockIdx.x, tid = threadIdx.x;
   if (bid < P.gdn_blocks) {
     // Committed state of one (GDN layer, value head, NC groups of 16 columns): replay

@@ -26,7 +26,7 @@ constexpr int kKvRowsPerItem = 96; // bf16 attention: query rows per split-pass 
 constexpr int kKvStages = 5;       // bf16 attention: LDS tile ring of the split pass
 constexpr int kKvQuarters = 4;     // bf16 attention: output columns split over this many blocks
 constexpr int kGdnThreads = 256;   // commit: 4 waves
-constexpr int kCommitCols = 4;     // commit: 16-column groups per GDN workgroup (state slices per lane)
+constexpr int kCommitCols = 2;     // commit: 16-column groups per GDN workgroup (state slices per lane)
 constexpr int kGdnCols = 16;       // value columns per GDN workgroup
 // GDN walk: lanes per value column (16: one DPP row; 32 would put two waves on a
 // SIMD, which measured no faster: the per-column reduction work doubles)
