@@ -23,7 +23,7 @@ constexpr int kKvWaves = 4;        // bf16 attention: waves per tree-pass workgr
 constexpr int kKvThreads = kKvWaves * 64;
 constexpr int kMaxDynamicLds = 160 * 1024;  // gfx950 LDS per workgroup
 constexpr int kKvRowsPerItem = 96; // bf16 attention: query rows per split-pass workgroup (6 blocks of 16)
-constexpr int kKvStages = 5;       // bf16 attention: LDS tile ring of the split pass
+constexpr int kKvStages = 4;       // bf16 attention: LDS tile ring of the split pass
 constexpr int kKvQuarters = 4;     // bf16 attention: output columns split over this many blocks
 constexpr int kGdnThreads = 256;   // commit: 4 waves
 constexpr int kCommitCols = 2;     // commit: 16-column groups per GDN workgroup (state slices per lane)
