@@ -157,12 +157,12 @@ __global__ __launch_bounds__(kConvThreads) void gdn_conv_kernel(const ConvLaunch
 constexpr int kPfConvTokens = 8;
 
 template <bool BF, int W>
-__global__ __launch_bounds__(kConvThreads) void pf_conv_kernel(const PfConv P) {
+__global__ __launch_bounds__(kPfConvThreads) void pf_conv_kernel(const PfConv P) {
   constexpr int CPT = BF ? 8 : 4;
   const int t0 = blockIdx.y * kPfConvTokens;
   const int CQ = P.hk * P.dk;
   const int C = 2 * CQ + P.hv * P.dv;
-  const int c0 = (blockIdx.x * kConvThreads + threadIdx.x) * CPT;
+  const int c0 = (blockIdx.x * kPfConvThreads + threadIdx.x) * CPT;
   if (t0 >= P.T || c0 >= C) return;
   const void *in;
   void *out;
@@ -229,11 +229,11 @@ __global__ __launch_bounds__(kConvThreads) void pf_conv_kernel(const PfConv P) {
 // combined row T + i; each thread moves its 16 bytes of channels in ascending i, so a
 // tail row is read (T + i > i) before it is overwritten.  Runs after pf_conv_kernel.
 template <bool BF>
-__global__ __launch_bounds__(kConvThreads) void pf_conv_tail_kernel(const PfConv P) {
+__global__ __launch_bounds__(kPfConvThreads) void pf_conv_tail_kernel(const PfConv P) {
   constexpr int CPT = BF ? 8 : 4;
   const int CQ = P.hk * P.dk;
   const int C = 2 * CQ + P.hv * P.dv;
-  const int c0 = (blockIdx.x * kConvThreads + threadIdx.x) * CPT;
+  const int c0 = (blockIdx.x * kPfConvThreads + threadIdx.x) * CPT;
   if (c0 >= C) return;
   const void *in;
   int64_t row_len, col;
@@ -286,9 +286,9 @@ hipError_t launch_gdn_conv(const ConvLaunch &a, int bf16, hipStream_t s, KernelE
 hipError_t launch_pf_conv(const PfConv &a, int bf16, hipStream_t s, KernelEvents ev) {
   const int C = 2 * a.hk * a.dk + a.hv * a.dv;
   const int cpt = conv_channels_per_thread(bf16);
-  const dim3 grid((C / cpt + kConvThreads - 1) / kConvThreads, (a.T + kPfConvTokens - 1) / kPfConvTokens);
+  const dim3 grid((C / cpt + kPfConvThreads - 1) / kPfConvThreads, (a.T + kPfConvTokens - 1) / kPfConvTokens);
 #define HDT_PFCONV(BF, W)                                                                     \
-  hipExtLaunchKernelGGL((pf_conv_kernel<BF, W>), grid, dim3(kConvThreads), 0, s, ev.start,   \
+  hipExtLaunchKernelGGL((pf_conv_kernel<BF, W>), grid, dim3(kPfConvThreads), 0, s, ev.start,   \
                         ev.stop, 0, a)
 #define HDT_PFCONV_W(BF)                                                                      \
   switch (a.width) {                                                                          \
@@ -307,11 +307,11 @@ hipError_t launch_pf_conv(const PfConv &a, int bf16, hipStream_t s, KernelEvents
 #undef HDT_PFCONV
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.width < 2) return err;
-  const dim3 tgrid((C / cpt + kConvThreads - 1) / kConvThreads);
+  const dim3 tgrid((C / cpt + kPfConvThreads - 1) / kPfConvThreads);
   if (bf16) {
-    hipLaunchKernelGGL((pf_conv_tail_kernel<true>), tgrid, dim3(kConvThreads), 0, s, a);
+    hipLaunchKernelGGL((pf_conv_tail_kernel<true>), tgrid, dim3(kPfConvThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL((pf_conv_tail_kernel<false>), tgrid, dim3(kConvThreads), 0, s, a);
+    hipLaunchKernelGGL((pf_conv_tail_kernel<false>), tgrid, dim3(kPfConvThreads), 0, s, a);
   }
   return hipGetLastError();
 }

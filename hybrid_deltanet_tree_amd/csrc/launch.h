@@ -74,6 +74,7 @@ struct GdnLaunch {
 // norm of q and k.  Channels of a token: q (hk*dk), k (hk*dk), v (hv*dv).
 constexpr int kConvMaxWidth = 4;
 constexpr int kConvThreads = 64;   // one wave: more, smaller workgroups spread the conv over more CUs
+constexpr int kPfConvThreads = 256; // the span conv over a prefill piece (8 tokens a thread)
 struct ConvTree {
   const void *q, *k, *v;                 // pre-conv inputs [n][hk][dk], [n][hk][dk], [n][hv][dv]
   const void *tail;                      // committed tail of this layer [width-1][C]
